@@ -1,0 +1,14 @@
+"""CPU oracle for the frame-wise gated delta rule and block-causal ReLU linear attention.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; never by the product package.  It shares no code
+with the HIP path.  Every function here is "parity pinned" by the tests in
+``tests/test_oracle_pins.py``.
+"""
+from .oracle import (  # noqa: F401
+    NORMALIZE_K,
+    ADDITIVE,
+    build,
+    gdn_forward,
+    linear_attn_block_causal,
+)

@@ -1,0 +1,135 @@
+"""ctypes wrapper around ``oracle_gdn.c`` (TEST INFRASTRUCTURE ONLY).
+
+The C source is the oracle; this file only compiles it (gcc, OpenMP), marshals numpy
+arrays and returns float64 results.  Inputs are widened to float32 before the call:
+bf16 tensors convert to float32 exactly, so the oracle works on the same values the
+GPU receives.
+
+Definitions and citations are in the header of ``oracle_gdn.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+NORMALIZE_K = 1
+ADDITIVE = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_gdn.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_gdn.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle into ``oracle/liboracle_gdn.so`` (gcc -O2 -fopenmp)."""
+    stale = (not os.path.exists(_LIB_PATH)) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    if force or stale:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            fp = ctypes.POINTER(ctypes.c_float)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i = ctypes.c_int
+            lib.oracle_gdn_forward.argtypes = [fp, fp, fp, fp, fp, fp, dp, dp,
+                                               i, i, i, i, i, i, ctypes.c_uint, i]
+            lib.oracle_gdn_forward.restype = i
+            lib.oracle_linear_attn_block_causal.argtypes = [fp, fp, fp, fp, fp, dp, dp, dp,
+                                                            i, i, i, i, i, i, ctypes.c_double, i]
+            lib.oracle_linear_attn_block_causal.restype = i
+            _lib = lib
+    return _lib
+
+
+def _f32(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor -> numpy float32 (exact for bf16)
+        import torch
+        x = x.detach().to("cpu", torch.float32).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def gdn_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None,
+                flags=NORMALIZE_K, n_threads=0, want_state=True):
+    """Frame-wise gated delta rule (see ``oracle_gdn.c``).
+
+    q, k: [B, H, T, d_k]; v: [B, H, T, d_v]; alpha, beta: [B, H, T] (ignored when
+    ``flags`` has ADDITIVE; may then be None); state_in: [B, H, d_v, d_k] or None.
+    Returns (out [B, H, T, d_v] float64, state_out [B, H, d_v, d_k] float64 or None).
+    """
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if T != n_frames * frame_len or k.shape != q.shape or v.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch")
+    additive = bool(flags & ADDITIVE)
+    alpha = _f32(alpha) if not additive or alpha is not None else None
+    beta = _f32(beta) if not additive or beta is not None else None
+    if not additive and (alpha is None or beta is None or alpha.shape != (B, H, T) or beta.shape != (B, H, T)):
+        raise ValueError("alpha/beta must be [B, H, T]")
+    s_in = _f32(state_in)
+    if s_in is not None and s_in.shape != (B, H, dv, dk):
+        raise ValueError("state_in must be [B, H, d_v, d_k]")
+    out = np.zeros((B, H, T, dv), dtype=np.float64)
+    s_out = np.zeros((B, H, dv, dk), dtype=np.float64) if want_state else None
+    rc = lib.oracle_gdn_forward(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float),
+                                _ptr(s_in, ctypes.c_float), _ptr(s_out, ctypes.c_double),
+                                _ptr(out, ctypes.c_double), B, H, n_frames, frame_len, dk, dv,
+                                int(flags), int(n_threads))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_forward failed (%d)" % rc)
+    return out, s_out
+
+
+def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=None,
+                             eps=1e-6, n_threads=0):
+    """Block-causal ReLU linear attention (see ``oracle_gdn.c``).
+
+    Returns (out [B, H, T, d_v], state_out [B, H, d_k, d_v], z_out [B, H, d_k]), float64.
+    """
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if T != n_frames * frame_len or k.shape != q.shape or v.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch")
+    s_in, z = _f32(state_in), _f32(z_in)
+    if s_in is not None and s_in.shape != (B, H, dk, dv):
+        raise ValueError("state_in must be [B, H, d_k, d_v]")
+    if z is not None and z.shape != (B, H, dk):
+        raise ValueError("z_in must be [B, H, d_k]")
+    out = np.zeros((B, H, T, dv), dtype=np.float64)
+    s_out = np.zeros((B, H, dk, dv), dtype=np.float64)
+    z_out = np.zeros((B, H, dk), dtype=np.float64)
+    rc = lib.oracle_linear_attn_block_causal(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                             _ptr(v, ctypes.c_float), _ptr(s_in, ctypes.c_float),
+                                             _ptr(z, ctypes.c_float), _ptr(s_out, ctypes.c_double),
+                                             _ptr(z_out, ctypes.c_double), _ptr(out, ctypes.c_double),
+                                             B, H, n_frames, frame_len, dk, dv, float(eps), int(n_threads))
+    if rc != 0:
+        raise RuntimeError("oracle_linear_attn_block_causal failed (%d)" % rc)
+    return out, s_out, z_out

@@ -1,0 +1,224 @@
+/*
+ * oracle_gdn.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously-correct CPU reference for the frame-wise recurrent
+ * linear attention computed by the HIP library in this repository.  Only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark may
+ * load this file's shared object.  It shares no code, header, table or helper
+ * with the GPU path: everything below is written out from the definitions.
+ *
+ * Accumulation is in double precision.  Inputs arrive as float32 arrays; bf16
+ * tensors widen to float32 exactly, so the oracle sees the very values the
+ * GPU sees.
+ *
+ * Sources of the definitions (cited by page title and section):
+ *  [V]  "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+ *       Transformer" (ICLR 2026 oral, talk transcript), block-KV-cache segment:
+ *       the linear-attention state has a fixed D x D shape whatever the
+ *       sequence length; block i's state is block i-1's cached state plus
+ *       block i's own key-value contribution; blocks are generated causally.
+ *  [W]  "SANA-WM ... 720p video" news summary (vi.news.hada.io, topic 29572),
+ *       section "core design and generation pipeline" / "hybrid architecture
+ *       for long rollouts": the token mixer is a frame-wise Gated DeltaNet.
+ *  [P4] "How NVIDIA SANA-WM generates 60-second 720p video on one GPU"
+ *       (dothoosh.com), technical-specification paragraph: the Gated DeltaNet
+ *       recurrent state has a fixed size regardless of video length.
+ *  [GDN] The pages name the gated delta rule but do not print it.  Its update
+ *       is the published one (Yang, Kautz & Hatamizadeh, "Gated Delta
+ *       Networks: Improving Mamba2 with Delta Rule", ICLR 2025, the gated
+ *       delta rule recurrence):  S_t = a_t S_{t-1} (I - b_t k_t k_t^T)
+ *       + b_t v_t k_t^T, with S of shape d_v x d_k and L2-normalised k.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  - frame-wise readout: every token of frame f reads o_t = S_f q_t where S_f
+ *    is the state after frame f's last token (bidirectional inside a frame,
+ *    causal across frames), which is what [V]'s "block i uses S_i = S_{i-1} +
+ *    block i's contribution" gives when the gate is 1 and the delta term off;
+ *  - tokens of a frame are consumed in memory order;
+ *  - k is normalised as k / sqrt(max(sum k^2, 1e-12));
+ *  - a_t is clamped below at FLT_MIN so that it stays in (0, 1];
+ *  - no scaling of q;
+ *  - block-causal ReLU attention: o_t = phi(q_t)^T S_f / (phi(q_t).z_f + eps)
+ *    with phi = ReLU, S_f = sum over frames g <= f of phi(K_g)^T V_g and
+ *    z_f = sum of phi(k) (plus optional carried S_in, z_in).
+ *
+ * Layouts: q, k, out [B, H, T, d] (T = n_frames * frame_len), alpha and beta
+ * [B, H, T], GDN state [B, H, d_v, d_k], block-causal state [B, H, d_k, d_v]
+ * and normaliser [B, H, d_k]; all row-major.
+ */
+#include <float.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_NORMALIZE_K 1u /* L2-normalise k before use                  */
+#define ORACLE_ADDITIVE    2u /* S += v k^T: no gate, no beta, no delta term */
+
+int oracle_abi_version(void) { return 1; }
+
+/*
+ * Frame-wise gated delta rule, one token at a time ([W] frame-wise Gated
+ * DeltaNet with the [GDN] update, [V] frame-boundary readout).
+ *   a = max(alpha_t, FLT_MIN)
+ *   S <- a S (I - b k k^T) + b v k^T
+ * expanded without forming d x d matrices:  with s = S k,
+ *   S <- a S + b (v - a s) k^T.
+ * With ORACLE_ADDITIVE:  S <- S + v k^T.
+ * After a frame's last token, o_t = S q_t for every token t of the frame.
+ *
+ * state_in may be NULL (zero state); state_out may be NULL.
+ * Returns 0, or -1 on bad sizes / allocation failure.
+ */
+int oracle_gdn_forward(const float* q, const float* k, const float* v,
+                       const float* alpha, const float* beta,
+                       const float* state_in, double* state_out, double* out,
+                       int B, int H, int n_frames, int frame_len, int dk, int dv,
+                       unsigned flags, int n_threads)
+{
+    if (B < 0 || H < 0 || n_frames < 0 || frame_len < 0 || dk <= 0 || dv <= 0) return -1;
+    const long long T = (long long)n_frames * frame_len;
+    const int BH = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (int bh = 0; bh < BH; ++bh) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dv * dk);  /* d_v x d_k */
+        double* kk = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* s = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !kk || !s) { free(S); free(kk); free(s); failed = 1; continue; }
+        if (state_in) {
+            for (long long i = 0; i < (long long)dv * dk; ++i)
+                S[i] = (double)state_in[(size_t)bh * dv * dk + i];
+        } else {
+            memset(S, 0, sizeof(double) * (size_t)dv * dk);
+        }
+        const float* qh = q + (size_t)bh * T * dk;
+        const float* kh = k + (size_t)bh * T * dk;
+        const float* vh = v + (size_t)bh * T * dv;
+        const float* ah = alpha ? alpha + (size_t)bh * T : NULL;
+        const float* bth = beta ? beta + (size_t)bh * T : NULL;
+        double* oh = out + (size_t)bh * T * dv;
+
+        for (int f = 0; f < n_frames; ++f) {
+            const long long t0 = (long long)f * frame_len;
+            /* recurrence over the frame's tokens, in memory order */
+            for (long long t = t0; t < t0 + frame_len; ++t) {
+                double nrm2 = 0.0;
+                for (int j = 0; j < dk; ++j) {
+                    kk[j] = (double)kh[t * dk + j];
+                    nrm2 += kk[j] * kk[j];
+                }
+                if (flags & ORACLE_NORMALIZE_K) {
+                    const double inv = 1.0 / sqrt(nrm2 > 1e-12 ? nrm2 : 1e-12);
+                    for (int j = 0; j < dk; ++j) kk[j] *= inv;
+                }
+                const float* vt = vh + t * dv;
+                if (flags & ORACLE_ADDITIVE) {
+                    for (int i = 0; i < dv; ++i)
+                        for (int j = 0; j < dk; ++j)
+                            S[(size_t)i * dk + j] += (double)vt[i] * kk[j];
+                } else {
+                    const double a = (double)(ah[t] > FLT_MIN ? ah[t] : FLT_MIN);
+                    const double b = (double)bth[t];
+                    for (int i = 0; i < dv; ++i) {
+                        double acc = 0.0;
+                        for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * kk[j];
+                        s[i] = acc;
+                    }
+                    for (int i = 0; i < dv; ++i) {
+                        const double coef = b * ((double)vt[i] - a * s[i]);
+                        for (int j = 0; j < dk; ++j)
+                            S[(size_t)i * dk + j] = a * S[(size_t)i * dk + j] + coef * kk[j];
+                    }
+                }
+            }
+            /* readout from the state after the frame's last token */
+            for (long long t = t0; t < t0 + frame_len; ++t) {
+                for (int i = 0; i < dv; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * (double)qh[t * dk + j];
+                    oh[t * dv + i] = acc;
+                }
+            }
+        }
+        if (state_out)
+            memcpy(state_out + (size_t)bh * dv * dk, S, sizeof(double) * (size_t)dv * dk);
+        free(S); free(kk); free(s);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Block-causal linear attention with a ReLU feature map ([V], block-KV-cache
+ * segment: the state is a fixed D x D sum, updated additively block by block,
+ * and each block reads the state that already includes its own contribution).
+ *   S_f = S_in + sum_{g <= f} phi(K_g)^T V_g        (d_k x d_v)
+ *   z_f = z_in + sum_{g <= f} sum_{t in g} phi(k_t) (d_k)
+ *   o_t = phi(q_t)^T S_f / (phi(q_t) . z_f + eps)
+ * state_in, z_in, state_out, z_out may be NULL.
+ */
+int oracle_linear_attn_block_causal(const float* q, const float* k, const float* v,
+                                    const float* state_in, const float* z_in,
+                                    double* state_out, double* z_out, double* out,
+                                    int B, int H, int n_frames, int frame_len,
+                                    int dk, int dv, double eps, int n_threads)
+{
+    if (B < 0 || H < 0 || n_frames < 0 || frame_len < 0 || dk <= 0 || dv <= 0) return -1;
+    const long long T = (long long)n_frames * frame_len;
+    const int BH = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (int bh = 0; bh < BH; ++bh) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);  /* d_k x d_v */
+        double* z = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* ph = (double*)malloc(sizeof(double) * (size_t)dk);
+        if (!S || !z || !ph) { free(S); free(z); free(ph); failed = 1; continue; }
+        for (long long i = 0; i < (long long)dk * dv; ++i)
+            S[i] = state_in ? (double)state_in[(size_t)bh * dk * dv + i] : 0.0;
+        for (int i = 0; i < dk; ++i) z[i] = z_in ? (double)z_in[(size_t)bh * dk + i] : 0.0;
+        const float* qh = q + (size_t)bh * T * dk;
+        const float* kh = k + (size_t)bh * T * dk;
+        const float* vh = v + (size_t)bh * T * dv;
+        double* oh = out + (size_t)bh * T * dv;
+        for (int f = 0; f < n_frames; ++f) {
+            const long long t0 = (long long)f * frame_len;
+            for (long long t = t0; t < t0 + frame_len; ++t) {
+                for (int i = 0; i < dk; ++i) {
+                    const double x = (double)kh[t * dk + i];
+                    ph[i] = x > 0.0 ? x : 0.0;
+                    z[i] += ph[i];
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        S[(size_t)i * dv + j] += ph[i] * (double)vh[t * dv + j];
+            }
+            for (long long t = t0; t < t0 + frame_len; ++t) {
+                double den = 0.0;
+                for (int i = 0; i < dk; ++i) {
+                    const double x = (double)qh[t * dk + i];
+                    ph[i] = x > 0.0 ? x : 0.0;
+                    den += ph[i] * z[i];
+                }
+                den += eps;
+                for (int j = 0; j < dv; ++j) {
+                    double num = 0.0;
+                    for (int i = 0; i < dk; ++i) num += ph[i] * S[(size_t)i * dv + j];
+                    oh[t * dv + j] = num / den;
+                }
+            }
+        }
+        if (state_out) memcpy(state_out + (size_t)bh * dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        if (z_out) memcpy(z_out + (size_t)bh * dk, z, sizeof(double) * (size_t)dk);
+        free(S); free(z); free(ph);
+    }
+    return failed ? -1 : 0;
+}

@@ -1,0 +1,257 @@
+"""Pins of the CPU oracle to things other than itself: hand-derived values, closed
+forms, textbook special cases, a different route through the algebra (explicit products
+of d x d transition matrices, the chunked WY form) and invariants.  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_ref import gdn_chunked
+from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "handworked_d2.json")
+
+
+def _np(x):
+    return x.detach().to(torch.float32).numpy().astype(np.float64) if hasattr(x, "detach") else x
+
+
+def _rand_gdn(B=1, H=2, F=3, N=5, d=6, dv=None, seed=7, gates="config", state_std=None):
+    inp = gdn_inputs(B, H, F, N, d, dtype=torch.float32, workload_id=seed, gates=gates,
+                     state_std=state_std, dv=dv)
+    return inp
+
+
+# ---------------------------------------------------------------- hand-worked values
+def test_gdn_handworked_d2():
+    g = json.load(open(GOLD))["gdn"]
+    arr = lambda x: np.asarray(x, dtype=np.float32)[None, None]
+    out, st = oracle.gdn_forward(arr(g["q"]), arr(g["k"]), arr(g["v"]), arr(g["alpha"]),
+                                 arr(g["beta"]), g["n_frames"], g["frame_len"])
+    np.testing.assert_allclose(out[0, 0], np.asarray(g["out"]), atol=1e-6, rtol=1e-6)
+    np.testing.assert_allclose(st[0, 0], np.asarray(g["state_out"]), atol=1e-6, rtol=1e-6)
+
+
+def test_block_causal_handworked_d2():
+    g = json.load(open(GOLD))["block_causal"]
+    arr = lambda x: np.asarray(x, dtype=np.float32)[None, None]
+    out, st, z = oracle.linear_attn_block_causal(arr(g["q"]), arr(g["k"]), arr(g["v"]),
+                                                 g["n_frames"], g["frame_len"], eps=g["eps"])
+    num = np.asarray(g["num"], dtype=np.float64)
+    den = np.asarray(g["den"], dtype=np.float64) + g["eps"]
+    np.testing.assert_allclose(out[0, 0], num / den[:, None], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st[0, 0], np.asarray(g["state_out"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(z[0, 0], np.asarray(g["z_out"]), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- textbook special cases
+def _frame_mask(F, N):
+    fr = np.repeat(np.arange(F), N)
+    return (fr[None, :] <= fr[:, None]).astype(np.float64)  # M[t, s] = frame(s) <= frame(t)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_block_causal_equals_masked_quadratic_form(with_state):
+    F, N, d, dv = 4, 3, 5, 4
+    inp = block_causal_inputs(1, 2, F, N, d, dtype=torch.float32, workload_id=11,
+                              state_std=0.5 if with_state else None, dv=dv)
+    out, st, z = oracle.linear_attn_block_causal(inp["q"], inp["k"], inp["v"], F, N,
+                                                 state_in=inp["state_in"], z_in=inp["z_in"])
+    M = _frame_mask(F, N)
+    for h in range(2):
+        q, k, v = (_np(inp[n])[0, h] for n in ("q", "k", "v"))
+        pq, pk = np.maximum(q, 0), np.maximum(k, 0)
+        A = M * (pq @ pk.T)
+        num, den = A @ v, A.sum(1)
+        s_out, z_out = pk.T @ v, pk.sum(0)
+        if with_state:
+            S0, z0 = _np(inp["state_in"])[0, h], _np(inp["z_in"])[0, h]
+            num, den = num + pq @ S0, den + pq @ z0
+            s_out, z_out = s_out + S0, z_out + z0
+        np.testing.assert_allclose(out[0, h], num / (den + 1e-6)[:, None], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(st[0, h], s_out, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(z[0, h], z_out, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+def test_gdn_additive_equals_block_causal_quadratic_form(normalize):
+    """gate 1, no delta term: O = (M o Q K^T) V + Q S_in^T (S is d_v x d_k)."""
+    F, N, d, dv = 3, 4, 5, 3
+    inp = _rand_gdn(F=F, N=N, d=d, dv=dv, seed=12, state_std=0.7)
+    flags = oracle.ADDITIVE | (oracle.NORMALIZE_K if normalize else 0)
+    out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], None, None, F, N,
+                                 state_in=inp["state_in"], flags=flags)
+    M = _frame_mask(F, N)
+    for h in range(2):
+        q, k, v = (_np(inp[n])[0, h] for n in ("q", "k", "v"))
+        if normalize:
+            k = k / np.linalg.norm(k, axis=1, keepdims=True)
+        S0 = _np(inp["state_in"])[0, h]
+        np.testing.assert_allclose(out[0, h], (M * (q @ k.T)) @ v + q @ S0.T, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(st[0, h], S0 + v.T @ k, rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_gdn_beta_zero_pure_decay():
+    """beta = 0: S_f = (prod_{t <= end of f} a_t) S_0 and O_f = Q_f S_f^T."""
+    F, N, d = 4, 3, 6
+    inp = _rand_gdn(F=F, N=N, d=d, seed=13, gates="near_one", state_std=1.0)
+    beta = torch.zeros_like(inp["beta"])
+    out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], beta, F, N,
+                                 state_in=inp["state_in"])
+    a = _np(inp["alpha"])
+    for h in range(2):
+        S0, q = _np(inp["state_in"])[0, h], _np(inp["q"])[0, h]
+        for f in range(F):
+            Sf = np.prod(a[0, h, :(f + 1) * N]) * S0
+            np.testing.assert_allclose(out[0, h, f * N:(f + 1) * N], q[f * N:(f + 1) * N] @ Sf.T,
+                                       rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(st[0, h], np.prod(a[0, h]) * S0, rtol=1e-12)
+
+
+def test_gdn_alpha_zero_is_clamped_and_forgets():
+    """a_t = 0 is clamped to FLT_MIN: the past is wiped except for ~1e-38 of it."""
+    F, N, d = 2, 3, 4
+    inp = _rand_gdn(F=F, N=N, d=d, seed=14, state_std=1.0)
+    alpha = inp["alpha"].clone()
+    alpha[..., N] = 0.0  # first token of frame 2
+    out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], alpha, inp["beta"], F, N,
+                                 state_in=inp["state_in"])
+    out2, st2 = oracle.gdn_forward(inp["q"][..., N:, :], inp["k"][..., N:, :], inp["v"][..., N:, :],
+                                   alpha[..., N:], inp["beta"][..., N:], 1, N, state_in=None)
+    np.testing.assert_allclose(out[..., N:, :], out2, rtol=1e-9, atol=1e-30)
+    np.testing.assert_allclose(st, st2, rtol=1e-9, atol=1e-30)
+
+
+def _unit_keys(inp):
+    k = _np(inp["k"])
+    return (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+
+
+def test_gdn_beta_one_retrieval():
+    """b_t = 1: the delta rule writes v_t exactly, S_t k^_t = v_t, whatever a_t."""
+    T, d = 12, 8
+    inp = _rand_gdn(F=T, N=1, d=d, seed=15, state_std=1.0)
+    kh = _unit_keys(inp)
+    out, _ = oracle.gdn_forward(kh, kh, inp["v"], inp["alpha"], torch.ones_like(inp["beta"]),
+                                T, 1, state_in=inp["state_in"])
+    # q = kh (float32) has norm 1 +- 1e-7; the oracle normalises in float64
+    nrm = np.linalg.norm(kh.astype(np.float64), axis=-1, keepdims=True)
+    np.testing.assert_allclose(out / nrm, _np(inp["v"]), rtol=1e-12, atol=1e-12)
+
+
+def test_gdn_delta_rule_defining_property():
+    """S_t k^_t = a_t (1 - b_t) S_{t-1} k^_t + b_t v_t, token by token (frame_len 1)."""
+    T, d, dv = 16, 7, 5
+    inp = _rand_gdn(F=T, N=1, d=d, dv=dv, seed=16, state_std=1.0)
+    kh = _unit_keys(inp)
+    k_next = np.concatenate([kh[..., 1:, :], kh[..., :1, :]], axis=2)
+    o_same, _ = oracle.gdn_forward(kh, kh, inp["v"], inp["alpha"], inp["beta"], T, 1,
+                                   state_in=inp["state_in"])          # S_t k^_t
+    o_next, _ = oracle.gdn_forward(k_next, kh, inp["v"], inp["alpha"], inp["beta"], T, 1,
+                                   state_in=inp["state_in"])          # S_t k^_{t+1}
+    a, b, v = _np(inp["alpha"]), _np(inp["beta"]), _np(inp["v"])
+    nrm = np.linalg.norm(kh.astype(np.float64), axis=-1, keepdims=True)  # q carries |kh| != 1 exactly
+    lhs = (o_same / nrm)[..., 1:, :]
+    rhs = (a * (1 - b))[..., 1:, None] * (o_next[..., :-1, :] / nrm[..., 1:, :]) + b[..., 1:, None] * v[..., 1:, :]
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-12)
+
+
+def test_gdn_explicit_transition_products():
+    """Unrolled closed form with dense d x d transition matrices:
+    S_F = S_0 prod_t A_t + sum_t b_t v_t k^_t^T prod_{s>t} A_s,  A_t = a_t (I - b_t k^ k^T)."""
+    F, N, d, dv = 2, 4, 5, 3
+    inp = _rand_gdn(F=F, N=N, d=d, dv=dv, seed=17, state_std=1.0)
+    out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], F, N,
+                                 state_in=inp["state_in"])
+    a, b = _np(inp["alpha"]), _np(inp["beta"])
+    for h in range(2):
+        k = _np(inp["k"])[0, h]
+        kh = k / np.linalg.norm(k, axis=1, keepdims=True)
+        v, q, S0 = _np(inp["v"])[0, h], _np(inp["q"])[0, h], _np(inp["state_in"])[0, h]
+        A = [a[0, h, t] * (np.eye(d) - b[0, h, t] * np.outer(kh[t], kh[t])) for t in range(F * N)]
+        for f in range(F):
+            end = (f + 1) * N
+            tail = [np.eye(d)] * (end + 1)      # tail[t] = prod_{t <= s < end} A_s
+            for t in range(end - 1, -1, -1):
+                tail[t] = A[t] @ tail[t + 1]
+            Sf = S0 @ tail[0] + sum(b[0, h, t] * np.outer(v[t], kh[t]) @ tail[t + 1] for t in range(end))
+            np.testing.assert_allclose(out[0, h, f * N:end], q[f * N:end] @ Sf.T, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(st[0, h], Sf, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- equivalences / invariants
+@pytest.mark.parametrize("chunk", [64, 16, 7, 1])
+@pytest.mark.parametrize("affine", [False, True])
+def test_chunked_form_equals_sequential(chunk, affine):
+    """The WY/UT chunk algebra the kernels implement (with tail chunks) equals the
+    token-by-token oracle to float64 round-off."""
+    F, N, d, dv = 3, 150, 16, 12  # 150 = 2*64 + 22: a ragged tail chunk
+    for gates in ("config", "near_one"):
+        inp = _rand_gdn(B=1, H=1, F=F, N=N, d=d, dv=dv, seed=18, gates=gates, state_std=0.5)
+        out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], F, N,
+                                     state_in=inp["state_in"])
+        o2, s2 = gdn_chunked(_np(inp["q"])[0, 0], _np(inp["k"])[0, 0], _np(inp["v"])[0, 0],
+                             _np(inp["alpha"])[0, 0], _np(inp["beta"])[0, 0], F, N, chunk=chunk,
+                             state_in=_np(inp["state_in"])[0, 0], affine=affine)
+        scale = np.sqrt(np.mean(out ** 2))
+        assert np.max(np.abs(o2 - out[0, 0])) <= 1e-11 * scale
+        assert np.max(np.abs(s2 - st[0, 0])) <= 1e-11 * np.sqrt(np.mean(st ** 2))
+
+
+def test_chunked_additive_equals_sequential():
+    F, N, d = 2, 70, 8
+    inp = _rand_gdn(B=1, H=1, F=F, N=N, d=d, seed=19, state_std=0.5)
+    out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], None, None, F, N,
+                                 state_in=inp["state_in"], flags=oracle.ADDITIVE | oracle.NORMALIZE_K)
+    o2, s2 = gdn_chunked(_np(inp["q"])[0, 0], _np(inp["k"])[0, 0], _np(inp["v"])[0, 0], None, None,
+                         F, N, state_in=_np(inp["state_in"])[0, 0], additive=True)
+    np.testing.assert_allclose(o2, out[0, 0], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(s2, st[0, 0], rtol=1e-11, atol=1e-11)
+
+
+def test_gdn_segments_compose():
+    """Frames [0, F1) then [F1, F) with the state carried equal one call over [0, F)."""
+    F, F1, N, d = 6, 2, 5, 8
+    inp = _rand_gdn(F=F, N=N, d=d, seed=20, gates="near_one", state_std=0.5)
+    full, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], F, N,
+                                  state_in=inp["state_in"])
+    c = F1 * N
+    o1, s1 = oracle.gdn_forward(inp["q"][..., :c, :], inp["k"][..., :c, :], inp["v"][..., :c, :],
+                                inp["alpha"][..., :c], inp["beta"][..., :c], F1, N, state_in=inp["state_in"])
+    o2, s2 = oracle.gdn_forward(inp["q"][..., c:, :], inp["k"][..., c:, :], inp["v"][..., c:, :],
+                                inp["alpha"][..., c:], inp["beta"][..., c:], F - F1, N,
+                                state_in=s1.astype(np.float32))
+    # the carried state passes through float32 (what a caller stores); compare accordingly
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), full, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(s2, st, rtol=1e-6, atol=1e-6)
+
+
+def test_gdn_linear_in_values_and_state():
+    F, N, d = 3, 4, 6
+    i1 = _rand_gdn(F=F, N=N, d=d, seed=21, state_std=1.0)
+    i2 = _rand_gdn(F=F, N=N, d=d, seed=22, state_std=1.0)
+    run = lambda v, s: oracle.gdn_forward(i1["q"], i1["k"], v, i1["alpha"], i1["beta"], F, N, state_in=s)
+    o1, s1 = run(i1["v"], i1["state_in"])
+    o2, s2 = run(i2["v"], i2["state_in"])
+    o3, s3 = run(_np(i1["v"]) + _np(i2["v"]), _np(i1["state_in"]) + _np(i2["state_in"]))
+    np.testing.assert_allclose(o3, o1 + o2, rtol=1e-6, atol=1e-6)  # sums rounded to fp32 on input
+    np.testing.assert_allclose(s3, s1 + s2, rtol=1e-6, atol=1e-6)
+
+
+def test_oracle_state_is_constant_size():
+    """The carried state is d_v x d_k per (b, h) whatever the sequence length."""
+    for F in (1, 7):
+        inp = _rand_gdn(F=F, N=3, d=4, dv=3, seed=23)
+        _, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], F, 3)
+        assert st.shape == (1, 2, 3, 4)
+
+
+def test_oracle_threads_do_not_change_results():
+    inp = _rand_gdn(B=2, H=3, F=2, N=9, d=8, seed=24)
+    o1, s1 = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], 2, 9, n_threads=1)
+    o4, s4 = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], 2, 9, n_threads=4)
+    assert np.array_equal(o1, o4) and np.array_equal(s1, s4)
