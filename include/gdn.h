@@ -1,0 +1,154 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) frame-wise recurrent linear attention library
+ * (libgdn_mi355x.so).
+ *
+ * What is computed (definitions restated from the sources; see the oracle for the
+ * plain reference implementation):
+ *
+ *  Frame-wise gated delta rule.  "SANA-WM ... 720p video" news summary
+ *  (vi.news.hada.io, topic 29572), section "hybrid architecture for long rollouts":
+ *  the token mixer is a frame-wise Gated DeltaNet; "How NVIDIA SANA-WM generates
+ *  60-second 720p video on one GPU" (dothoosh.com), technical-specification paragraph:
+ *  its recurrent state keeps a fixed size whatever the video length.  The update is the
+ *  published gated delta rule (Yang, Kautz & Hatamizadeh, "Gated Delta Networks",
+ *  ICLR 2025), per (batch b, head h), with S of shape d_v x d_k:
+ *      k^_t = k_t / sqrt(max(|k_t|^2, 1e-12))          (GDN_F_NORMALIZE_K)
+ *      S    <- a_t S (I - b_t k^_t k^_t^T) + b_t v_t k^_t^T,  a_t = max(alpha_t, FLT_MIN)
+ *  Readout is frame-wise ("SANA-Video ... Block Linear Diffusion Transformer" talk,
+ *  block-KV-cache segment: block i reads the state that already holds its own
+ *  contribution): every token t of frame f gets o_t = S_f q_t, S_f being the state
+ *  after frame f's last token.  Tokens of a frame are consumed in memory order.
+ *  With GDN_F_ADDITIVE the update is S <- S + v_t k_t^T (gate 1, no delta term), the
+ *  reduction to block-causal linear attention.
+ *
+ *  Block-causal linear attention (same talk, same segment), ReLU feature map phi:
+ *      S_f = S_in + sum_{g<=f} phi(K_g)^T V_g   (d_k x d_v),   z_f = z_in + sum phi(k)
+ *      o_t = phi(q_t)^T S_f / (phi(q_t) . z_f + 1e-6)
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; `dims` is a HOST pointer.
+ *  - Layouts are contiguous row-major: q, k, out [B, H, T, d]; v [B, H, T, d_v];
+ *    alpha, beta [B, H, T] (float32); GDN state [B, H, d_v, d_k] (float32);
+ *    block-causal state [B, H, d_k, d_v] and normaliser [B, H, d_k] (float32);
+ *    T = n_frames * frame_len.
+ *  - dtype (GDN_BF16 or GDN_F32) is the type of q, k, v and, unless GDN_F_OUT_F32 is
+ *    set, of out.  bf16 inputs are contracted on bf16 matrix cores with float32
+ *    accumulation and a float32 state; operands that carry the state are split into
+ *    bf16 hi + lo pairs so they keep ~16 significant bits.  float32 inputs run on
+ *    float32 matrix cores.  A bf16 out is the round-to-nearest-even of the float32
+ *    result that GDN_F_OUT_F32 returns.
+ *  - Supported: d_k == d_v in {16, 32, 64, 112, 128}; frame_len >= 1; every pointer
+ *    16-byte aligned.  B, H or n_frames may be 0 (nothing to compute; a forward call
+ *    with n_frames == 0 copies state_in, or zeros, to state_out).
+ *  - workspace: caller-owned device scratch of at least gdn_workspace_bytes(dims,
+ *    entry) bytes.  Its size grows with B*H but never with n_frames: frames are
+ *    processed in windows of at most 8192 (b, h, frame) units (the environment
+ *    variable GDN_WINDOW_UNITS, read at each call, overrides that bound).  Contents
+ *    need no initialisation and are garbage afterwards.
+ *  - stream: a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; the library never allocates, frees or synchronises.
+ *  - Errors: every check runs on the host before anything is enqueued and returns a
+ *    negative gdn_status_t; nothing is launched then.  A failed launch returns
+ *    GDN_ERR_HIP.  Device faults surface at the caller's next synchronisation.
+ *  - Aliasing: state_out may equal state_in (updated in place).  out must not overlap
+ *    any input, state or the workspace; overlaps the library can see (pointer ranges)
+ *    return GDN_ERR_ALIAS, others are undefined behaviour.
+ *  - Results are deterministic: no atomics, fixed reduction order.
+ */
+#ifndef GDN_MI355X_H
+#define GDN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL                              */
+    GDN_ERR_DIMS = -2,        /* negative or inconsistent sizes, or size overflow         */
+    GDN_ERR_DTYPE = -3,       /* dtype not GDN_BF16 / GDN_F32                             */
+    GDN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
+    GDN_ERR_ALIAS = -5,       /* out overlaps an input, a state or the workspace          */
+    GDN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than gdn_workspace_bytes()     */
+    GDN_ERR_UNSUPPORTED = -7, /* d_k != d_v, d not in {16,32,64,112,128}, or a bad flag   */
+    GDN_ERR_HIP = -8          /* a HIP launch failed                                      */
+} gdn_status_t;
+
+enum { GDN_BF16 = 0, GDN_F32 = 1 };
+
+enum {
+    GDN_F_NORMALIZE_K = 1u << 0, /* L2-normalise k inside the kernel (float32)            */
+    GDN_F_ADDITIVE = 1u << 1,    /* gated delta rule entries: S <- S + v k^T              */
+    GDN_F_RELU_QK = 1u << 2,     /* block-causal entry: phi = ReLU on q and k (else id)  */
+    GDN_F_OUT_F32 = 1u << 3      /* out is float32 whatever dtype is (all entries)        */
+};
+
+enum { GDN_ENTRY_FORWARD = 0, GDN_ENTRY_READONLY = 1, GDN_ENTRY_BLOCK_CAUSAL = 2 };
+
+typedef struct gdn_dims {
+    int32_t B, H;                 /* batch (independent rollouts) and heads              */
+    int32_t n_frames, frame_len;  /* T = n_frames * frame_len tokens per (b, h)          */
+    int32_t d_k, d_v;             /* head dimensions (equal)                             */
+    int32_t dtype;                /* GDN_BF16 or GDN_F32: q, k, v, out                   */
+    uint32_t flags;               /* GDN_F_* bits                                        */
+    void* workspace;              /* device scratch, >= gdn_workspace_bytes() bytes      */
+    size_t workspace_bytes;
+} gdn_dims_t;
+
+/*
+ * Frame-wise gated delta rule, forward over n_frames frames, carrying the state.
+ *  q, k      [B,H,T,d_k] dtype      v, out [B,H,T,d_v] dtype
+ *  alpha     [B,H,T] float32 gate in (0,1] (clamped below at FLT_MIN); may be NULL
+ *            only with GDN_F_ADDITIVE.  beta [B,H,T] float32 in [0,1]; same rule.
+ *  state_in  [B,H,d_v,d_k] float32, NULL = zero state.  Read only.
+ *  state_out [B,H,d_v,d_k] float32, the state after the last frame; NULL = not
+ *            written; may equal state_in.
+ *  out       o_t = S_f q_t for every token of every frame.
+ */
+int gdn_frame_forward(const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta,
+                      const float* state_in, float* state_out, void* out,
+                      const gdn_dims_t* dims, void* stream);
+
+/*
+ * Read-only-state variant for the denoising steps inside a frame ("SANA-Video" talk,
+ * opening: video is generated block by block causally and diffused within the block;
+ * the cached state is only updated once the block is final).  Same outputs as
+ * gdn_frame_forward (each frame attends to the carried state advanced through its own
+ * tokens); state_in is never written and no state is returned.
+ */
+int gdn_frame_forward_readonly(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               const float* state_in, void* out,
+                               const gdn_dims_t* dims, void* stream);
+
+/*
+ * Block-causal linear attention (bidirectional inside a frame, causal across frames).
+ *  q, k [B,H,T,d_k], v, out [B,H,T,d_v] dtype.  phi = ReLU when GDN_F_RELU_QK is set.
+ *  state_in [B,H,d_k,d_v], z_in [B,H,d_k] float32 (NULL = zero); state_out, z_out
+ *  (NULL = not written; may equal state_in / z_in).
+ */
+int linear_attn_block_causal(const void* q, const void* k, const void* v,
+                             const float* state_in, const float* z_in,
+                             float* state_out, float* z_out, void* out,
+                             const gdn_dims_t* dims, void* stream);
+
+/* Bytes of workspace the entry (GDN_ENTRY_*) needs for these dims; 0 on invalid dims.
+ * Bounded independently of n_frames. */
+size_t gdn_workspace_bytes(const gdn_dims_t* dims, int entry);
+
+/* Static, human-readable text for a gdn_status_t value. */
+const char* gdn_status_str(int status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_MI355X_H */

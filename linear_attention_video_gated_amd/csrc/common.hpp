@@ -1,0 +1,168 @@
+// common.hpp -- gfx950 (CDNA4) building blocks shared by the kernels of this library:
+// element types, matrix-core (MFMA) wrappers and the register "fragment" layouts.
+//
+// Fragment layouts (wave64, 16x16 output tiles).  Lane l is split into c = l % 16 and
+// g = l / 16.
+//   K32 step (v_mfma_f32_16x16x32_bf16, or eight v_mfma_f32_16x16x4_f32):
+//     A operand: lane (c, g) holds A[row c][slot (g, j)], j = 0..7
+//     B operand: lane (c, g) holds B[slot (g, j)][col c]
+//     The hardware pairs A's and B's slot (g, j); which logical k a slot stands for
+//     is the loader's choice, as long as A and B agree.  Two slot maps are used:
+//       IDENT: slot (g, j) -> k = 8g + j
+//       PAIR : slot (g, j) -> k = 4g + j (j < 4), 16 + 4g + (j - 4) (j >= 4)
+//   K16 step (v_mfma_f32_16x16x16_bf16, or four v_mfma_f32_16x16x4_f32):
+//     lane (c, g) holds 4 values, slot (g, i) -> k = 4g + i.
+//   Accumulator D (16x16 fp32): lane (c, g) holds D[4g + i][c], i = 0..3.
+// PAIR exists so that two accumulator tiles stacked along rows (rows 0..15 and
+// 16..31) become, without any data movement, the B operand of the next contraction
+// over those 32 rows; likewise one accumulator tile is a K16 B operand.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4_ __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+template <typename E> struct Ops;
+
+// bf16 inputs: bf16 operands, fp32 accumulation.
+template <> struct Ops<bf16> {
+    using F8 = bf16x8;   // K32 fragment, 16 B per lane
+    using F4 = bf16x4;   // K16 fragment, 8 B per lane
+    using V16 = bf16x8;  // 16-byte vector of elements
+    static constexpr int EPV = 8;
+    static __device__ __forceinline__ f32x4 mma32(F8 a, F8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(F4 a, F4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_, a),
+                                                         __builtin_bit_cast(short4_, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ bf16 cvt(float x) { return (bf16)x; }
+    static __device__ __forceinline__ F8 pack8(f32x4 lo, f32x4 hi) {
+        F8 r;
+        r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+        r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+        return r;
+    }
+    static __device__ __forceinline__ F4 pack4(f32x4 x) {
+        F4 r;
+        r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
+        return r;
+    }
+    // 8 consecutive elements from LDS / global (16-byte aligned)
+    static __device__ __forceinline__ F8 ld8(const bf16* p) { return *(const F8*)p; }
+    // elements [p0, p0+4) then [p1, p1+4)  (PAIR slot map from two 8-byte pieces)
+    static __device__ __forceinline__ F8 ld44(const bf16* p0, const bf16* p1) {
+        bf16x4 a = *(const bf16x4*)p0, b = *(const bf16x4*)p1;
+        return F8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    static __device__ __forceinline__ F4 ld4(const bf16* p) { return *(const F4*)p; }
+    static __device__ __forceinline__ void st8(bf16* p, F8 x) { *(F8*)p = x; }
+    static __device__ __forceinline__ void st4(bf16* p, f32x4 x) { *(F4*)p = pack4(x); }
+    static __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+        F4 x = *(const F4*)p;
+        return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+    static __device__ __forceinline__ F8 zero8() {
+        F8 r;
+        for (int j = 0; j < 8; ++j) r[j] = (bf16)0.f;
+        return r;
+    }
+    // x = hi + lo + O(2^-16 |x|): hi = RNE(x), lo = RNE(x - hi)
+    static constexpr bool kSplit = true;
+    static __device__ __forceinline__ void split8(f32x4 a, f32x4 b, F8& hi, F8& lo) {
+        hi = pack8(a, b);
+        f32x4 ra, rb;
+        for (int i = 0; i < 4; ++i) {
+            ra[i] = a[i] - (float)hi[i];
+            rb[i] = b[i] - (float)hi[4 + i];
+        }
+        lo = pack8(ra, rb);
+    }
+    static __device__ __forceinline__ void split4(f32x4 a, F4& hi, F4& lo) {
+        hi = pack4(a);
+        f32x4 r;
+        for (int i = 0; i < 4; ++i) r[i] = a[i] - (float)hi[i];
+        lo = pack4(r);
+    }
+    static __device__ __forceinline__ float lo_of(float x) { return x - (float)(bf16)x; }
+};
+
+// fp32 inputs: fp32 matrix cores (v_mfma_f32_16x16x4_f32), fp32 throughout.
+template <> struct Ops<float> {
+    using F8 = f32x8;
+    using F4 = f32x4;
+    using V16 = f32x4;
+    static constexpr int EPV = 4;
+    static __device__ __forceinline__ f32x4 mma32(F8 a, F8 b, f32x4 c) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ f32x4 mma16(F4 a, F4 b, f32x4 c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ float cvt(float x) { return x; }
+    static __device__ __forceinline__ F8 pack8(f32x4 lo, f32x4 hi) {
+        return F8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    static __device__ __forceinline__ F4 pack4(f32x4 x) { return x; }
+    static __device__ __forceinline__ F8 ld8(const float* p) {
+        f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+        return F8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    static __device__ __forceinline__ F8 ld44(const float* p0, const float* p1) {
+        f32x4 a = *(const f32x4*)p0, b = *(const f32x4*)p1;
+        return F8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    static __device__ __forceinline__ F4 ld4(const float* p) { return *(const F4*)p; }
+    static __device__ __forceinline__ void st8(float* p, F8 x) {
+        *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
+        *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+    static __device__ __forceinline__ void st4(float* p, f32x4 x) { *(f32x4*)p = x; }
+    static __device__ __forceinline__ f32x4 ld4f(const float* p) { return *(const f32x4*)p; }
+    static __device__ __forceinline__ F8 zero8() { return F8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    // fp32 operands need no split: lo is identically zero and never used
+    static constexpr bool kSplit = false;
+    static __device__ __forceinline__ void split8(f32x4 a, f32x4 b, F8& hi, F8& lo) {
+        hi = pack8(a, b);
+        lo = zero8();
+    }
+    static __device__ __forceinline__ void split4(f32x4 a, F4& hi, F4& lo) {
+        hi = a;
+        lo = zero4();
+    }
+    static __device__ __forceinline__ float lo_of(float) { return 0.f; }
+};
+
+template <typename E> __device__ __forceinline__ float tof(E x) { return (float)x; }
+
+// Split precision: bf16 operands that must carry ~16 significant bits are sent to the
+// matrix cores as hi + lo pairs (hi = RNE(x), lo = RNE(x - hi)); a product a*b is then
+// a_hi*b_hi + a_lo*b_hi + a_hi*b_lo (the lo*lo term is below fp32 accumulation noise).
+// NSPLIT is the number of stored parts of such an operand.
+template <typename E> struct SplitCount { static constexpr int N = Ops<E>::kSplit ? 2 : 1; };
+
+// Geometry derived from the head dimension d = 16 * ND.
+template <typename E, int ND_> struct Geo {
+    static constexpr int ND = ND_;              // 16-wide tiles along d
+    static constexpr int D = 16 * ND;
+    static constexpr int KB = (ND + 1) / 2;     // 32-wide k steps along d (zero padded)
+    static constexpr int DP = 32 * KB;          // padded d
+    static constexpr int EPV = Ops<E>::EPV;     // elements per 16-byte vector
+    static constexpr int FRAG = 64 * 8;         // elements in one K32 operand fragment
+};
+
+}  // namespace gdn

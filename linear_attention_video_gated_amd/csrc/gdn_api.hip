@@ -1,0 +1,284 @@
+// gdn_api.hip -- the C ABI declared in include/gdn.h: argument checks (host only, before
+// anything is enqueued), workspace sizing and layout, and dispatch over (dtype, d) to the
+// kernel launchers.  Frames are processed in windows of at most kMaxUnits (b, h, frame)
+// units so the workspace never grows with the number of frames.
+#include "gdn.h"
+#include "common.hpp"
+#include "gdn_kernels.hpp"
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define GDN_API extern "C" __attribute__((visibility("default")))
+
+namespace gdn {
+namespace {
+
+constexpr long long kMaxUnits = 8192;  // default (b, h, frame) units per window
+
+long long window_units() {
+    const char* e = getenv("GDN_WINDOW_UNITS");
+    const long long v = e ? atoll(e) : 0;
+    return v > 0 ? v : kMaxUnits;
+}
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int nd_of(int d) {
+    switch (d) {
+        case 16: return 1;
+        case 32: return 2;
+        case 64: return 4;
+        case 112: return 7;
+        case 128: return 8;
+        default: return 0;
+    }
+}
+
+int esize_of(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+// Plan of one call: window size and workspace offsets.
+struct Plan {
+    long long BH = 0, T = 0;
+    int nd = 0, es = 0, nfw = 0, nwin = 0;
+    size_t off_a = 0, off_b = 0, off_c = 0, off_carry = 0, total = 0;
+};
+
+int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
+    if (!d) return GDN_ERR_NULL;
+    if (d->dtype != GDN_BF16 && d->dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (d->B < 0 || d->H < 0 || d->n_frames < 0 || d->frame_len < 1) return GDN_ERR_DIMS;
+    if (d->d_k != d->d_v || nd_of(d->d_k) == 0) return GDN_ERR_UNSUPPORTED;
+    const uint32_t allowed = (entry == GDN_ENTRY_BLOCK_CAUSAL)
+                                 ? (uint32_t)(GDN_F_RELU_QK | GDN_F_OUT_F32)
+                                 : (uint32_t)(GDN_F_NORMALIZE_K | GDN_F_ADDITIVE | GDN_F_OUT_F32);
+    if (d->flags & ~allowed) return GDN_ERR_UNSUPPORTED;
+    p->BH = (long long)d->B * d->H;
+    p->T = (long long)d->n_frames * d->frame_len;
+    if (p->BH > 65535) return GDN_ERR_DIMS;  // grid y extent
+    p->nd = nd_of(d->d_k);
+    p->es = esize_of(d->dtype);
+    // element count of q must fit comfortably in 63 bits
+    if (p->T > ((long long)1 << 40) / (p->BH ? p->BH : 1) / d->d_k) return GDN_ERR_DIMS;
+    if (p->BH == 0 || d->n_frames == 0) return GDN_OK;
+    long long nfw = window_units() / p->BH;
+    if (nfw < 1) nfw = 1;
+    if (nfw > d->n_frames) nfw = d->n_frames;
+    p->nfw = (int)nfw;
+    p->nwin = (int)((d->n_frames + nfw - 1) / nfw);
+    const size_t units = (size_t)p->BH * (size_t)nfw;
+    size_t a = 0, b = 0, c = 0, carry = 0;
+    if (entry == GDN_ENTRY_BLOCK_CAUSAL) {
+        bc_unit_bytes(p->nd, p->es, &a, &c);
+        carry = (size_t)p->BH * p->nd * (p->nd + 1) * 256 * 4;
+    } else {
+        gdn_unit_bytes(p->nd, p->es, &a, &b, &c);
+        carry = (size_t)p->BH * d->d_k * d->d_v * 4;
+    }
+    p->off_a = 0;
+    p->off_b = align_up(units * a);
+    p->off_c = p->off_b + align_up(units * b);
+    p->off_carry = p->off_c + align_up(units * c);
+    p->total = p->off_carry + (p->nwin > 1 ? align_up(carry) : 0);
+    return GDN_OK;
+}
+
+bool misaligned(const void* ptr) { return ptr && ((uintptr_t)ptr & 15u) != 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+__global__ void fill_or_copy(const float* src, float* dst, long long n) {
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+int set_state(const float* src, float* dst, long long n, hipStream_t st) {
+    if (!dst || dst == src || n == 0) return GDN_OK;
+    long long blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_or_copy, dim3((unsigned)blocks), dim3(256), 0, st, src, dst, n);
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+template <typename E, int ND>
+int run_gdn(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+            const float* state_in, float* state_out, void* out, const gdn_dims_t* d,
+            const Plan& p, hipStream_t st) {
+    char* ws = (char*)d->workspace;
+    float* carry = (float*)(ws + p.off_carry);
+    for (int wi = 0; wi < p.nwin; ++wi) {
+        const int f0 = wi * p.nfw;
+        const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
+        const bool last = wi == p.nwin - 1;
+        P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, (int)p.BH, d->flags,
+                  ws + p.off_a, (float*)(ws + p.off_b)};
+        P2Args a2{ws + p.off_a, (const float*)(ws + p.off_b), wi == 0 ? state_in : carry,
+                  last ? state_out : carry, ws + p.off_c, nf};
+        P3Args a3{q, out, ws + p.off_c, p.T, d->frame_len, f0, nf, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
+        if (launch_gdn_window<E, ND>(a1, a2, a3, st) != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+template <typename E, int ND>
+int run_bc(const void* q, const void* k, const void* v, const float* s_in, const float* z_in,
+           float* s_out, float* z_out, void* out, const gdn_dims_t* d, const Plan& p, hipStream_t st) {
+    char* ws = (char*)d->workspace;
+    float* carry = (float*)(ws + p.off_carry);
+    const unsigned relu = (d->flags & GDN_F_RELU_QK) ? 1u : 0u;
+    for (int wi = 0; wi < p.nwin; ++wi) {
+        const int f0 = wi * p.nfw;
+        const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
+        const bool last = wi == p.nwin - 1;
+        BC1Args a1{k, v, p.T, d->frame_len, f0, nf, relu, (float*)(ws + p.off_a)};
+        BC2Args a2{(const float*)(ws + p.off_a), wi == 0 ? s_in : nullptr, wi == 0 ? z_in : nullptr,
+                   wi == 0 ? nullptr : carry, last ? nullptr : carry, last ? s_out : nullptr,
+                   last ? z_out : nullptr, ws + p.off_c, nf};
+        BC3Args a3{q, out, ws + p.off_c, p.T, d->frame_len, f0, nf, relu, 1e-6f, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
+        if (launch_bc_window<E, ND>(a1, a2, a3, (int)p.BH, st) != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+#define DISPATCH(FN, ...)                                                              \
+    do {                                                                               \
+        if (d->dtype == GDN_BF16) {                                                    \
+            switch (p.nd) {                                                            \
+                case 1: return FN<bf16, 1>(__VA_ARGS__);                               \
+                case 2: return FN<bf16, 2>(__VA_ARGS__);                               \
+                case 4: return FN<bf16, 4>(__VA_ARGS__);                               \
+                case 7: return FN<bf16, 7>(__VA_ARGS__);                               \
+                case 8: return FN<bf16, 8>(__VA_ARGS__);                               \
+            }                                                                          \
+        } else {                                                                       \
+            switch (p.nd) {                                                            \
+                case 1: return FN<float, 1>(__VA_ARGS__);                              \
+                case 2: return FN<float, 2>(__VA_ARGS__);                              \
+                case 4: return FN<float, 4>(__VA_ARGS__);                              \
+                case 7: return FN<float, 7>(__VA_ARGS__);                              \
+                case 8: return FN<float, 8>(__VA_ARGS__);                              \
+            }                                                                          \
+        }                                                                              \
+        return GDN_ERR_UNSUPPORTED;                                                    \
+    } while (0)
+
+int gdn_common(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+               const float* state_in, float* state_out, void* out, const gdn_dims_t* d, void* stream,
+               int entry) {
+    Plan p;
+    int rc = check_dims(d, entry, &p);
+    if (rc != GDN_OK) return rc;
+    const long long nstate = p.BH * d->d_k * d->d_v;
+    const size_t sbytes = (size_t)nstate * 4;
+    hipStream_t st = (hipStream_t)stream;
+    if (p.BH == 0) return GDN_OK;
+    if (d->n_frames == 0) {
+        if (misaligned(state_in) || misaligned(state_out)) return GDN_ERR_ALIGN;
+        return entry == GDN_ENTRY_FORWARD ? set_state(state_in, state_out, nstate, st) : GDN_OK;
+    }
+    const bool additive = (d->flags & GDN_F_ADDITIVE) != 0;
+    if (!q || !k || !v || !out) return GDN_ERR_NULL;
+    if (!additive && (!alpha || !beta)) return GDN_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(alpha) ||
+        misaligned(beta) || misaligned(state_in) || misaligned(state_out) || misaligned(d->workspace))
+        return GDN_ERR_ALIGN;
+    if (!d->workspace || d->workspace_bytes < p.total) return GDN_ERR_WORKSPACE;
+    const size_t tbytes = (size_t)p.BH * p.T * d->d_k * p.es;
+    const size_t obytes = (size_t)p.BH * p.T * d->d_k * ((d->flags & GDN_F_OUT_F32) ? 4 : p.es);
+    const size_t gbytes = (size_t)p.BH * p.T * 4;
+    const void* ins[] = {q, k, v, additive ? nullptr : alpha, additive ? nullptr : beta, state_in, state_out};
+    const size_t lens[] = {tbytes, tbytes, tbytes, gbytes, gbytes, sbytes, sbytes};
+    for (int i = 0; i < 7; ++i) {
+        if (overlap(out, obytes, ins[i], lens[i])) return GDN_ERR_ALIAS;
+        if (overlap(d->workspace, p.total, ins[i], lens[i])) return GDN_ERR_ALIAS;
+    }
+    if (overlap(out, obytes, d->workspace, p.total)) return GDN_ERR_ALIAS;
+    if (state_out && state_out != state_in && overlap(state_out, sbytes, state_in, sbytes)) return GDN_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(state_out, sbytes, ins[i], lens[i])) return GDN_ERR_ALIAS;
+    DISPATCH(run_gdn, q, k, v, alpha, beta, state_in, entry == GDN_ENTRY_FORWARD ? state_out : nullptr,
+             out, d, p, st);
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+GDN_API int gdn_frame_forward(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* state_in, float* state_out, void* out,
+                              const gdn_dims_t* dims, void* stream) {
+    return gdn_common(q, k, v, alpha, beta, state_in, state_out, out, dims, stream, GDN_ENTRY_FORWARD);
+}
+
+GDN_API int gdn_frame_forward_readonly(const void* q, const void* k, const void* v, const float* alpha,
+                                       const float* beta, const float* state_in, void* out,
+                                       const gdn_dims_t* dims, void* stream) {
+    return gdn_common(q, k, v, alpha, beta, state_in, nullptr, out, dims, stream, GDN_ENTRY_READONLY);
+}
+
+GDN_API int linear_attn_block_causal(const void* q, const void* k, const void* v, const float* state_in,
+                                     const float* z_in, float* state_out, float* z_out, void* out,
+                                     const gdn_dims_t* dims, void* stream) {
+    const gdn_dims_t* d = dims;
+    Plan p;
+    int rc = check_dims(d, GDN_ENTRY_BLOCK_CAUSAL, &p);
+    if (rc != GDN_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const long long ns = p.BH * d->d_k * d->d_v, nz = p.BH * d->d_k;
+    const size_t sbytes = (size_t)ns * 4, zbytes = (size_t)nz * 4;
+    if (p.BH == 0) return GDN_OK;
+    if (misaligned(state_in) || misaligned(state_out) || misaligned(z_in) || misaligned(z_out)) return GDN_ERR_ALIGN;
+    if (d->n_frames == 0) {
+        rc = set_state(state_in, state_out, ns, st);
+        return rc != GDN_OK ? rc : set_state(z_in, z_out, nz, st);
+    }
+    if (!q || !k || !v || !out) return GDN_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(d->workspace))
+        return GDN_ERR_ALIGN;
+    if (!d->workspace || d->workspace_bytes < p.total) return GDN_ERR_WORKSPACE;
+    const size_t tbytes = (size_t)p.BH * p.T * d->d_k * p.es;
+    const size_t obytes = (size_t)p.BH * p.T * d->d_k * ((d->flags & GDN_F_OUT_F32) ? 4 : p.es);
+    const void* ins[] = {q, k, v, state_in, z_in, state_out, z_out};
+    const size_t lens[] = {tbytes, tbytes, tbytes, sbytes, zbytes, sbytes, zbytes};
+    for (int i = 0; i < 7; ++i) {
+        if (overlap(out, obytes, ins[i], lens[i])) return GDN_ERR_ALIAS;
+        if (overlap(d->workspace, p.total, ins[i], lens[i])) return GDN_ERR_ALIAS;
+    }
+    if (overlap(out, obytes, d->workspace, p.total)) return GDN_ERR_ALIAS;
+    if (state_out && state_out != state_in && overlap(state_out, sbytes, state_in, sbytes)) return GDN_ERR_ALIAS;
+    if (z_out && z_out != z_in && overlap(z_out, zbytes, z_in, zbytes)) return GDN_ERR_ALIAS;
+    for (int i = 0; i < 3; ++i)
+        if (overlap(state_out, sbytes, ins[i], lens[i]) || overlap(z_out, zbytes, ins[i], lens[i]))
+            return GDN_ERR_ALIAS;
+    DISPATCH(run_bc, q, k, v, state_in, z_in, state_out, z_out, out, d, p, st);
+}
+
+GDN_API size_t gdn_workspace_bytes(const gdn_dims_t* dims, int entry) {
+    if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_BLOCK_CAUSAL) return 0;
+    Plan p;
+    if (check_dims(dims, entry, &p) != GDN_OK) return 0;
+    return p.total;
+}
+
+GDN_API const char* gdn_status_str(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_DIMS: return "invalid or inconsistent sizes";
+        case GDN_ERR_DTYPE: return "unsupported dtype (expected GDN_BF16 or GDN_F32)";
+        case GDN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case GDN_ERR_ALIAS: return "output overlaps an input, a state or the workspace";
+        case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_workspace_bytes()";
+        case GDN_ERR_UNSUPPORTED: return "unsupported head dimension or flag";
+        case GDN_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+GDN_API int gdn_abi_version(void) { return GDN_ABI_VERSION; }

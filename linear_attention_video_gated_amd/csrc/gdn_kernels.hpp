@@ -1,0 +1,97 @@
+// gdn_kernels.hpp -- argument blocks and launcher declarations shared by the kernel
+// sources and the C ABI layer.  Workspace formats (per (b, h, frame) "unit", frames of
+// one window stored contiguously per (b, h)):
+//   Apack  A_f^T as K32 A-operand fragments, PAIR slot map over k_in: ND x KB fragments
+//          of 64 lanes x 8 elements (dtype of the inputs); for bf16 a hi set then a lo set.
+//   Bt     B_f as accumulator tiles: ND slices x ND tiles x 64 lanes x 4 fp32.
+//   Spack  S_f as K32 A-operand fragments, IDENT slot map over d_k: ND x KB fragments
+//          (bf16: hi set then lo set).
+//   BCpart block-causal per-frame sums phi(K)^T [V | 1]: ND x (ND+1) accumulator tiles.
+//   BCpack block-causal S_f^T and z_f as K32 A-operand fragments: (ND+1) x KB fragments
+//          (bf16: hi set then lo set).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn {
+
+struct P1Args {
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    long long T;        // tokens per (b, h)
+    int frame_len;
+    int f0;             // first frame of the window
+    int nf;             // frames in the window
+    int BH;
+    unsigned flags;     // bit 0: normalise k, bit 1: additive
+    void* Apack;
+    float* Bt;
+};
+
+struct P2Args {
+    const void* Apack;
+    const float* Bt;
+    const float* state_src;  // [BH, d, d] or NULL (zero state)
+    float* state_dst;        // [BH, d, d] or NULL
+    void* Spack;
+    int nf;
+};
+
+struct P3Args {
+    const void* q;
+    void* out;
+    const void* Spack;
+    long long T;
+    int frame_len;
+    int f0;
+    int nf;
+    int out_f32;        // out is float32 (else the input dtype)
+};
+
+struct BC1Args {
+    const void* k;
+    const void* v;
+    long long T;
+    int frame_len;
+    int f0;
+    int nf;
+    unsigned relu;
+    float* part;
+};
+
+struct BC2Args {
+    const float* part;
+    const float* s_in;   // [BH, d_k, d_v] or NULL (window 0 only)
+    const float* z_in;   // [BH, d_k] or NULL
+    const float* carry_in;  // tile-layout carry from the previous window or NULL
+    float* carry_out;       // tile-layout carry for the next window or NULL
+    float* s_out;        // [BH, d_k, d_v] or NULL (last window only)
+    float* z_out;        // [BH, d_k] or NULL
+    void* pack;
+    int nf;
+};
+
+struct BC3Args {
+    const void* q;
+    void* out;
+    const void* pack;
+    long long T;
+    int frame_len;
+    int f0;
+    int nf;
+    unsigned relu;
+    float eps;
+    int out_f32;
+};
+
+template <typename E, int ND>
+hipError_t launch_gdn_window(const P1Args&, const P2Args&, const P3Args&, hipStream_t);
+template <typename E, int ND>
+hipError_t launch_bc_window(const BC1Args&, const BC2Args&, const BC3Args&, int BH, hipStream_t);
+
+size_t gdn_unit_bytes(int nd, int esize, size_t* apack, size_t* bt, size_t* spack);
+size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack);
+
+}  // namespace gdn

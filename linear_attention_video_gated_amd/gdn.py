@@ -1,0 +1,220 @@
+"""Python binding of ``libgdn_mi355x.so`` (the C ABI of ``include/gdn.h``).
+
+Argument marshalling only: tensors are passed as device pointers, the stream is torch's
+current stream on the tensors' device, and the scratch workspace is a torch allocation.
+Every step of the computation runs in the library's HIP kernels; if the library is not
+built, importing works but every call raises ``GdnLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn_mi355x.so")
+
+GDN_BF16, GDN_F32 = 0, 1
+NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32 = 1, 2, 4, 8
+ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL = 0, 1, 2
+EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "linear_attn_block_causal",
+           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version")
+
+
+class GdnLibraryMissing(RuntimeError):
+    pass
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("gdn error %d: %s" % (code, msg))
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("n_frames", ctypes.c_int32),
+                ("frame_len", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the shared library (raises GdnLibraryMissing when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GdnLibraryMissing("%s not found: run `python -m linear_attention_video_gated_amd.build`"
+                                    % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp = ctypes.c_void_p, ctypes.c_void_p
+        dp = ctypes.POINTER(Dims)
+        L.gdn_frame_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
+        L.gdn_frame_forward.restype = ctypes.c_int
+        L.gdn_frame_forward_readonly.argtypes = [vp, vp, vp, fp, fp, fp, vp, dp, vp]
+        L.gdn_frame_forward_readonly.restype = ctypes.c_int
+        L.linear_attn_block_causal.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
+        L.linear_attn_block_causal.restype = ctypes.c_int
+        L.gdn_workspace_bytes.argtypes = [dp, ctypes.c_int]
+        L.gdn_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_status_str.argtypes = [ctypes.c_int]
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(code):
+    return lib().gdn_status_str(int(code)).decode()
+
+
+def _check(code):
+    if code != 0:
+        raise GdnError(code, status_str(code))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    if dt == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dt)
+
+
+def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0):
+    return Dims(B, H, n_frames, frame_len, d, d, dtype_code, flags,
+                None if workspace is None else workspace.data_ptr(), nbytes)
+
+
+def workspace_bytes(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K,
+                    entry=ENTRY_FORWARD):
+    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(dtype), flags)
+    return lib().gdn_workspace_bytes(ctypes.byref(dims), entry)
+
+
+_ws_cache = {}
+
+
+def _workspace(device, nbytes):
+    """A cached uint8 device buffer of at least nbytes (grown on demand, per device)."""
+    if nbytes == 0:
+        return None
+    key = torch.device(device)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shapes(q, k, v, n_frames, frame_len):
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, T, d] with equal shapes")
+    B, H, T, d = q.shape
+    if T != n_frames * frame_len:
+        raise ValueError("T=%d != n_frames*frame_len=%d" % (T, n_frames * frame_len))
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    return B, H, T, d
+
+
+def _out(q, out, out_dtype, flags):
+    """Allocate / check the output; float32 output of bf16 inputs sets OUT_F32."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous device tensor shaped like q")
+    if out.dtype == torch.float32:
+        flags |= OUT_F32
+    elif out.dtype != q.dtype:
+        raise ValueError("out must have q's dtype or float32")
+    return out, flags
+
+
+def _f32(t, shape, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or not t.is_cuda:
+        raise ValueError("%s must be a contiguous float32 device tensor of shape %s" % (name, tuple(shape)))
+    return t
+
+
+def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
+                  out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None):
+    """gdn_frame_forward.  Returns (out [B,H,T,d], state_out [B,H,d,d] float32 or None).
+    out_dtype=torch.float32 (or a float32 ``out``) returns the unrounded float32 result."""
+    B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
+    alpha = _f32(alpha, (B, H, T), "alpha")
+    beta = _f32(beta, (B, H, T), "beta")
+    state_in = _f32(state_in, (B, H, d, d), "state_in")
+    out, flags = _out(q, out, out_dtype, flags)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    state_out = _f32(state_out, (B, H, d, d), "state_out")
+    code = _dtype_code(q.dtype)
+    need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
+                                     ENTRY_FORWARD)
+    ws = _workspace(q.device, need)
+    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel())
+    _check(lib().gdn_frame_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+                                   _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q.device, stream)))
+    return out, state_out
+
+
+def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, out=None,
+                           flags=NORMALIZE_K, stream=None, out_dtype=None):
+    """gdn_frame_forward_readonly.  Returns out; state_in is never written."""
+    B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
+    alpha = _f32(alpha, (B, H, T), "alpha")
+    beta = _f32(beta, (B, H, T), "beta")
+    state_in = _f32(state_in, (B, H, d, d), "state_in")
+    out, flags = _out(q, out, out_dtype, flags)
+    code = _dtype_code(q.dtype)
+    need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
+                                     ENTRY_READONLY)
+    ws = _workspace(q.device, need)
+    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel())
+    _check(lib().gdn_frame_forward_readonly(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                            _ptr(state_in), _ptr(out), ctypes.byref(dims),
+                                            _stream(q.device, stream)))
+    return out
+
+
+def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=None, state_out=None,
+                             z_out=None, out=None, flags=RELU_QK, return_state=True, stream=None,
+                             out_dtype=None):
+    """linear_attn_block_causal.  Returns (out, state_out [B,H,d,d], z_out [B,H,d])."""
+    B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
+    state_in = _f32(state_in, (B, H, d, d), "state_in")
+    z_in = _f32(z_in, (B, H, d), "z_in")
+    out, flags = _out(q, out, out_dtype, flags)
+    if return_state:
+        if state_out is None:
+            state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+        if z_out is None:
+            z_out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    state_out = _f32(state_out, (B, H, d, d), "state_out")
+    z_out = _f32(z_out, (B, H, d), "z_out")
+    code = _dtype_code(q.dtype)
+    need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
+                                     ENTRY_BLOCK_CAUSAL)
+    ws = _workspace(q.device, need)
+    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel())
+    _check(lib().linear_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(z_in),
+                                          _ptr(state_out), _ptr(z_out), _ptr(out), ctypes.byref(dims),
+                                          _stream(q.device, stream)))
+    return out, state_out, z_out

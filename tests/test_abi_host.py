@@ -1,0 +1,138 @@
+"""The C ABI library loads, exports exactly what include/gdn.h declares, and rejects bad
+arguments on the host, before anything is enqueued (no GPU needed: every call here
+returns from argument checking)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_video_gated_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdn.LIB_PATH), reason="library not built")
+
+FAKE = 0x7F0000000000  # a 256-byte aligned non-NULL address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared_functions() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol_and_nothing_else():
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln and not ln.split()[-1].startswith("_")})
+    assert exported == declared_functions()
+    L = gdn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name)
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.lib().gdn_abi_version() == 1
+    for code in range(0, -9, -1):
+        s = gdn.status_str(code)
+        assert s and s != "unknown status"
+    assert gdn.status_str(-99) == "unknown status"
+
+
+def dims(B=1, H=2, F=3, N=16, d=32, dtype=gdn.GDN_BF16, flags=gdn.NORMALIZE_K, ws=None, nbytes=0):
+    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes)
+
+
+def wsb(dm, entry=gdn.ENTRY_FORWARD):
+    return gdn.lib().gdn_workspace_bytes(ctypes.byref(dm), entry)
+
+
+def fwd(dm, q=FAKE, k=FAKE + 2 ** 28, v=FAKE + 2 ** 29, a=FAKE + 2 ** 30, b=FAKE + 2 ** 31,
+        s_in=None, s_out=None, out=FAKE + 2 ** 32):
+    return gdn.lib().gdn_frame_forward(q, k, v, a, b, s_in, s_out, out, ctypes.byref(dm), None)
+
+
+def test_workspace_is_bounded_independently_of_frame_count():
+    sizes = [wsb(dims(B=1, H=20, F=F, N=880, d=112)) for F in (1, 100, 240, 1000, 100000)]
+    assert sizes[0] > 0
+    assert max(sizes) <= 1.05 * wsb(dims(B=1, H=20, F=8192 // 20 + 1, N=880, d=112))
+    # and it does not depend on the frame length at all
+    assert wsb(dims(F=240, N=880, d=112)) == wsb(dims(F=240, N=16, d=112))
+
+
+def test_workspace_zero_for_invalid_or_empty():
+    assert wsb(dims(d=48)) == 0            # unsupported d
+    assert wsb(dims(dtype=7)) == 0
+    assert wsb(dims(F=0)) == 0
+    assert wsb(dims(), entry=9) == 0
+
+
+@pytest.mark.parametrize("field,val,code", [
+    ("dtype", 5, -3), ("B", -1, -2), ("frame_len", 0, -2), ("n_frames", -2, -2),
+    ("d_k", 48, -7), ("flags", 16, -7),
+])
+def test_bad_dims_rejected(field, val, code):
+    dm = dims()
+    setattr(dm, field, val)
+    assert fwd(dm) == code
+
+
+def test_dv_must_equal_dk():
+    dm = dims()
+    dm.d_v = 64
+    assert fwd(dm) == -7
+
+
+def test_null_dims_and_pointers():
+    assert gdn.lib().gdn_frame_forward(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == -1
+    assert fwd(dims(), q=None) == -1
+    assert fwd(dims(), a=None) == -1
+    assert fwd(dims(flags=gdn.NORMALIZE_K | gdn.ADDITIVE), a=None, b=None) == -6  # gates optional, then workspace
+
+
+def test_misaligned_pointer_rejected():
+    dm = dims(ws=FAKE + 2 ** 34, nbytes=1 << 30)
+    assert fwd(dm, q=FAKE + 2) == -4
+    assert fwd(dm, s_in=FAKE + 2 ** 33 + 8) == -4
+
+
+def test_missing_or_small_workspace_rejected():
+    dm = dims()
+    assert fwd(dm) == -6
+    need = wsb(dm)
+    dm.workspace, dm.workspace_bytes = FAKE + 2 ** 34, need - 1
+    assert fwd(dm) == -6
+
+
+def test_overlapping_output_rejected():
+    dm = dims(ws=FAKE + 2 ** 34, nbytes=1 << 30)
+    assert fwd(dm, out=FAKE) == -5                      # out == q
+    assert fwd(dm, out=FAKE + 2 ** 28 + 256) == -5      # out inside k
+    assert fwd(dm, out=FAKE + 2 ** 34 + 4096) == -5     # out inside the workspace
+    assert fwd(dm, s_out=FAKE + 2 ** 29) == -5          # state_out inside v
+
+
+def test_block_causal_flag_rules():
+    dm = dims(flags=gdn.NORMALIZE_K)
+    assert gdn.lib().linear_attn_block_causal(FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                              ctypes.byref(dm), None) == -7
+    dm = dims(flags=gdn.RELU_QK)
+    assert gdn.lib().linear_attn_block_causal(FAKE, FAKE + 2 ** 28, FAKE + 2 ** 29, None, None, None, None,
+                                              FAKE + 2 ** 30, ctypes.byref(dm), None) == -6
+
+
+def test_empty_batch_is_a_noop():
+    assert fwd(dims(B=0)) == 0
+    assert fwd(dims(H=0), q=None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", "/nonexistent/libgdn_mi355x.so")
+    with pytest.raises(gdn.GdnLibraryMissing):
+        gdn.lib()
