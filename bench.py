@@ -1,0 +1,290 @@
+"""Benchmark of the frame-wise gated delta rule forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one gdn_frame_forward call over the whole workload (default: the 60 s
+720p-shaped rollout, B=1, H=20, d=112, 240 frames x 880 tokens = 211,200 tokens), with
+inputs already resident in HBM.  Prints one JSON line:
+  value         tokens/s = B*T / (time per call)
+  roofline      the dominant kernel's achieved algorithmic bandwidth against 8 TB/s; its
+                duration comes from HIP events the library records around each launch
+  path          the same for the whole call (all three kernels)
+  cpu_baseline  the CPU oracle (float64, token by token, OpenMP) on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd tokens/s (720p 60s, H=20 d=112) + % of MFMA/HBM roofline"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["linear_attention_video_gated_amd/csrc/gdn_frame.hip",
+                  "linear_attention_video_gated_amd/csrc/block_causal.hip",
+                  "linear_attention_video_gated_amd/csrc/common.hpp"]
+
+# Per-kernel algorithmic bytes per token-head (d, element size es):
+#   gdn_frame_affine  reads k, v and the two gates:  2*d*es + 8
+#   gdn_frame_chain   per-frame state maps only (no per-token algorithmic traffic)
+#   gdn_frame_readout reads q, writes o:             2*d*es
+#   bc_partial        reads k, v:                    2*d*es
+#   bc_scan           per-frame sums only
+#   bc_readout        reads q, writes o:             2*d*es
+GDN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_frame_readout")
+BC_KERNELS = ("bc_partial", "bc_scan", "bc_readout")
+
+
+def kernel_bytes_per_token_head(kind, d, es):
+    if kind == "block_causal":
+        return {"bc_partial": 2 * d * es, "bc_scan": 0, "bc_readout": 2 * d * es}
+    return {"gdn_frame_affine": 2 * d * es + 8, "gdn_frame_chain": 0, "gdn_frame_readout": 2 * d * es}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (same runtime)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = h
+        return arr
+
+    def elapsed_ms(self, a, b):
+        self.rt.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for h in arr:
+            self.rt.hipEventDestroy(h)
+
+
+def read_counters(workload):
+    """HBM bytes per launch of the dominant kernel from a committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "counters_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return {"kernel": kv["kernel"], "bytes": float(kv["hbm_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def setup(wl, device):
+    import torch
+    from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if wl.kind == "block_causal":
+        return block_causal_inputs(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
+                                   workload_id=wl.wid, device=device)
+    return gdn_inputs(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt, workload_id=wl.wid,
+                      device=device, state_std=wl.state_std)
+
+
+def make_step(wl, inp, events=None):
+    """One pass of the hot path: a closure that enqueues it on the current stream."""
+    from linear_attention_video_gated_amd import gdn
+    import torch
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    out = torch.empty_like(q)
+    if wl.kind == "block_causal":
+        st = torch.empty(wl.B, wl.H, wl.d, wl.d, device=q.device)
+        z = torch.empty(wl.B, wl.H, wl.d, device=q.device)
+        return lambda ev=None: gdn.linear_attn_block_causal(q, k, v, wl.n_frames, wl.frame_len, out=out,
+                                                            state_out=st, z_out=z, events=ev)
+    st = torch.empty(wl.B, wl.H, wl.d, wl.d, device=q.device)
+    if wl.kind == "stream":
+        # denoising steps against a read-only state, then one commit of the frame
+        def step(ev=None):
+            for _ in range(wl.steps):
+                gdn.frame_forward_readonly(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
+                                           state_in=inp["state_in"], out=out, events=ev)
+            gdn.frame_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
+                              state_in=inp["state_in"], state_out=st, out=out)
+        return step
+    return lambda ev=None: gdn.frame_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
+                                             state_in=inp["state_in"], state_out=st, out=out, events=ev)
+
+
+def copy_bandwidth_gbps(device, nbytes=2 << 30):
+    """Device-to-device copy rate (read + write bytes / time): the reachable HBM rate."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(5):
+        b.copy_(a)
+    t1.record()
+    t1.synchronize()
+    ms = t0.elapsed_time(t1) / 5
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(wl, inp, budget_heads=16, frames=None):
+    """The oracle (as it stands) on a bounded sample of the same inputs, on host cores."""
+    import numpy as np
+    import oracle
+    ncpu = os.cpu_count() or 1
+    cores = max(1, min(16, ncpu, wl.B * wl.H))
+    heads = min(wl.H, budget_heads)
+    frames = wl.n_frames if frames is None else min(frames, wl.n_frames)
+    T = frames * wl.frame_len
+    take = lambda x: x[:1, :heads, :T].detach().float().cpu().numpy() if x is not None else None
+    q, k, v = take(inp["q"]), take(inp["k"]), take(inp["v"])
+    t0 = time.perf_counter()
+    if wl.kind == "block_causal":
+        oracle.linear_attn_block_causal(q, k, v, frames, wl.frame_len, n_threads=cores)
+    else:
+        a, b = take(inp["alpha"]), take(inp["beta"])
+        s_in = inp["state_in"][:1, :heads].float().cpu().numpy() if inp["state_in"] is not None else None
+        oracle.gdn_forward(q, k, v, a, b, frames, wl.frame_len, state_in=s_in, n_threads=cores)
+    dt = time.perf_counter() - t0
+    # tokens/s of the whole workload: the sample covers heads/H of each token's work
+    value = T * heads / wl.H / dt
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "B=1, %d of %d heads, %d of %d frames x %d tokens (%.1f s on %d threads, float64)"
+                      % (heads, wl.H, frames, wl.n_frames, wl.frame_len, dt, cores)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gdn_720p_60s")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 2 GiB device copy (a known-size kernel for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (got --gpus %d); the multi-GPU sharding "
+              "is a design note, not an implemented path" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_video_gated_amd import gdn
+    from linear_attention_video_gated_amd.workloads import WORKLOADS
+    gdn.lib()
+    wl = WORKLOADS[args.workload]
+    dev = "cuda:0"
+    inp = setup(wl, dev)
+    step = make_step(wl, inp)
+    hip = HipEvents()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel times from the events the library records around its launches
+    nk = 3
+    ev = [hip.create(4) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(ev[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    names = BC_KERNELS if wl.kind == "block_causal" else GDN_KERNELS
+    kms = [0.0] * nk
+    for e in ev:
+        for j in range(nk):
+            kms[j] += hip.elapsed_ms(e[j], e[j + 1])
+        hip.destroy(e)
+    kms = [x / args.steps for x in kms]
+    if wl.kind == "stream":  # events bracket the last read-only call of each step
+        pass
+    calls = wl.steps + 1 if wl.kind == "stream" else 1
+
+    tokens = wl.B * wl.T * calls
+    value = wl.B * wl.T / (ms_step * 1e-3)
+    es = 2 if wl.dtype == "bf16" else 4
+    th = wl.B * wl.H * wl.T
+    per = kernel_bytes_per_token_head(wl.kind, wl.d, es)
+    j = max(range(nk), key=lambda i: kms[i])
+    kname = names[j]
+    kbytes = per[kname] * th
+    achieved = kbytes / (kms[j] * 1e-3) / 1e9
+    counters = read_counters(args.workload)
+    traffic = counters["bytes"] if counters and counters["kernel"] == kname else None
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel_ms": round(kms[j], 4),
+                "algorithmic_bytes": kbytes,
+                "all_kernels_ms": {n: round(x, 4) for n, x in zip(names, kms)}}
+    path_bytes = sum(per.values()) * th * calls
+    path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
+    path = {"algorithmic_bytes_per_call": sum(per.values()) * th, "achieved": round(path_gbps, 1),
+            "unit": "GB/s", "frac_of_8TBps": round(path_gbps / HBM_PEAK_GBPS, 4)}
+
+    extra = {}
+    if args.copy_calib:
+        extra["hbm_copy_GBps"] = round(copy_bandwidth_gbps(dev), 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded; shapes of 720p/480p latent frames)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "d": wl.d, "n_frames": wl.n_frames,
+                   "frame_len": wl.frame_len, "tokens": wl.T, "calls_per_step": calls,
+                   "parallelism": "single GPU"},
+        "roofline": roofline, "path": path, "cpu_baseline": cpu,
+        "wall_s_timed": round(t_wall, 3), "kernel_source_sha": kernel_source_hash(),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,6 +98,10 @@ typedef struct gdn_dims {
     uint32_t flags;               /* GDN_F_* bits                                        */
     void* workspace;              /* device scratch, >= gdn_workspace_bytes() bytes      */
     size_t workspace_bytes;
+    void* const* phase_events;    /* optional, may be NULL: 4 caller-created hipEvent_t
+                                     recorded on `stream` before the first launch and after
+                                     each of the three launches of the first window, for
+                                     per-kernel timing; nothing else touches them         */
 } gdn_dims_t;
 
 /*

@@ -207,19 +207,22 @@ __global__ __launch_bounds__(256) void bc_readout(BC3Args a) {
 }
 
 template <typename E, int ND>
-hipError_t launch_bc_window(const BC1Args& a1, const BC2Args& a2, const BC3Args& a3, int BH, hipStream_t st) {
+hipError_t launch_bc_window(const BC1Args& a1, const BC2Args& a2, const BC3Args& a3, int BH, hipStream_t st,
+                            void* const* ev) {
+    hipError_t e = record(ev, 0, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bc_partial<E, ND>), dim3(a1.nf, BH), dim3(256), 0, st, a1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((bc_scan<E, ND>), dim3(ND * (ND + 1), BH), dim3(64), 0, st, a2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 2, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((bc_readout<E, ND>), dim3(a3.nf, BH), dim3(256), 0, st, a3);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return record(ev, 3, st);
 }
 
-#define BC_INST(E, ND) \
-    template hipError_t launch_bc_window<E, ND>(const BC1Args&, const BC2Args&, const BC3Args&, int, hipStream_t);
+#define BC_INST(E, ND)                                                                                     \
+    template hipError_t launch_bc_window<E, ND>(const BC1Args&, const BC2Args&, const BC3Args&, int, hipStream_t, \
+                                                void* const*);
 BC_INST(bf16, 1) BC_INST(bf16, 2) BC_INST(bf16, 4) BC_INST(bf16, 7) BC_INST(bf16, 8)
 BC_INST(float, 1) BC_INST(float, 2) BC_INST(float, 4) BC_INST(float, 7) BC_INST(float, 8)
 

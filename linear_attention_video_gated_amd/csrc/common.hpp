@@ -25,6 +25,8 @@ namespace gdn {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short short4_ __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -67,6 +69,7 @@ template <> struct Ops<bf16> {
     }
     static __device__ __forceinline__ F4 ld4(const bf16* p) { return *(const F4*)p; }
     static __device__ __forceinline__ void st8(bf16* p, F8 x) { *(F8*)p = x; }
+    static __device__ __forceinline__ void st2(bf16* p, bf16 a, bf16 b) { *(bf16x2*)p = bf16x2{a, b}; }
     static __device__ __forceinline__ void st4(bf16* p, f32x4 x) { *(F4*)p = pack4(x); }
     static __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
         F4 x = *(const F4*)p;
@@ -132,6 +135,7 @@ template <> struct Ops<float> {
         *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
     }
     static __device__ __forceinline__ void st4(float* p, f32x4 x) { *(f32x4*)p = x; }
+    static __device__ __forceinline__ void st2(float* p, float a, float b) { *(f32x2*)p = f32x2{a, b}; }
     static __device__ __forceinline__ f32x4 ld4f(const float* p) { return *(const f32x4*)p; }
     static __device__ __forceinline__ F8 zero8() { return F8{0, 0, 0, 0, 0, 0, 0, 0}; }
     // fp32 operands need no split: lo is identically zero and never used

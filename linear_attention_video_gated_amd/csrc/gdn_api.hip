@@ -120,7 +120,8 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         P2Args a2{ws + p.off_a, (const float*)(ws + p.off_b), wi == 0 ? state_in : carry,
                   last ? state_out : carry, ws + p.off_c, nf};
         P3Args a3{q, out, ws + p.off_c, p.T, d->frame_len, f0, nf, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
-        if (launch_gdn_window<E, ND>(a1, a2, a3, st) != hipSuccess) return GDN_ERR_HIP;
+        if (launch_gdn_window<E, ND>(a1, a2, a3, st, wi == 0 ? d->phase_events : nullptr) != hipSuccess)
+            return GDN_ERR_HIP;
     }
     return GDN_OK;
 }
@@ -140,7 +141,8 @@ int run_bc(const void* q, const void* k, const void* v, const float* s_in, const
                    wi == 0 ? nullptr : carry, last ? nullptr : carry, last ? s_out : nullptr,
                    last ? z_out : nullptr, ws + p.off_c, nf};
         BC3Args a3{q, out, ws + p.off_c, p.T, d->frame_len, f0, nf, relu, 1e-6f, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
-        if (launch_bc_window<E, ND>(a1, a2, a3, (int)p.BH, st) != hipSuccess) return GDN_ERR_HIP;
+        if (launch_bc_window<E, ND>(a1, a2, a3, (int)p.BH, st, wi == 0 ? d->phase_events : nullptr) != hipSuccess)
+            return GDN_ERR_HIP;
     }
     return GDN_OK;
 }

@@ -61,7 +61,7 @@ template <typename E, int ND> struct P1 {
     static constexpr int OFF_TD = OFF_KT + KT_B;
     static constexpr int OFF_W = OFF_TD + TD_B;
     static constexpr int OFF_SC = OFF_W + W_B;
-    static constexpr int LDS_B = OFF_SC + 5 * 64 * 4 + 64;
+    static constexpr int LDS_B = OFF_SC + 6 * 64 * 4 + 64;
     static_assert(APK_E * (int)sizeof(E) <= OFF_KT, "A_f staging must fit in sKrow+sVrow");
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
 };
@@ -90,6 +90,7 @@ __global__ __launch_bounds__(64 * ND, 1) void gdn_frame_affine(P1Args a) {
     float* sN = sBeta + 192;
     float* sG = sBeta + 256;
     float* sGam = sBeta + 320;
+    float* sAlp = sBeta + 336;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, g = lane >> 4;
@@ -111,43 +112,77 @@ __global__ __launch_bounds__(64 * ND, 1) void gdn_frame_affine(P1Args a) {
         XB[t] = zero4();
     }
 
+    // Chunk loads: thread (p = tid % 32, colblock cb) owns token rows 2p and 2p+1 of a
+    // 16-byte column block; the next chunk is fetched into registers while this one is
+    // being computed.  Row pairs let the transposed copy use one 4-byte (bf16) store per
+    // element pair.
+    constexpr int CB = D / EPV;                 // 16-byte column blocks per row
+    constexpr int NCB = L::NT / 32;             // column blocks covered per pass
+    constexpr int NPASS = (CB + NCB - 1) / NCB;
+    const int pr = tid & 31, cb0 = tid >> 5;
+    V16 rk[NPASS][2], rv[NPASS][2];
+    float ra = 0.f, rb = 0.f;
+    auto fetch = [&](int c0, int Cc) {
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+            const int cb = cb0 + ps * NCB;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = 2 * pr + h;
+                if (cb < CB && row < Cc) {
+                    rk[ps][h] = *(const V16*)(kp + (long long)(c0 + row) * D + cb * EPV);
+                    rv[ps][h] = *(const V16*)(vp + (long long)(c0 + row) * D + cb * EPV);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < EPV; ++j) rk[ps][h][j] = rv[ps][h][j] = (E)0.f;
+                }
+            }
+        }
+        if (tid < 64 && tid < Cc && !additive) {
+            ra = a.alpha[tok0 + c0 + tid];
+            rb = a.beta[tok0 + c0 + tid];
+        }
+    };
+
     const int nch = (N + 63) / 64;
+    fetch(0, min(64, N));
     for (int ch = 0; ch < nch; ++ch) {
         const int c0 = ch * 64;
         const int Cc = min(64, N - c0);
         __syncthreads();  // readers of the previous chunk are done
-        // ---- load K (row-major + transposed) and V (row-major); zero padding
+        // ---- registers -> LDS: K row-major and transposed, V row-major; zero padding
         {
-            constexpr int UPR = DP / EPV;
-            for (int u = tid; u < 64 * UPR; u += L::NT) {
-                const int row = u / UPR, col = (u % UPR) * EPV;
-                V16 val;
-                if (row < Cc && col < D) {
-                    val = *(const V16*)(kp + (long long)(c0 + row) * D + col);
-                } else {
 #pragma unroll
-                    for (int j = 0; j < EPV; ++j) val[j] = (E)0.f;
-                }
-                *(V16*)(sKrow + row * L::KR_P + col) = val;
-                if (col < D) {
+            for (int ps = 0; ps < NPASS; ++ps) {
+                const int cb = cb0 + ps * NCB;
+                if (cb < CB) {
 #pragma unroll
-                    for (int j = 0; j < EPV; ++j) sKt[(col + j) * L::KT_P + row] = val[j];
+                    for (int h = 0; h < 2; ++h) {
+                        *(V16*)(sKrow + (2 * pr + h) * L::KR_P + cb * EPV) = rk[ps][h];
+                        *(V16*)(sVrow + (2 * pr + h) * L::VR_P + cb * EPV) = rv[ps][h];
+                    }
+#pragma unroll
+                    for (int j = 0; j < EPV; ++j) {
+                        O::st2(sKt + (cb * EPV + j) * L::KT_P + 2 * pr, rk[ps][0][j], rk[ps][1][j]);
+                    }
                 }
             }
-            constexpr int UPV = D / EPV;
-            for (int u = tid; u < 64 * UPV; u += L::NT) {
-                const int row = u / UPV, col = (u % UPV) * EPV;
-                V16 val;
-                if (row < Cc) {
-                    val = *(const V16*)(vp + (long long)(c0 + row) * D + col);
-                } else {
+            // zero the padded columns D..DP-1 of sKrow (sL overwrote them)
+            constexpr int PADV = (DP - D) / EPV;
+            if (PADV > 0) {
+                V16 z;
 #pragma unroll
-                    for (int j = 0; j < EPV; ++j) val[j] = (E)0.f;
-                }
-                *(V16*)(sVrow + row * L::VR_P + col) = val;
+                for (int j = 0; j < EPV; ++j) z[j] = (E)0.f;
+                for (int u = tid; u < 64 * PADV; u += L::NT)
+                    *(V16*)(sKrow + (u / PADV) * L::KR_P + D + (u % PADV) * EPV) = z;
+            }
+            if (tid < 64) {
+                sAlp[tid] = ra;
+                sBeta[tid] = rb;
             }
         }
         __syncthreads();
+        if (ch + 1 < nch) fetch(c0 + 64, min(64, N - c0 - 64));  // overlaps this chunk's compute
         // ---- per-token scalars: key norm, log-gate prefix, derived scales (wave 0)
         if (w == 0) {
             const int t = lane;
@@ -165,8 +200,8 @@ __global__ __launch_bounds__(64 * ND, 1) void gdn_frame_affine(P1Args a) {
                 if (additive) {
                     be = 1.f;
                 } else {
-                    gl = log2f(fmaxf(a.alpha[tok0 + c0 + t], FLT_MIN));
-                    be = a.beta[tok0 + c0 + t];
+                    gl = log2f(fmaxf(sAlp[t], FLT_MIN));
+                    be = sBeta[t];
                 }
             }
             float Gs = gl;  // inclusive prefix sum over the chunk (log2 units)
@@ -399,24 +434,34 @@ __global__ __launch_bounds__(64) void gdn_frame_chain(P2Args a) {
         const E* ah = (const E*)a.Apack + unit * NS * APK_E;
         const E* al = ah + APK_E;
         const float* bt = a.Bt + unit * (ND * ND * 256) + (long long)s * ND * 256;
+        // issue every load of the frame before the first use
+        F8 fh[ND][KB], fl[ND][KB];
+        f32x4 acc[ND];
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+            acc[t] = *(const f32x4*)(bt + t * 256 + lane * 4);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = ((t * KB + kb) * 64 + lane) * 8;
+                fh[t][kb] = O::ld8(ah + off);
+                fl[t][kb] = O::kSplit ? O::ld8(al + off) : O::zero8();
+            }
+        }
         F8 xh[KB], xl[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             O::split8(X[2 * kb], (2 * kb + 1 < ND) ? X[(2 * kb + 1) % ND] : zero4(), xh[kb], xl[kb]);
 #pragma unroll
         for (int t = 0; t < ND; ++t) {
-            f32x4 acc = *(const f32x4*)(bt + t * 256 + lane * 4);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int off = ((t * KB + kb) * 64 + lane) * 8;
-                const F8 fh = O::ld8(ah + off);
-                acc = O::mma32(fh, xh[kb], acc);
+                acc[t] = O::mma32(fh[t][kb], xh[kb], acc[t]);
                 if (O::kSplit) {
-                    acc = O::mma32(O::ld8(al + off), xh[kb], acc);
-                    acc = O::mma32(fh, xl[kb], acc);
+                    acc[t] = O::mma32(fl[t][kb], xh[kb], acc[t]);
+                    acc[t] = O::mma32(fh[t][kb], xl[kb], acc[t]);
                 }
             }
-            X[t] = acc;
+            X[t] = acc[t];
         }
         // S_f as readout operand (hi, then lo for bf16): fragment (n = s, kb = t/2),
         // lane c + 16 (2 (t%2) + g/2), elements 4 (g%2) .. +3  (IDENT slot map over d_k)
@@ -505,7 +550,8 @@ __global__ __launch_bounds__(256) void gdn_frame_readout(P3Args a) {
 // launchers
 // -------------------------------------------------------------------------------------
 template <typename E, int ND>
-hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p3, hipStream_t st) {
+hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p3, hipStream_t st,
+                             void* const* ev) {
     using L = P1<E, ND>;
     static bool attr_done = false;
     if (!attr_done) {
@@ -515,18 +561,20 @@ hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p
         attr_done = true;
     }
     const int BH = p1.BH;
+    hipError_t e = record(ev, 0, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_frame_affine<E, ND>), dim3(p1.nf, BH), dim3(L::NT), L::LDS_B, st, p1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3(ND, BH), dim3(64), 0, st, p2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 2, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_frame_readout<E, ND>), dim3(p3.nf, BH), dim3(256), 0, st, p3);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return record(ev, 3, st);
 }
 
 #define GDN_INST(E, ND) \
-    template hipError_t launch_gdn_window<E, ND>(const P1Args&, const P2Args&, const P3Args&, hipStream_t);
+    template hipError_t launch_gdn_window<E, ND>(const P1Args&, const P2Args&, const P3Args&, hipStream_t, \
+                                                 void* const*);
 GDN_INST(bf16, 1) GDN_INST(bf16, 2) GDN_INST(bf16, 4) GDN_INST(bf16, 7) GDN_INST(bf16, 8)
 GDN_INST(float, 1) GDN_INST(float, 2) GDN_INST(float, 4) GDN_INST(float, 7) GDN_INST(float, 8)
 

@@ -86,10 +86,16 @@ struct BC3Args {
     int out_f32;
 };
 
+// ev: NULL or 4 events, recorded before the first launch and after each launch.
 template <typename E, int ND>
-hipError_t launch_gdn_window(const P1Args&, const P2Args&, const P3Args&, hipStream_t);
+hipError_t launch_gdn_window(const P1Args&, const P2Args&, const P3Args&, hipStream_t, void* const* ev);
 template <typename E, int ND>
-hipError_t launch_bc_window(const BC1Args&, const BC2Args&, const BC3Args&, int BH, hipStream_t);
+hipError_t launch_bc_window(const BC1Args&, const BC2Args&, const BC3Args&, int BH, hipStream_t,
+                            void* const* ev);
+
+inline hipError_t record(void* const* ev, int i, hipStream_t st) {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+}
 
 size_t gdn_unit_bytes(int nd, int esize, size_t* apack, size_t* bt, size_t* spack);
 size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack);

@@ -36,7 +36,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("n_frames", ctypes.c_int32),
                 ("frame_len", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -89,9 +89,11 @@ def _dtype_code(dt):
     raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dt)
 
 
-def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0):
+def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0, events=None):
+    """events: None or a ctypes array of 4 hipEvent_t handles (per-kernel timing)."""
     return Dims(B, H, n_frames, frame_len, d, d, dtype_code, flags,
-                None if workspace is None else workspace.data_ptr(), nbytes)
+                None if workspace is None else workspace.data_ptr(), nbytes,
+                None if events is None else ctypes.cast(events, ctypes.c_void_p).value)
 
 
 def workspace_bytes(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K,
@@ -154,7 +156,8 @@ def _f32(t, shape, name):
 
 
 def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
-                  out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None):
+                  out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
+                  events=None):
     """gdn_frame_forward.  Returns (out [B,H,T,d], state_out [B,H,d,d] float32 or None).
     out_dtype=torch.float32 (or a float32 ``out``) returns the unrounded float32 result."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
@@ -169,14 +172,14 @@ def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, stat
     need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
                                      ENTRY_FORWARD)
     ws = _workspace(q.device, need)
-    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel())
+    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
     _check(lib().gdn_frame_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
                                    _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q.device, stream)))
     return out, state_out
 
 
 def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, out=None,
-                           flags=NORMALIZE_K, stream=None, out_dtype=None):
+                           flags=NORMALIZE_K, stream=None, out_dtype=None, events=None):
     """gdn_frame_forward_readonly.  Returns out; state_in is never written."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     alpha = _f32(alpha, (B, H, T), "alpha")
@@ -187,7 +190,7 @@ def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=N
     need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
                                      ENTRY_READONLY)
     ws = _workspace(q.device, need)
-    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel())
+    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
     _check(lib().gdn_frame_forward_readonly(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                             _ptr(state_in), _ptr(out), ctypes.byref(dims),
                                             _stream(q.device, stream)))
@@ -196,7 +199,7 @@ def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=N
 
 def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=None, state_out=None,
                              z_out=None, out=None, flags=RELU_QK, return_state=True, stream=None,
-                             out_dtype=None):
+                             out_dtype=None, events=None):
     """linear_attn_block_causal.  Returns (out, state_out [B,H,d,d], z_out [B,H,d])."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     state_in = _f32(state_in, (B, H, d, d), "state_in")
@@ -213,7 +216,7 @@ def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=N
     need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
                                      ENTRY_BLOCK_CAUSAL)
     ws = _workspace(q.device, need)
-    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel())
+    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
     _check(lib().linear_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(z_in),
                                           _ptr(state_out), _ptr(z_out), _ptr(out), ctypes.byref(dims),
                                           _stream(q.device, stream)))

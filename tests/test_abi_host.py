@@ -45,7 +45,7 @@ def test_abi_version_and_status_strings():
 
 
 def dims(B=1, H=2, F=3, N=16, d=32, dtype=gdn.GDN_BF16, flags=gdn.NORMALIZE_K, ws=None, nbytes=0):
-    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes)
+    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None)
 
 
 def wsb(dm, entry=gdn.ENTRY_FORWARD):
