@@ -153,6 +153,28 @@ template <> struct Ops<float> {
 
 template <typename E> __device__ __forceinline__ float tof(E x) { return (float)x; }
 
+// Hardware transcendentals (v_exp_f32, v_log_f32, v_rsq_f32; about 1 ulp).  exp2 of
+// arguments below -126 may flush to zero, which is the correct limit for a decay.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then row broadcasts of lane 15 and lane 31.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+#define GDN_DPP(CTRL, ROWMASK)                                                                        \
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, \
+                                                               ROWMASK, 0xf, false))
+    GDN_DPP(0x111, 0xf);  // row_shr:1
+    GDN_DPP(0x112, 0xf);  // row_shr:2
+    GDN_DPP(0x114, 0xf);  // row_shr:4
+    GDN_DPP(0x118, 0xf);  // row_shr:8
+    GDN_DPP(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    GDN_DPP(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef GDN_DPP
+    return x;
+}
+
 // Split precision: bf16 operands that must carry ~16 significant bits are sent to the
 // matrix cores as hi + lo pairs (hi = RNE(x), lo = RNE(x - hi)); a product a*b is then
 // a_hi*b_hi + a_lo*b_hi + a_hi*b_lo (the lo*lo term is below fp32 accumulation noise).

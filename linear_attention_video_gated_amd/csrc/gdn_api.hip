@@ -16,10 +16,26 @@ namespace {
 
 constexpr long long kMaxUnits = 8192;  // default (b, h, frame) units per window
 
+long long env_ll(const char* name) {
+    const char* e = getenv(name);
+    return e ? atoll(e) : 0;
+}
+
 long long window_units() {
-    const char* e = getenv("GDN_WINDOW_UNITS");
-    const long long v = e ? atoll(e) : 0;
+    const long long v = env_ll("GDN_WINDOW_UNITS");
     return v > 0 ? v : kMaxUnits;
+}
+
+// Frames per group of the gated-delta-rule path: the serial chain steps once per group,
+// and groups of frames form the parallel work of the frame-map kernel, so groups grow
+// only while there are still >= ~4 workgroups per CU (GDN_GROUP_FRAMES overrides).
+int group_frames(long long BH, int nfw) {
+    long long G = env_ll("GDN_GROUP_FRAMES");
+    if (G <= 0) G = (BH * nfw) / 1024;
+    if (G < 1) G = 1;
+    if (G > 8) G = 8;
+    if (G > nfw) G = nfw;
+    return (int)G;
 }
 constexpr size_t kAlign = 256;
 
@@ -41,7 +57,7 @@ int esize_of(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
 // Plan of one call: window size and workspace offsets.
 struct Plan {
     long long BH = 0, T = 0;
-    int nd = 0, es = 0, nfw = 0, nwin = 0;
+    int nd = 0, es = 0, nfw = 0, nwin = 0, G = 1;
     size_t off_a = 0, off_b = 0, off_c = 0, off_carry = 0, total = 0;
 };
 
@@ -75,11 +91,15 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
     } else {
         gdn_unit_bytes(p->nd, p->es, &a, &b, &c);
         carry = (size_t)p->BH * d->d_k * d->d_v * 4;
+        p->G = group_frames(p->BH, p->nfw);
     }
+    // per-group (not per-frame) third region for the gated delta rule
+    const size_t units_c = entry == GDN_ENTRY_BLOCK_CAUSAL ? units
+                                                           : (size_t)p->BH * ((p->nfw + p->G - 1) / p->G);
     p->off_a = 0;
     p->off_b = align_up(units * a);
     p->off_c = p->off_b + align_up(units * b);
-    p->off_carry = p->off_c + align_up(units * c);
+    p->off_carry = p->off_c + align_up(units_c * c);
     p->total = p->off_carry + (p->nwin > 1 ? align_up(carry) : 0);
     return GDN_OK;
 }
@@ -115,11 +135,12 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         const int f0 = wi * p.nfw;
         const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
         const bool last = wi == p.nwin - 1;
-        P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, (int)p.BH, d->flags,
-                  ws + p.off_a, (float*)(ws + p.off_b)};
-        P2Args a2{ws + p.off_a, (const float*)(ws + p.off_b), wi == 0 ? state_in : carry,
-                  last ? state_out : carry, ws + p.off_c, nf};
-        P3Args a3{q, out, ws + p.off_c, p.T, d->frame_len, f0, nf, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
+        void* apack = ws + p.off_a;
+        float* bt = (float*)(ws + p.off_b);
+        float* sgrp = (float*)(ws + p.off_c);
+        P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, (int)p.BH, d->flags, apack, bt};
+        P2Args a2{apack, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
+        P3Args a3{q, out, apack, bt, sgrp, p.T, d->frame_len, f0, nf, p.G, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
         if (launch_gdn_window<E, ND>(a1, a2, a3, st, wi == 0 ? d->phase_events : nullptr) != hipSuccess)
             return GDN_ERR_HIP;
     }

@@ -4,8 +4,8 @@
 //   Apack  A_f^T as K32 A-operand fragments, PAIR slot map over k_in: ND x KB fragments
 //          of 64 lanes x 8 elements (dtype of the inputs); for bf16 a hi set then a lo set.
 //   Bt     B_f as accumulator tiles: ND slices x ND tiles x 64 lanes x 4 fp32.
-//   Spack  S_f as K32 A-operand fragments, IDENT slot map over d_k: ND x KB fragments
-//          (bf16: hi set then lo set).
+//   (A_f, B_f) of a frame is the partial map of its group up to that frame's end.
+//   Sgrp   the state before each group of frames, fp32 [d_v][d_k] row-major.
 //   BCpart block-causal per-frame sums phi(K)^T [V | 1]: ND x (ND+1) accumulator tiles.
 //   BCpack block-causal S_f^T and z_f as K32 A-operand fragments: (ND+1) x KB fragments
 //          (bf16: hi set then lo set).
@@ -24,10 +24,11 @@ struct P1Args {
     int frame_len;
     int f0;             // first frame of the window
     int nf;             // frames in the window
+    int G;              // frames per group
     int BH;
     unsigned flags;     // bit 0: normalise k, bit 1: additive
-    void* Apack;
-    float* Bt;
+    void* Apack;        // partial maps A of every frame of the window
+    float* Bt;          // partial maps B
 };
 
 struct P2Args {
@@ -35,18 +36,22 @@ struct P2Args {
     const float* Bt;
     const float* state_src;  // [BH, d, d] or NULL (zero state)
     float* state_dst;        // [BH, d, d] or NULL
-    void* Spack;
+    float* Sgrp;             // [BH, groups, d, d]: state before each group
     int nf;
+    int G;
 };
 
 struct P3Args {
     const void* q;
     void* out;
-    const void* Spack;
+    const void* Apack;
+    const float* Bt;
+    const float* Sgrp;
     long long T;
     int frame_len;
     int f0;
     int nf;
+    int G;
     int out_f32;        // out is float32 (else the input dtype)
 };
 
@@ -97,7 +102,7 @@ inline hipError_t record(void* const* ev, int i, hipStream_t st) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
 }
 
-size_t gdn_unit_bytes(int nd, int esize, size_t* apack, size_t* bt, size_t* spack);
+size_t gdn_unit_bytes(int nd, int esize, size_t* apack, size_t* bt, size_t* sgrp);
 size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack);
 
 }  // namespace gdn
