@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void bc_partial(BC1Args a) {
 
     for (int c0 = 0; c0 < N; c0 += 64) {
         const int Cc = min(64, N - c0);
-        __syncthreads();
+        lds_barrier();
         constexpr int UPR = D / EPV;
         for (int u = tid; u < 64 * UPR; u += 256) {
             const int row = u / UPR, col = (u % UPR) * EPV;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void bc_partial(BC1Args a) {
                 sVt[(col + j) * P + row] = vv[j];
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
             const int q = w + 4 * qi;

@@ -159,6 +159,16 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits for every
+// outstanding global load and store of the wave, which would stall register prefetches
+// and write-backs at each barrier; kernels whose waves communicate through LDS alone use
+// this instead.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4, 8
 // inside each row of 16 lanes, then row broadcasts of lane 15 and lane 31.
 __device__ __forceinline__ float wave_incl_scan(float x) {

@@ -59,7 +59,7 @@ template <typename E, int ND> struct P1 {
     static constexpr int W_P = G::D + 4;          // W staging pitch
     static constexpr int LD_P = 20;               // diagonal L blocks / scratch pitch (floats)
     static constexpr int CB = G::D / G::EPV;      // 16-byte column blocks per row
-    static constexpr int NFR = 14;                // fragments: 6 L_IJ, 4 (T_II - I), 4 (-T_II)
+    static constexpr int NFR = 10;                // fragments: 6 L_IJ, 4 (T_II - I)
     static constexpr int FR_E = NFR * 64 * 4;     // elements per fragment set
     static constexpr int al(int b) { return (b + 255) / 256 * 256; }
     static constexpr int KT_B = al(G::D * KT_P * (int)sizeof(E));
@@ -77,8 +77,8 @@ template <typename E, int ND> struct P1 {
     static constexpr int OFF_KR = OFF_W + W_B;             // row-major K (prep wave)
     static constexpr int OFF_LD = OFF_KR + KR_B;           // diagonal blocks of L (prep wave)
     static constexpr int OFF_RAW = OFF_LD + LD_B;          // raw alpha, beta of the next chunk
-    static constexpr int OFF_TK = OFF_RAW + RAW_B;         // per-token G, n, beta (prep wave)
-    static constexpr int LDS_B = OFF_TK + al(3 * 64 * 4);
+    static constexpr int OFF_TK = OFF_RAW + RAW_B;         // per-token scalars (prep wave)
+    static constexpr int LDS_B = OFF_TK + al(7 * 64 * 4);
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
     static constexpr int APK_E = G::ND * G::KB * G::FRAG;  // A fragments (elements)
 };
@@ -87,7 +87,6 @@ template <typename E, int ND> struct P1 {
 // fragment index of L_IJ (I > J) in a fragment set
 __host__ __device__ constexpr int frL(int I, int J) { return I * (I - 1) / 2 + J; }
 __host__ __device__ constexpr int frTm(int I) { return 6 + I; }
-__host__ __device__ constexpr int frTn(int I) { return 10 + I; }
 
 template <typename E, int ND>
 __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
@@ -197,21 +196,33 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         }
     };
 
-    // ---- prep wave, first half: per-token scalars, Gram matrix, L
-    auto prep1 = [&](int p) {
+    // ---- prep wave, first part (beside the substitution): Gram matrix on the matrix
+    //      cores, key norms, gate prefix and the per-token scalars of the chunk
+    auto prep1 = [&](int p, f32x4 (&gr)[10]) {
         const int Cc = chunk_len(p);
         float* sc = SC(p);
-        E* fr = FR(p);
         const int t = lane;
         const bool valid = t < Cc;
-        float n2 = 0.f;
+        // Gram tiles computed transposed, K_J K_I^T: lane (c, g) then holds row 16I + c,
+        // columns 16J + 4g .. +3 of K K^T -- the row layout of the K16 A operand.  Each
+        // 16-token row block of K is read from LDS once, as fragments kf[X][kb].
+        {
+            F8 kf[4][KB];
 #pragma unroll
-        for (int j = 0; j < D; j += EPV) {
-            const V16 x = *(const V16*)(sKR + t * L::KR_P + j);
+            for (int X = 0; X < 4; ++X)
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) n2 += (float)x[e] * (float)x[e];
+                for (int kb = 0; kb < KB; ++kb) kf[X][kb] = O::ld8(sKR + (16 * X + c) * L::KR_P + 32 * kb + 8 * g);
+#pragma unroll
+            for (int q = 0; q < 10; ++q) {
+                const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;  // lower-triangle tile (I, J)
+                const int J = q - I * (I + 1) / 2;
+                gr[q] = zero4();
+                if (!additive || (normalize && I == J)) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) gr[q] = O::mma32(kf[J][kb], kf[I][kb], gr[q]);
+                }
+            }
         }
-        const float nrm = valid ? (normalize ? hw_rsq(fmaxf(n2, 1e-12f)) : 1.f) : 0.f;
         float gl = 0.f, be = 0.f;
         if (valid) {
             if (additive) {
@@ -222,79 +233,122 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             }
         }
         const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
-        // (the lane-read builtin is integer-typed: move the bits, not the value)
-        const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gs), 63));
+        // (the lane-read builtins are integer-typed: move the bits, not the value)
+        auto lane_of = [](float x, int l) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+        };
+        const float GC = lane_of(Gs, 63);
+        // key norm of token t from the Gram diagonal: lane (c, c/4) of diagonal tile I holds
+        // k_i.k_i for i = 16I + c, in element c % 4
+        float n2 = 0.f;
+        {
+            const int src = (t & 15) + 16 * ((t & 15) >> 2), e = c & 3;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const f32x4 x = gr[I * (I + 3) / 2];
+                const float d = e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+                const float v = __shfl(d, src);
+                if ((t >> 4) == I) n2 = v;
+            }
+        }
+        const float nrm = valid ? (normalize ? hw_rsq(fmaxf(n2, 1e-12f)) : 1.f) : 0.f;
+        sTK[64 + t] = nrm;
         sc[t] = additive ? 0.f : be * hw_exp2(Gs) * nrm;
         sc[64 + t] = be;
         sc[128 + t] = hw_exp2(GC - Gs) * nrm;
         if (t == 0) sc[192] = hw_exp2(GC);
+        // decay factors of L split at the end of 16-token block J (both factors <= 1):
+        // e^{G_i - G_j} = e^{G_i - G_end(J)} e^{G_end(J) - G_j} for i in a later block
+        const int Jt = t >> 4;
+        const float Gend = lane_of(Gs, 15) * (Jt == 0) + lane_of(Gs, 31) * (Jt == 1) +
+                           lane_of(Gs, 47) * (Jt == 2) + lane_of(Gs, 63) * (Jt == 3);
         sTK[t] = Gs;
-        sTK[64 + t] = nrm;
-        sTK[128 + t] = be;
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // other lanes read these
-        // Gram tiles computed transposed, K_J K_I^T: lane (c, g) then holds row 16I + c,
-        // columns 16J + 4g .. +3 of K K^T -- the row layout of the K16 A operand
+        sTK[128 + t] = be * nrm;
+        sTK[192 + t] = nrm * hw_exp2(Gend - Gs);
+#pragma unroll
+        for (int J = 0; J < 3; ++J)
+            sTK[256 + 64 * J + t] = J < Jt ? be * nrm * hw_exp2(Gs - lane_of(Gs, 16 * J + 15)) : 0.f;
+    };
+    // ---- prep wave, second part (beside the state update): L from the Gram tiles, its
+    //      off-diagonal blocks as operand fragments, inverses of its diagonal blocks as
+    //      (T_II - I) and -T_II fragments
+    auto prep2 = [&](int p, f32x4 (&gr)[10]) {
+        E* fr = FR(p);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // sTK written by other lanes
+        // every per-token factor first (reads only), then the scaling, then the writes
+        f32x4 cf[3], gj[4], nj[4];
+        float rf[6], si[4], gi_[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J < 3) cf[J] = *(const f32x4*)(sTK + 192 + 16 * J + 4 * g);
+            gj[J] = *(const f32x4*)(sTK + 16 * J + 4 * g);
+            nj[J] = *(const f32x4*)(sTK + 64 + 16 * J + 4 * g);
+            si[J] = sTK[128 + 16 * J + c];
+            gi_[J] = sTK[16 * J + c];
+        }
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
-            const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;  // lower-triangle tile (I, J)
+            const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
             const int J = q - I * (I + 1) / 2;
-            f32x4 acc = zero4();
-            if (!additive) {
+            if (I != J) rf[frL(I, J)] = sTK[256 + 64 * J + 16 * I + c];
+        }
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const F8 fa = O::ld8(sKR + (16 * J + c) * L::KR_P + 32 * kb + 8 * g);
-                    const F8 fb = O::ld8(sKR + (16 * I + c) * L::KR_P + 32 * kb + 8 * g);
-                    acc = O::mma32(fa, fb, acc);
-                }
-                const int i = 16 * I + c;
-                const float si = sTK[128 + i] * sTK[64 + i], gi_ = sTK[i];
-                const f32x4 gj = *(const f32x4*)(sTK + 16 * J + 4 * g);
-                const f32x4 nj = *(const f32x4*)(sTK + 64 + 16 * J + 4 * g);
+        for (int q = 0; q < 10; ++q) {
+            const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+            const int J = q - I * (I + 1) / 2;
+            const int i = 16 * I + c;
+            f32x4& acc = gr[q];
+            if (additive) {
+                acc = zero4();
+            } else if (I != J) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) acc[ii] *= rf[frL(I, J)] * cf[J][ii];
+            } else {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int j = 16 * J + 4 * g + ii;
-                    acc[ii] = (i > j) ? si * nj[ii] * hw_exp2(gi_ - gj[ii]) * acc[ii] : 0.f;
+                    acc[ii] = (i > j) ? si[I] * nj[J][ii] * hw_exp2(gi_[I] - gj[J][ii]) * acc[ii] : 0.f;
                 }
             }
+        }
+#pragma unroll
+        for (int q = 0; q < 10; ++q) {
+            const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+            const int J = q - I * (I + 1) / 2;
             if (I != J) {
-                *(F4*)(fr + (frL(I, J) * 64 + lane) * 4) = O::pack4(acc);
+                *(F4*)(fr + (frL(I, J) * 64 + lane) * 4) = O::pack4(gr[q]);
             } else {
-                *(f32x4*)(sLD + (16 * I + c) * L::LD_P + 4 * g) = acc;
+                *(f32x4*)(sLD + (16 * I + c) * L::LD_P + 4 * g) = gr[q];
             }
         }
-    };
-    // ---- prep wave, second half: inverses of the diagonal blocks -> (T - I), -T fragments
-    auto prep2 = [&](int p) {
-        E* fr = FR(p);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // sLD written by other lanes
+        // lane (bb, j): column j of T_bb = (I + L_bb)^-1 by forward substitution; the
+        // block is read into registers first, then each solved entry updates all later rows
         const int bb = lane >> 4, j = lane & 15;
         const float* lb = sLD + (16 * bb) * L::LD_P;
-        float tc[16];
+        float lr[16][16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc0 = 0.f, acc1 = 0.f;
+        for (int i = 1; i < 16; ++i)
 #pragma unroll
             for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
                 const f32x4 r = *(const f32x4*)(lb + i * L::LD_P + 4 * k4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int kk = 4 * k4 + e;
-                    if (kk < i) {
-                        if (e & 1) acc1 += r[e] * tc[kk];
-                        else acc0 += r[e] * tc[kk];
-                    }
-                }
+                for (int e = 0; e < 4; ++e) lr[i][4 * k4 + e] = r[e];
             }
-            tc[i] = (i == j) ? 1.f : (i > j ? -(acc0 + acc1) : 0.f);
-        }
-        // lane (bb, j) holds column j of T_bb; fragment row i, lane group j/4, element j%4
-        E* tm = fr + (frTm(bb) * 64) * 4;
-        E* tn = fr + (frTn(bb) * 64) * 4;
+        float acc[16], tc[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int o = (i + 16 * (j >> 2)) * 4 + (j & 3);
-            tm[o] = O::cvt(tc[i] - (i == j ? 1.f : 0.f));
-            tn[o] = O::cvt(-tc[i]);
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            tc[k] = (k == j) ? 1.f : (k > j ? -acc[k] : 0.f);
+#pragma unroll
+            for (int i = k + 1; i < 16; ++i) acc[i] += lr[i][k] * tc[k];
         }
+        // fragment row i, lane group j/4, element j%4 (-T_II = -(T_II - I) - I is formed
+        // by its users: exact in any precision, T's diagonal being 1)
+        E* tm = fr + (frTm(bb) * 64) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tm[(i + 16 * (j >> 2)) * 4 + (j & 3)] = O::cvt(i == j ? 0.f : tc[i]);
     };
 
     // ---- chain waves: state slices XA, XB (declared in the chain waves' branch below),
@@ -315,8 +369,9 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const f32x4 ws = *(const f32x4*)(sc + 16 * I + 4 * g);
             const f32x4 bs = *(const f32x4*)(sc + 64 + 16 * I + 4 * g);
             const f32x4 rw = ws * kcol, ru = bs * vcol;
-            f32x4 yw = O::mma16(*(const F4*)(fr + (frTm(I) * 64 + lane) * 4), O::pack4(rw), zero4());
-            f32x4 yu = O::mma16(*(const F4*)(fr + (frTm(I) * 64 + lane) * 4), O::pack4(ru), zero4());
+            const F4 tmf = *(const F4*)(fr + (frTm(I) * 64 + lane) * 4);
+            f32x4 yw = O::mma16(tmf, O::pack4(rw), zero4());
+            f32x4 yu = O::mma16(tmf, O::pack4(ru), zero4());
             if (I > 0) {
                 f32x4 aw = zero4(), au = zero4();
 #pragma unroll
@@ -325,7 +380,9 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                     aw = O::mma16(lf, pw[J], aw);
                     au = O::mma16(lf, pu[J], au);
                 }
-                const F4 tn = *(const F4*)(fr + (frTn(I) * 64 + lane) * 4);
+                F4 tn;  // -T_II = -(T_II - I) - I
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tn[e] = (4 * g + e == c) ? (E)(-1.f) : (E)(-tof(tmf[e]));
                 yw = O::mma16(tn, O::pack4(aw), yw);
                 yu = O::mma16(tn, O::pack4(au), yu);
             }
@@ -409,26 +466,36 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         }
     };
 
-    // frame end: the partial map of the group so far.  B as accumulator tiles; A straight
-    // from registers into its operand fragments (PAIR slot map over k_in), hi then lo.
+    // frame end: the partial map of the group so far.  B as accumulator tiles.  A goes out
+    // as the A operand of the map application (PAIR slot map over A's rows), hi then lo;
+    // that needs A's tiles transposed, which one K16 product with the identity does
+    // exactly (a bf16 or fp32 operand times 1, accumulated in fp32): it turns lane (c, g)
+    // into the owner of A[16w + 4g + i][16t + c], i.e. of 4 consecutive slots of its own
+    // fragment lane, written as one 8-byte piece.
     auto emit = [&](int fl, const f32x4 (&XA)[ND], const f32x4 (&XB)[ND]) {
         const long long unit = (long long)bh * a.nf + fw0 + fl;
         float* bt = a.Bt + unit * (ND * ND * 256) + (long long)w * ND * 256;
 #pragma unroll
         for (int t = 0; t < ND; ++t) *(f32x4*)(bt + t * 256 + lane * 4) = XB[t];
-        const int kbw = w >> 1, jb = (w & 1) * 4 + (c & 3);
+        f32x4 eye;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 1.f : 0.f;
+        const F4 eyef = O::pack4(eye);
+        const int kbw = w >> 1, half = w & 1;
 #pragma unroll
         for (int part = 0; part < NS; ++part) {
             E* ap = (E*)a.Apack + (unit * NS + part) * L::APK_E;
 #pragma unroll
             for (int t = 0; t < ND; ++t) {
+                f32x4 x = XA[t];
+                if (part) {
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    E* frg = ap + ((t * KB + kbw) * 64 + 4 * g + ii + 16 * (c >> 2)) * 8;
-                    const float x = XA[t][ii];
-                    frg[jb] = O::cvt(part ? O::lo_of(x) : x);
-                    if ((ND & 1) && w == ND - 1) frg[4 + (c & 3)] = (E)0.f;
+                    for (int i = 0; i < 4; ++i) x[i] = O::lo_of(x[i]);
                 }
+                const f32x4 xt = O::mma16(O::pack4(x), eyef, zero4());
+                E* frg = ap + ((t * KB + kbw) * 64 + lane) * 8;
+                O::st4(frg + 4 * half, xt);
+                if ((ND & 1) && w == ND - 1) O::st4(frg + 4, zero4());  // rows past d_k
             }
         }
     };
@@ -436,15 +503,16 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     // The prep wave and the chain waves run separate loops with the same barriers, so
     // that neither keeps the other's registers live.
     if (prep) {
+        f32x4 gr[10];  // Gram tiles of the chunk being prepared
         fetch(0);
         if constexpr (L::PIPE) {
             stash(0);
             if (nq > 1) fetch(1);
-            __syncthreads();
-            prep1(0);
-            __syncthreads();
-            prep2(0);
-            __syncthreads();
+            lds_barrier();
+            prep1(0, gr);
+            lds_barrier();
+            prep2(0, gr);
+            lds_barrier();
         }
         for (int q = 0; q < nq; ++q) {
             if constexpr (L::PIPE) {
@@ -453,21 +521,21 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                     stash(q + 1);
                     if (q + 2 < nq) fetch(q + 2);
                 }
-                __syncthreads();  // B1: chunk q+1 in LDS
-                if (more) prep1(q + 1);
-                __syncthreads();  // B2: W of chunk q staged by the chain waves
-                if (more) prep2(q + 1);
-                __syncthreads();  // B3: chunk q's buffers free
+                lds_barrier();  // B1: chunk q+1 in LDS
+                if (more) prep1(q + 1, gr);
+                lds_barrier();  // B2: W of chunk q staged by the chain waves
+                if (more) prep2(q + 1, gr);
+                lds_barrier();  // B3: chunk q's buffers free
             } else {
                 stash(q);
                 if (q + 1 < nq) fetch(q + 1);
-                __syncthreads();
-                prep1(q);
-                __syncthreads();
-                prep2(q);
-                __syncthreads();
-                __syncthreads();
-                __syncthreads();
+                lds_barrier();
+                prep1(q, gr);
+                lds_barrier();
+                prep2(q, gr);
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
             }
         }
     } else {
@@ -483,9 +551,9 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         if constexpr (L::PIPE) {
             stash(0);
             if (nq > 1) fetch(1);
-            __syncthreads();
-            __syncthreads();
-            __syncthreads();
+            lds_barrier();
+            lds_barrier();
+            lds_barrier();
         }
         for (int q = 0; q < nq; ++q) {
             if constexpr (L::PIPE) {
@@ -493,22 +561,22 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                     stash(q + 1);
                     if (q + 2 < nq) fetch(q + 2);
                 }
-                __syncthreads();  // B1
+                lds_barrier();  // B1
                 subst(q, Ur);
-                __syncthreads();  // B2
+                lds_barrier();  // B2
             } else {
                 stash(q);
                 if (q + 1 < nq) fetch(q + 1);
-                __syncthreads();
-                __syncthreads();
-                __syncthreads();
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
                 subst(q, Ur);
-                __syncthreads();
+                lds_barrier();
             }
             chain(q, XA, XB, Ur);
             const int fl = q / nch;
             if (q - fl * nch == nch - 1) emit(fl, XA, XB);
-            __syncthreads();  // B3
+            lds_barrier();  // B3
         }
     }
 }
@@ -645,7 +713,7 @@ __global__ __launch_bounds__(256) void gdn_frame_readout(P3Args a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     F8 sh[ND][KB], sl[ND][KB];
 #pragma unroll
     for (int n = 0; n < ND; ++n)
