@@ -582,175 +582,277 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
 }
 
 // -------------------------------------------------------------------------------------
-// Phase 2: the serial chain over groups, S_g = S_{g-1} A_g + B_g, one 16-row slice per wave
+// Phase 2: the serial chain over groups, S_g = S_{g-1} A_g + B_g
 // -------------------------------------------------------------------------------------
-// acc[t] = Bt[t] + A^T[t][:] X  for one 16-row slice, with the A fragments (hi then lo)
-// of one map unit and X split into hi + lo on the fly.
-template <typename E, int ND>
-__device__ __forceinline__ void apply_map(const E* ah, const float* bt, f32x4 (&X)[ND], int lane) {
-    using O = Ops<E>;
-    using F8 = typename O::F8;
-    constexpr int KB = (ND + 1) / 2;
-    constexpr int APK_E = ND * KB * 64 * 8;
-    F8 fh[ND][KB], fl[ND][KB];
-    f32x4 acc[ND];
-#pragma unroll
-    for (int t = 0; t < ND; ++t) {
-        acc[t] = *(const f32x4*)(bt + t * 256 + lane * 4);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int off = ((t * KB + kb) * 64 + lane) * 8;
-            fh[t][kb] = O::ld8(ah + off);
-            fl[t][kb] = O::kSplit ? O::ld8(ah + APK_E + off) : O::zero8();
-        }
-    }
-    F8 xh[KB], xl[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-        O::split8(X[2 * kb], (2 * kb + 1 < ND) ? X[(2 * kb + 1) % ND] : zero4(), xh[kb], xl[kb]);
-#pragma unroll
-    for (int t = 0; t < ND; ++t) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            acc[t] = O::mma32(fh[t][kb], xh[kb], acc[t]);
-            if (O::kSplit) {
-                acc[t] = O::mma32(fl[t][kb], xh[kb], acc[t]);
-                acc[t] = O::mma32(fh[t][kb], xl[kb], acc[t]);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < ND; ++t) X[t] = acc[t];
-}
+// One workgroup of 4 waves per (b, h, 4 row slices of S).  The group maps are read from
+// HBM once per workgroup: each step's A fragments are staged in LDS (double-buffered)
+// and the next step's are already in flight in registers while this step computes.
+template <typename E, int ND> struct P2 {
+    static constexpr int KB = (ND + 1) / 2;
+    static constexpr int NS = SplitCount<E>::N;
+    static constexpr int APK_E = ND * KB * 64 * 8;             // one part of A (elements)
+    static constexpr int TOTV = NS * APK_E * (int)sizeof(E) / 16;  // 16-byte pieces of A
+    static constexpr int NV = (TOTV + 255) / 256;              // per thread
+    static constexpr int SPW = 4;                              // slices per workgroup
+    static constexpr int LDS_B = 2 * NS * APK_E * (int)sizeof(E);
+};
 
 template <typename E, int ND>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_frame_chain(P2Args a) {
-    using Gm = Geo<E, ND>;
-    constexpr int D = Gm::D, KB = Gm::KB;
-    constexpr int APK_E = ND * KB * Gm::FRAG;
-    constexpr int NS = SplitCount<E>::N;
-    const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
-    const int s = blockIdx.x, bh = blockIdx.y;
+__global__ __launch_bounds__(256, 1) void gdn_frame_chain(P2Args a) {
+    using O = Ops<E>;
+    using F8 = typename O::F8;
+    using P = P2<E, ND>;
+    constexpr int D = 16 * ND, KB = P::KB, APK_E = P::APK_E, NS = P::NS;
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    E* const sA = (E*)smem;  // [2][NS * APK_E]
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int s = blockIdx.x * P::SPW + w;  // row slice of this wave
+    const bool active = s < ND;
+    const int bh = blockIdx.y;
     const int ngw = (a.nf + a.G - 1) / a.G;
+    auto unit_of = [&](int gi) { return (long long)bh * a.nf + min(gi * a.G + a.G, a.nf) - 1; };  // group end
+
+    u32x4 pa[P::NV];
+    auto loadA = [&](int gi) {
+        const u32x4* src = (const u32x4*)((const E*)a.Apack + unit_of(gi) * NS * APK_E);
+#pragma unroll
+        for (int k = 0; k < P::NV; ++k)
+            if (tid + 256 * k < P::TOTV) pa[k] = src[tid + 256 * k];
+    };
+    auto storeA = [&](int buf) {
+        u32x4* dst = (u32x4*)(sA + buf * NS * APK_E);
+#pragma unroll
+        for (int k = 0; k < P::NV; ++k)
+            if (tid + 256 * k < P::TOTV) dst[tid + 256 * k] = pa[k];
+    };
+    f32x4 bt[ND], btn[ND];
+    auto loadB = [&](int gi, f32x4 (&b)[ND]) {
+        if (!active) return;
+        const float* p = a.Bt + unit_of(gi) * (ND * ND * 256) + (long long)s * ND * 256;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) b[t] = *(const f32x4*)(p + t * 256 + lane * 4);
+    };
 
     // state tiles: X[t] lane (c,g) = S[16s + c][16t + 4g + i]
     f32x4 X[ND];
     const long long srow = (long long)(16 * s + c) * D;
 #pragma unroll
     for (int t = 0; t < ND; ++t)
-        X[t] = a.state_src ? *(const f32x4*)(a.state_src + (long long)bh * D * D + srow + 16 * t + 4 * g) : zero4();
-
-    for (int gi = 0; gi < ngw; ++gi) {
-        // state before the group, for the readout
-        float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + srow;
-#pragma unroll
-        for (int t = 0; t < ND; ++t) *(f32x4*)(sg + 16 * t + 4 * g) = X[t];
-        const long long unit = (long long)bh * a.nf + min(gi * a.G + a.G, a.nf) - 1;  // group end
-        const E* ah = (const E*)a.Apack + unit * NS * APK_E;
-        const float* bt = a.Bt + unit * (ND * ND * 256) + (long long)s * ND * 256;
-        apply_map<E, ND>(ah, bt, X, lane);
+        X[t] = (active && a.state_src) ? *(const f32x4*)(a.state_src + (long long)bh * D * D + srow + 16 * t + 4 * g)
+                                       : zero4();
+    loadA(0);
+    loadB(0, bt);
+    storeA(0);
+    if (ngw > 1) {
+        loadA(1);
+        loadB(1, btn);
     }
-    if (a.state_dst) {
+    lds_barrier();
+    for (int gi = 0; gi < ngw; ++gi) {
+        if (active) {
+            // state before the group, for the readout
+            float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + srow;
+#pragma unroll
+            for (int t = 0; t < ND; ++t) *(f32x4*)(sg + 16 * t + 4 * g) = X[t];
+            // X <- Bt + A^T X, A streamed from LDS tile by tile
+            const E* ah = sA + (gi & 1) * NS * APK_E;
+            F8 xh[KB], xl[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                O::split8(X[2 * kb], (2 * kb + 1 < ND) ? X[(2 * kb + 1) % ND] : zero4(), xh[kb], xl[kb]);
+#pragma unroll
+            for (int t = 0; t < ND; ++t) {
+                f32x4 acc = bt[t];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int off = ((t * KB + kb) * 64 + lane) * 8;
+                    const F8 fh = O::ld8(ah + off);
+                    acc = O::mma32(fh, xh[kb], acc);
+                    if (O::kSplit) {
+                        acc = O::mma32(O::ld8(ah + APK_E + off), xh[kb], acc);
+                        acc = O::mma32(fh, xl[kb], acc);
+                    }
+                }
+                X[t] = acc;
+            }
+        }
+        if (gi + 1 < ngw) {
+            storeA((gi + 1) & 1);
+#pragma unroll
+            for (int t = 0; t < ND; ++t) bt[t] = btn[t];
+            if (gi + 2 < ngw) {
+                loadA(gi + 2);
+                loadB(gi + 2, btn);
+            }
+        }
+        lds_barrier();
+    }
+    if (active && a.state_dst) {
 #pragma unroll
         for (int t = 0; t < ND; ++t) *(f32x4*)(a.state_dst + (long long)bh * D * D + srow + 16 * t + 4 * g) = X[t];
     }
 }
 
 // -------------------------------------------------------------------------------------
-// Phase 3: S_f = S_{g-1} A_{g,<=f} + B_{g,<=f}, then O_f = Q_f S_f^T (as O^T = S_f Q^T so
-// each lane owns 4 outputs of one token)
+// Phase 3: S_f = S_{g-1} A_{g,<=f} + B_{g,<=f}, then O_f = Q_f S_f^T, computed as
+// O^T = S_f Q^T so that each lane owns 4 outputs of one token.  One workgroup of 4 waves
+// per (b, h, frame); wave w owns the 16-row slices w and w + 4 of S_f: it composes them
+// in registers, and the composed accumulator tiles are, as they stand, the A operand
+// fragments (PAIR slot map over d_k) of its output columns -- no data movement.  Q is
+// then read with the same slot map.
 // -------------------------------------------------------------------------------------
-template <typename E, int ND> struct P3 {
-    static constexpr int KB = (ND + 1) / 2;
-    static constexpr int APK_E = ND * KB * 64 * 8;
-    static constexpr int NS = SplitCount<E>::N;
-    static constexpr int LDS_B = NS * APK_E * (int)sizeof(E);
-};
-
 template <typename E, int ND>
-__global__ __launch_bounds__(256) void gdn_frame_readout(P3Args a) {
+__global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
     using O = Ops<E>;
     using F8 = typename O::F8;
-    using Gm = Geo<E, ND>;
-    constexpr int D = Gm::D, KB = Gm::KB;
-    constexpr int APK_E = P3<E, ND>::APK_E;
-    constexpr int NS = P3<E, ND>::NS;
-    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
-    E* sS = (E*)smem;  // S_f as readout operand fragments (IDENT slot map over d_k), hi then lo
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int D = 16 * ND, KB = (ND + 1) / 2;
+    constexpr int APK_E = ND * KB * 64 * 8;
+    constexpr int NS = SplitCount<E>::N;
+    constexpr int NSL = (ND + 3) / 4;  // slices per wave (at most 2)
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
     const int fw = blockIdx.x, bh = blockIdx.y;
     const int N = a.frame_len;
     const int ngw = (a.nf + a.G - 1) / a.G;
     const int gi = fw / a.G;
     const long long unit = (long long)bh * a.nf + fw;
+    bool own[NSL];
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) own[u] = w + 4 * u < ND;
 
-    // ---- compose S_f slice by slice (wave w: slices w, w+4)
-    for (int s = w; s < ND; s += 4) {
-        f32x4 X[ND];
-        const float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + (long long)(16 * s + c) * D;
+    // ---- compose: X_u = Sgrp slice (w + 4u) A + Bt slice, A streamed tile by tile
+    f32x4 X[NSL][ND];
 #pragma unroll
-        for (int t = 0; t < ND; ++t) X[t] = *(const f32x4*)(sg + 16 * t + 4 * g);
-        const E* ah = (const E*)a.Apack + unit * NS * APK_E;
-        const float* bt = a.Bt + unit * (ND * ND * 256) + (long long)s * ND * 256;
-        apply_map<E, ND>(ah, bt, X, lane);
-        // fragment (n = s, kb = t/2), lane c + 16 (2 (t%2) + g/2), elements 4 (g%2) .. +3
+    for (int u = 0; u < NSL; ++u) {
+        const int sl = own[u] ? w + 4 * u : 0;
+        const float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + (long long)(16 * sl + c) * D;
 #pragma unroll
-        for (int part = 0; part < NS; ++part) {
-#pragma unroll
-            for (int t = 0; t < ND; ++t) {
-                f32x4 v = X[t];
-                if (part) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = O::lo_of(v[i]);
-                }
-                const int lp = c + 16 * (2 * (t & 1) + (g >> 1));
-                O::st4(sS + part * APK_E + ((s * KB + (t >> 1)) * 64 + lp) * 8 + 4 * (g & 1), v);
-            }
-            if (ND & 1) {
-                const int lp = c + 16 * (2 + (g >> 1));
-                O::st4(sS + part * APK_E + ((s * KB + KB - 1) * 64 + lp) * 8 + 4 * (g & 1), zero4());
-            }
-        }
+        for (int t = 0; t < ND; ++t) X[u][t] = *(const f32x4*)(sg + 16 * t + 4 * g);
     }
-    lds_barrier();
-    F8 sh[ND][KB], sl[ND][KB];
+    F8 xh[NSL][KB], xl[NSL][KB];
 #pragma unroll
-    for (int n = 0; n < ND; ++n)
+    for (int u = 0; u < NSL; ++u)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            sh[n][kb] = O::ld8(sS + ((n * KB + kb) * 64 + lane) * 8);
-            sl[n][kb] = O::kSplit ? O::ld8(sS + APK_E + ((n * KB + kb) * 64 + lane) * 8) : O::zero8();
-        }
-
-    const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw) * N;
-    const E* qp = (const E*)a.q + tok0 * D;
-    const int ntile = (N + 15) / 16;
-    for (int tt = w; tt < ntile; tt += 4) {
-        const int t = 16 * tt + c;
-        const bool valid = t < N;
-        F8 qb[KB];
+        for (int kb = 0; kb < KB; ++kb)
+            O::split8(X[u][2 * kb], (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4(), xh[u][kb], xl[u][kb]);
+    {
+        const E* ah = (const E*)a.Apack + unit * NS * APK_E;
+        const float* bt = a.Bt + unit * (ND * ND * 256);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int col = 32 * kb + 8 * g;
-            qb[kb] = (valid && col < D) ? O::ld8(qp + (long long)t * D + col) : O::zero8();
-        }
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-            f32x4 acc = zero4();
+        for (int t = 0; t < ND; ++t) {
+            F8 fh[KB], fl[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                acc = O::mma32(sh[n][kb], qb[kb], acc);
-                if (O::kSplit) acc = O::mma32(sl[n][kb], qb[kb], acc);
+                const int off = ((t * KB + kb) * 64 + lane) * 8;
+                fh[kb] = O::ld8(ah + off);
+                fl[kb] = O::kSplit ? O::ld8(ah + APK_E + off) : O::zero8();
             }
-            if (valid) {
-                const long long o = (tok0 + t) * D + 16 * n + 4 * g;
-                if (a.out_f32) *(f32x4*)((float*)a.out + o) = acc;
-                else O::st4((E*)a.out + o, acc);
+#pragma unroll
+            for (int u = 0; u < NSL; ++u) {
+                const int sl = own[u] ? w + 4 * u : 0;
+                f32x4 acc = *(const f32x4*)(bt + ((long long)sl * ND + t) * 256 + lane * 4);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    acc = O::mma32(fh[kb], xh[u][kb], acc);
+                    if (O::kSplit) {
+                        acc = O::mma32(fl[kb], xh[u][kb], acc);
+                        acc = O::mma32(fh[kb], xl[u][kb], acc);
+                    }
+                }
+                X[u][t] = acc;
             }
         }
     }
+    // S_f slices as readout A fragments (hi, lo): slot (g, j) of k block kb holds
+    // S[16 s + c][32 kb + 4g + j] (j < 4), S[16 s + c][32 kb + 16 + 4g + j - 4] (j >= 4)
+    F8 sh[NSL][KB], sl_[NSL][KB];
+#pragma unroll
+    for (int u = 0; u < NSL; ++u)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            O::split8(X[u][2 * kb], (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4(), sh[u][kb], sl_[u][kb]);
+
+    // ---- readout: Q goes through LDS in chunks of 64 tokens (double-buffered, the next
+    //      chunk's global loads in flight while this one is computed); every wave reads
+    //      every token tile from LDS for its own output columns
+    constexpr int QP = D + 8;                              // LDS row pitch (elements)
+    constexpr int EPV = Ops<E>::EPV;
+    constexpr int CBQ = D / EPV;                           // 16-byte pieces per token row
+    constexpr int QV = (64 * CBQ + 255) / 256;             // pieces per thread per chunk
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    E* const sQ = (E*)smem;                                // [2][64][QP]
+    using V16 = typename Ops<E>::V16;
+    const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw) * N;
+    const E* qp = (const E*)a.q + tok0 * D;
+    const int nchq = (N + 63) / 64;
+    V16 qr[QV];
+    auto qload = [&](int ch) {
+#pragma unroll
+        for (int k = 0; k < QV; ++k) {
+            const int v = tid + 256 * k, row = v / CBQ, cb = v - row * CBQ;
+            if (v < 64 * CBQ && 64 * ch + row < N) qr[k] = *(const V16*)(qp + (long long)(64 * ch + row) * D + cb * EPV);
+            else {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) qr[k][e] = (E)0.f;
+            }
+        }
+    };
+    auto qstore = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < QV; ++k) {
+            const int v = tid + 256 * k, row = v / CBQ, cb = v - row * CBQ;
+            if (v < 64 * CBQ) *(V16*)(sQ + (buf * 64 + row) * QP + cb * EPV) = qr[k];
+        }
+    };
+    qload(0);
+    qstore(0);
+    if (nchq > 1) qload(1);
+    lds_barrier();
+    for (int ch = 0; ch < nchq; ++ch) {
+        const E* qb0 = sQ + (ch & 1) * 64 * QP;
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl) {
+            const int t = 64 * ch + 16 * tl + c;
+            F8 qb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const E* r = qb0 + (16 * tl + c) * QP + 32 * kb + 4 * g;
+                if (32 * kb + 16 < D) {
+                    qb[kb] = O::ld44(r, r + 16);
+                } else {  // d_k columns 32kb + 16.. do not exist
+                    qb[kb] = O::ld44(r, r);
+#pragma unroll
+                    for (int j = 4; j < 8; ++j) qb[kb][j] = (E)0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NSL; ++u) {
+                if (!own[u]) continue;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    acc = O::mma32(sh[u][kb], qb[kb], acc);
+                    if (O::kSplit) acc = O::mma32(sl_[u][kb], qb[kb], acc);
+                }
+                if (t < N) {
+                    const long long o = (tok0 + t) * D + 16 * (w + 4 * u) + 4 * g;
+                    if (a.out_f32) *(f32x4*)((float*)a.out + o) = acc;
+                    else O::st4((E*)a.out + o, acc);
+                }
+            }
+        }
+        if (ch + 1 < nchq) {
+            qstore((ch + 1) & 1);
+            if (ch + 2 < nchq) qload(ch + 2);
+        }
+        lds_barrier();
+    }
 }
+
+template <typename E, int ND> struct P3 {
+    static constexpr int LDS_B = 2 * 64 * (16 * ND + 8) * (int)sizeof(E);
+};
 
 // -------------------------------------------------------------------------------------
 // launchers
@@ -764,6 +866,9 @@ hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p
         hipError_t e = hipFuncSetAttribute((const void*)gdn_frame_affine<E, ND>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS_B);
         if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void*)gdn_frame_chain<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                P2<E, ND>::LDS_B);
+        if (e != hipSuccess) return e;
         e = hipFuncSetAttribute((const void*)gdn_frame_readout<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 P3<E, ND>::LDS_B);
         if (e != hipSuccess) return e;
@@ -775,7 +880,9 @@ hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_frame_affine<E, ND>), dim3(ngw, BH), dim3(L::NT), L::LDS_B, st, p1);
     if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3(ND, BH), dim3(64), 0, st, p2);
+    constexpr int lds2 = P2<E, ND>::LDS_B;
+    hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3((ND + P2<E, ND>::SPW - 1) / P2<E, ND>::SPW, BH), dim3(256), lds2,
+                       st, p2);
     if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 2, st)) != hipSuccess) return e;
     constexpr int lds3 = P3<E, ND>::LDS_B;
     hipLaunchKernelGGL((gdn_frame_readout<E, ND>), dim3(p3.nf, BH), dim3(256), lds3, st, p3);
