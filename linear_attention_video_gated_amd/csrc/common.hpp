@@ -31,6 +31,7 @@ typedef short short4_ __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -50,16 +51,17 @@ template <> struct Ops<bf16> {
                                                          __builtin_bit_cast(short4_, b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ bf16 cvt(float x) { return (bf16)x; }
+    // conversions written pairwise, so that each v_cvt_pk_bf16_f32 rounds two values (RNE)
+    static __device__ __forceinline__ unsigned pk2(float a, float b) {
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    }
     static __device__ __forceinline__ F8 pack8(f32x4 lo, f32x4 hi) {
-        F8 r;
-        r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
-        r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
-        return r;
+        const u32x4 w = {pk2(lo[0], lo[1]), pk2(lo[2], lo[3]), pk2(hi[0], hi[1]), pk2(hi[2], hi[3])};
+        return __builtin_bit_cast(F8, w);
     }
     static __device__ __forceinline__ F4 pack4(f32x4 x) {
-        F4 r;
-        r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
-        return r;
+        const u32x2 w = {pk2(x[0], x[1]), pk2(x[2], x[3])};
+        return __builtin_bit_cast(F4, w);
     }
     // 8 consecutive elements from LDS / global (16-byte aligned)
     static __device__ __forceinline__ F8 ld8(const bf16* p) { return *(const F8*)p; }
@@ -72,10 +74,7 @@ template <> struct Ops<bf16> {
     static __device__ __forceinline__ void st8(bf16* p, F8 x) { *(F8*)p = x; }
     static __device__ __forceinline__ void st2(bf16* p, bf16 a, bf16 b) { *(bf16x2*)p = bf16x2{a, b}; }
     static __device__ __forceinline__ void st4(bf16* p, f32x4 x) { *(F4*)p = pack4(x); }
-    static __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
-        F4 x = *(const F4*)p;
-        return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-    }
+    static __device__ __forceinline__ f32x4 ld4f(const bf16* p) { return __builtin_convertvector(*(const F4*)p, f32x4); }
     static __device__ __forceinline__ F8 zero8() {
         F8 r;
         for (int j = 0; j < 8; ++j) r[j] = (bf16)0.f;
@@ -85,18 +84,12 @@ template <> struct Ops<bf16> {
     static constexpr bool kSplit = true;
     static __device__ __forceinline__ void split8(f32x4 a, f32x4 b, F8& hi, F8& lo) {
         hi = pack8(a, b);
-        f32x4 ra, rb;
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = a[i] - (float)hi[i];
-            rb[i] = b[i] - (float)hi[4 + i];
-        }
-        lo = pack8(ra, rb);
+        lo = pack8(a - __builtin_convertvector(__builtin_shufflevector(hi, hi, 0, 1, 2, 3), f32x4),
+                   b - __builtin_convertvector(__builtin_shufflevector(hi, hi, 4, 5, 6, 7), f32x4));
     }
     static __device__ __forceinline__ void split4(f32x4 a, F4& hi, F4& lo) {
         hi = pack4(a);
-        f32x4 r;
-        for (int i = 0; i < 4; ++i) r[i] = a[i] - (float)hi[i];
-        lo = pack4(r);
+        lo = pack4(a - __builtin_convertvector(hi, f32x4));
     }
     static __device__ __forceinline__ float lo_of(float x) { return x - (float)(bf16)x; }
 };

@@ -197,10 +197,9 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     };
 
     // ---- prep wave, first part (beside the substitution): Gram matrix on the matrix
-    //      cores, key norms, gate prefix and the per-token scalars of the chunk
+    //      cores and the key norms
     auto prep1 = [&](int p, f32x4 (&gr)[10]) {
         const int Cc = chunk_len(p);
-        float* sc = SC(p);
         const int t = lane;
         const bool valid = t < Cc;
         // Gram tiles computed transposed, K_J K_I^T: lane (c, g) then holds row 16I + c,
@@ -223,21 +222,6 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                 }
             }
         }
-        float gl = 0.f, be = 0.f;
-        if (valid) {
-            if (additive) {
-                be = 1.f;
-            } else {
-                gl = hw_log2(fmaxf(sRAW[t], FLT_MIN));
-                be = sRAW[64 + t];
-            }
-        }
-        const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
-        // (the lane-read builtins are integer-typed: move the bits, not the value)
-        auto lane_of = [](float x, int l) {
-            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-        };
-        const float GC = lane_of(Gs, 63);
         // key norm of token t from the Gram diagonal: lane (c, c/4) of diagonal tile I holds
         // k_i.k_i for i = 16I + c, in element c % 4
         float n2 = 0.f;
@@ -253,6 +237,32 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         }
         const float nrm = valid ? (normalize ? hw_rsq(fmaxf(n2, 1e-12f)) : 1.f) : 0.f;
         sTK[64 + t] = nrm;
+    };
+    // ---- prep wave, second part (beside the state update): gate prefix and per-token
+    //      scalars, L from the Gram tiles, its off-diagonal blocks as operand fragments,
+    //      its diagonal blocks to LDS
+    auto prep2 = [&](int p, f32x4 (&gr)[10]) {
+        E* fr = FR(p);
+        const int Cc = chunk_len(p);
+        float* sc = SC(p);
+        const int t = lane;
+        const bool valid = t < Cc;
+        const float nrm = sTK[64 + t];
+        float gl = 0.f, be = 0.f;
+        if (valid) {
+            if (additive) {
+                be = 1.f;
+            } else {
+                gl = hw_log2(fmaxf(sRAW[t], FLT_MIN));
+                be = sRAW[64 + t];
+            }
+        }
+        const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
+        // (the lane-read builtins are integer-typed: move the bits, not the value)
+        auto lane_of = [](float x, int l) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+        };
+        const float GC = lane_of(Gs, 63);
         sc[t] = additive ? 0.f : be * hw_exp2(Gs) * nrm;
         sc[64 + t] = be;
         sc[128 + t] = hw_exp2(GC - Gs) * nrm;
@@ -268,12 +278,6 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
 #pragma unroll
         for (int J = 0; J < 3; ++J)
             sTK[256 + 64 * J + t] = J < Jt ? be * nrm * hw_exp2(Gs - lane_of(Gs, 16 * J + 15)) : 0.f;
-    };
-    // ---- prep wave, second part (beside the state update): L from the Gram tiles, its
-    //      off-diagonal blocks as operand fragments, inverses of its diagonal blocks as
-    //      (T_II - I) and -T_II fragments
-    auto prep2 = [&](int p, f32x4 (&gr)[10]) {
-        E* fr = FR(p);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // sTK written by other lanes
         // every per-token factor first (reads only), then the scaling, then the writes
         f32x4 cf[3], gj[4], nj[4];
@@ -321,40 +325,54 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                 *(f32x4*)(sLD + (16 * I + c) * L::LD_P + 4 * g) = gr[q];
             }
         }
+    };
+    // ---- prep wave, third part (beside the next chunk's stash): inverses of the diagonal
+    //      blocks of (I + L) -> (T_II - I) fragments
+    auto prep3 = [&](int p) {
+        E* fr = FR(p);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // sLD written by other lanes
-        // lane (bb, j): column j of T_bb = (I + L_bb)^-1 by forward substitution; the
-        // block is read into registers first, then each solved entry updates all later rows
-        const int bb = lane >> 4, j = lane & 15;
+        // lane (bb, r): row r of T_bb = (I + L_bb)^-1, from T (I + L) = I read backwards:
+        // T[r][j] = [r == j] - sum_{k > j} T[r][k] L[k][j].  The block is read into registers
+        // first; each solved entry then updates all earlier columns (independent FMAs).
+        const int bb = lane >> 4, r = lane & 15;
         const float* lb = sLD + (16 * bb) * L::LD_P;
         float lr[16][16];
 #pragma unroll
         for (int i = 1; i < 16; ++i)
 #pragma unroll
             for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
-                const f32x4 r = *(const f32x4*)(lb + i * L::LD_P + 4 * k4);
+                const f32x4 x = *(const f32x4*)(lb + i * L::LD_P + 4 * k4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lr[i][4 * k4 + e] = r[e];
+                for (int e = 0; e < 4; ++e) lr[i][4 * k4 + e] = x[e];
             }
-        float acc[16], tc[16];
+        float acc[16], tr[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        for (int k = 0; k < 16; ++k) acc[k] = 0.f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            tc[k] = (k == j) ? 1.f : (k > j ? -acc[k] : 0.f);
+        for (int k = 15; k >= 0; --k) {
+            tr[k] = (k == r) ? 1.f : (k < r ? -acc[k] : 0.f);
 #pragma unroll
-            for (int i = k + 1; i < 16; ++i) acc[i] += lr[i][k] * tc[k];
+            for (int jj = 0; jj < k; ++jj) acc[jj] += tr[k] * lr[k][jj];
         }
-        // fragment row i, lane group j/4, element j%4 (-T_II = -(T_II - I) - I is formed
-        // by its users: exact in any precision, T's diagonal being 1)
+        // (T_II - I) as K16 A operand: fragment lane (r, g) holds row r, columns 4g..4g+3.
+        // -T_II = -(T_II - I) - I is formed by its users (exact, T's diagonal being 1).
         E* tm = fr + (frTm(bb) * 64) * 4;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tm[(i + 16 * (j >> 2)) * 4 + (j & 3)] = O::cvt(i == j ? 0.f : tc[i]);
+        for (int gg = 0; gg < 4; ++gg) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (4 * gg + e == r) ? 0.f : tr[4 * gg + e];
+            O::st4(tm + (r + 16 * gg) * 4, x);
+        }
     };
 
     // ---- chain waves: state slices XA, XB (declared in the chain waves' branch below),
     //      kept transposed as accumulator tiles: XA[t] lane (c,g) = A[16w + c][16t + 4g + i]
-    // block forward substitution, correction form: X_I = R_I + Y_I,
-    // Y_I = (T_II - I) R_I - T_II sum_{J<I} L_IJ X_J,  R = diag(b e^G n) K  or  diag(b) V
+    // block forward substitution, correction form: with A_I = sum_{J<I} L_IJ X_J and
+    // Z_I = R_I - A_I (both fp32),  X_I = T_II Z_I = Z_I + (T_II - I) Z_I,  where only the
+    // correction's operand Z_I is rounded to bf16.  R = diag(b e^G n) K  or  diag(b) V.
+    // W goes to LDS pre-scaled by -kts and U stays in registers scaled by kts, so that the
+    // state update's innovation is U~ + W~ X^T straight off the matrix cores.
     auto subst = [&](int q, f32x4 (&Ur)[4]) {
         const float* sc = SC(q);
         const E* fr = FR(q);
@@ -368,10 +386,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const f32x4 vcol = O::ld4f(vt + 16 * I + 4 * g);
             const f32x4 ws = *(const f32x4*)(sc + 16 * I + 4 * g);
             const f32x4 bs = *(const f32x4*)(sc + 64 + 16 * I + 4 * g);
-            const f32x4 rw = ws * kcol, ru = bs * vcol;
-            const F4 tmf = *(const F4*)(fr + (frTm(I) * 64 + lane) * 4);
-            f32x4 yw = O::mma16(tmf, O::pack4(rw), zero4());
-            f32x4 yu = O::mma16(tmf, O::pack4(ru), zero4());
+            f32x4 zw = ws * kcol, zu = bs * vcol;
             if (I > 0) {
                 f32x4 aw = zero4(), au = zero4();
 #pragma unroll
@@ -380,14 +395,12 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                     aw = O::mma16(lf, pw[J], aw);
                     au = O::mma16(lf, pu[J], au);
                 }
-                F4 tn;  // -T_II = -(T_II - I) - I
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tn[e] = (4 * g + e == c) ? (E)(-1.f) : (E)(-tof(tmf[e]));
-                yw = O::mma16(tn, O::pack4(aw), yw);
-                yu = O::mma16(tn, O::pack4(au), yu);
+                zw -= aw;
+                zu -= au;
             }
-            XW[I] = rw + yw;
-            Ur[I] = ru + yu;
+            const F4 tmf = *(const F4*)(fr + (frTm(I) * 64 + lane) * 4);
+            XW[I] = O::mma16(tmf, O::pack4(zw), zw);
+            Ur[I] = O::mma16(tmf, O::pack4(zu), zu);
             pw[I] = O::pack4(XW[I]);
             pu[I] = O::pack4(Ur[I]);
         }
@@ -396,13 +409,13 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const f32x4 s = *(const f32x4*)(sc + 128 + 16 * I + 4 * g);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                sW[(16 * I + 4 * g + ii) * L::W_P + 16 * w + c] = O::cvt(XW[I][ii]);
+                sW[(16 * I + 4 * g + ii) * L::W_P + 16 * w + c] = O::cvt(-s[ii] * XW[I][ii]);
                 Ur[I][ii] *= s[ii];
             }
         }
     };
 
-    // apply the chunk to both slices:  X <- g_C X + K^T diag(kts) (Z - W X^T)
+    // apply the chunk to both slices:  X <- g_C X + K^T D',  D' = U~ + W~ X^T (chunk-start X)
     auto chain = [&](int q, f32x4 (&XA)[ND], f32x4 (&XB)[ND], const f32x4 (&Ur)[4]) {
         const float* sc = SC(q);
         const E* kt = KT(q);
@@ -415,8 +428,8 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             xa[kb] = O::pack8(XA[2 * kb], hiA);
             xb[kb] = O::pack8(XB[2 * kb], hiB);
         }
-        // token halves h = 0, 1: P = W X^T for the half's two token tiles, innovation
-        // D' = diag(kts) (Z - P), then X += K^T D' (xa / xb keep the chunk-start state)
+        // token halves h = 0, 1: innovation D' for the half's two token tiles, then
+        // X += K^T D' (xa / xb keep the chunk-start state)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x4 PA[2], PB[2];
@@ -424,7 +437,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             for (int u = 0; u < 2; ++u) {
                 const int tt = 2 * h + u;
                 PA[u] = zero4();
-                PB[u] = zero4();
+                PB[u] = Ur[tt];
                 const E* wr = sW + (16 * tt + c) * L::W_P + 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
@@ -438,12 +451,6 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                     }
                     PA[u] = O::mma32(wf, xa[kb], PA[u]);
                     PB[u] = O::mma32(wf, xb[kb], PB[u]);
-                }
-                const f32x4 s = *(const f32x4*)(sc + 128 + 16 * tt + 4 * g);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    PA[u][ii] = -PA[u][ii] * s[ii];
-                    PB[u][ii] = Ur[tt][ii] - PB[u][ii] * s[ii];
                 }
             }
             // the B part carries the state and gets a hi + lo innovation; the A part,
@@ -512,6 +519,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             prep1(0, gr);
             lds_barrier();
             prep2(0, gr);
+            prep3(0);
             lds_barrier();
         }
         for (int q = 0; q < nq; ++q) {
@@ -521,6 +529,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                     stash(q + 1);
                     if (q + 2 < nq) fetch(q + 2);
                 }
+                if (q > 0) prep3(q);
                 lds_barrier();  // B1: chunk q+1 in LDS
                 if (more) prep1(q + 1, gr);
                 lds_barrier();  // B2: W of chunk q staged by the chain waves
@@ -533,6 +542,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                 prep1(q, gr);
                 lds_barrier();
                 prep2(q, gr);
+                prep3(q);
                 lds_barrier();
                 lds_barrier();
                 lds_barrier();
