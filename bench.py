@@ -217,9 +217,16 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # per-kernel times from the events the library records around its launches
+    # per-kernel times from the events the library records around its launches (six per
+    # window: before/after each of the window's three launches, on that launch's stream)
     nk = 3
-    ev = [hip.create(4) for _ in range(args.steps)]
+    import torch as _t
+    dt = _t.bfloat16 if wl.dtype == "bf16" else _t.float32
+    entry = gdn.ENTRY_BLOCK_CAUSAL if wl.kind == "block_causal" else (
+        gdn.ENTRY_READONLY if wl.kind == "stream" else gdn.ENTRY_FORWARD)
+    nwin = gdn.window_count(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
+                            flags=gdn.RELU_QK if wl.kind == "block_causal" else gdn.NORMALIZE_K, entry=entry)
+    ev = [hip.create(6 * nwin) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
@@ -232,10 +239,11 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
     names = BC_KERNELS if wl.kind == "block_causal" else GDN_KERNELS
-    kms = [0.0] * nk
+    kms = [0.0] * nk  # per call, summed over the call's windows
     for e in ev:
-        for j in range(nk):
-            kms[j] += hip.elapsed_ms(e[j], e[j + 1])
+        for wi in range(nwin):
+            for j in range(nk):
+                kms[j] += hip.elapsed_ms(e[6 * wi + 2 * j], e[6 * wi + 2 * j + 1])
         hip.destroy(e)
     kms = [x / args.steps for x in kms]
     if wl.kind == "stream":  # events bracket the last read-only call of each step
@@ -249,15 +257,18 @@ def main():
     per = kernel_bytes_per_token_head(wl.kind, wl.d, es)
     j = max(range(nk), key=lambda i: kms[i])
     kname = names[j]
-    kbytes = per[kname] * th
-    achieved = kbytes / (kms[j] * 1e-3) / 1e9
+    # one launch per window: algorithmic bytes and duration per launch (window sizes are
+    # equal but for the last, so this is the call's total bytes over its total duration)
+    kbytes = per[kname] * th / nwin
+    kms_launch = kms[j] / nwin
+    achieved = kbytes / (kms_launch * 1e-3) / 1e9
     counters = read_counters(args.workload)
     traffic = counters["bytes"] if counters and counters["kernel"] == kname else None
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel_ms": round(kms[j], 4),
-                "algorithmic_bytes": kbytes,
-                "all_kernels_ms": {n: round(x, 4) for n, x in zip(names, kms)}}
+                "traffic": traffic, "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin,
+                "algorithmic_bytes": round(kbytes),
+                "all_kernels_ms_per_call": {n: round(x, 4) for n, x in zip(names, kms)}}
     path_bytes = sum(per.values()) * th * calls
     path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
     path = {"algorithmic_bytes_per_call": sum(per.values()) * th, "achieved": round(path_gbps, 1),

@@ -45,8 +45,8 @@
  *    processed in windows of at most 8192 (b, h, frame) units (the environment
  *    variable GDN_WINDOW_UNITS, read at each call, overrides that bound).  Contents
  *    need no initialisation and are garbage afterwards.
- *  - stream: a hipStream_t (NULL = the default stream).  Work is enqueued
- *    asynchronously; the library never allocates, frees or synchronises.
+ *  - stream: a hipStream_t (NULL = the default stream).  Every launch is enqueued on
+ *    it, asynchronously; the library never allocates, frees or synchronises.
  *  - Errors: every check runs on the host before anything is enqueued and returns a
  *    negative gdn_status_t; nothing is launched then.  A failed launch returns
  *    GDN_ERR_HIP.  Device faults surface at the caller's next synchronisation.
@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -98,10 +98,12 @@ typedef struct gdn_dims {
     uint32_t flags;               /* GDN_F_* bits                                        */
     void* workspace;              /* device scratch, >= gdn_workspace_bytes() bytes      */
     size_t workspace_bytes;
-    void* const* phase_events;    /* optional, may be NULL: 4 caller-created hipEvent_t
-                                     recorded on `stream` before the first launch and after
-                                     each of the three launches of the first window, for
-                                     per-kernel timing; nothing else touches them         */
+    void* const* phase_events;    /* optional, may be NULL: 6 * phase_windows caller-created
+                                     hipEvent_t.  For window w < phase_windows, events 6w+2i
+                                     and 6w+2i+1 are recorded just before and just after the
+                                     window's i-th launch (i = 0, 1, 2), on the stream that
+                                     launch goes to; for per-kernel timing only           */
+    int32_t phase_windows;        /* windows covered by phase_events (see gdn_window_count) */
 } gdn_dims_t;
 
 /*
@@ -145,6 +147,10 @@ int linear_attn_block_causal(const void* q, const void* k, const void* v,
 /* Bytes of workspace the entry (GDN_ENTRY_*) needs for these dims; 0 on invalid dims.
  * Bounded independently of n_frames. */
 size_t gdn_workspace_bytes(const gdn_dims_t* dims, int entry);
+
+/* Number of windows (each: three launches) a call with these dims makes, >= 0, or a
+ * negative gdn_status_t for invalid dims. */
+int gdn_window_count(const gdn_dims_t* dims, int entry);
 
 /* Static, human-readable text for a gdn_status_t value. */
 const char* gdn_status_str(int status);

@@ -212,12 +212,16 @@ hipError_t launch_bc_window(const BC1Args& a1, const BC2Args& a2, const BC3Args&
     hipError_t e = record(ev, 0, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bc_partial<E, ND>), dim3(a1.nf, BH), dim3(256), 0, st, a1);
-    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess ||
+        (e = record(ev, 2, st)) != hipSuccess)
+        return e;
     hipLaunchKernelGGL((bc_scan<E, ND>), dim3(ND * (ND + 1), BH), dim3(64), 0, st, a2);
-    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 2, st)) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 3, st)) != hipSuccess ||
+        (e = record(ev, 4, st)) != hipSuccess)
+        return e;
     hipLaunchKernelGGL((bc_readout<E, ND>), dim3(a3.nf, BH), dim3(256), 0, st, a3);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return record(ev, 3, st);
+    return record(ev, 5, st);
 }
 
 #define BC_INST(E, ND)                                                                                     \

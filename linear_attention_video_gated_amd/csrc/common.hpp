@@ -92,6 +92,15 @@ template <> struct Ops<bf16> {
         lo = pack4(a - __builtin_convertvector(hi, f32x4));
     }
     static __device__ __forceinline__ float lo_of(float x) { return x - (float)(bf16)x; }
+    // LDS transpose load (ds_read_b64_tr_b16): from a row-major 16-bit matrix M in LDS
+    // (row pitch pb bytes), lane (c, g) receives M[r0 + 4g + i][c0 + c], i = 0..3 -- a K16
+    // operand fragment whose k runs along M's rows.  In each 16-lane group, source lane s
+    // points at row r0 + 4g + s/4, columns c0 + 4(s%4) .. +3 (layout checked on gfx950).
+    static __device__ __forceinline__ F4 ldtr(const bf16* m, int pb, int r0, int c0, int lane) {
+        const int s = lane & 15, g = lane >> 4;
+        const bf16* p = (const bf16*)((const char*)m + (r0 + 4 * g + (s >> 2)) * pb) + c0 + 4 * (s & 3);
+        return __builtin_bit_cast(F4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_*)(p)));
+    }
 };
 
 // fp32 inputs: fp32 matrix cores (v_mfma_f32_16x16x4_f32), fp32 throughout.
@@ -143,6 +152,13 @@ template <> struct Ops<float> {
         lo = zero4();
     }
     static __device__ __forceinline__ float lo_of(float) { return 0.f; }
+    // lane (c, g) receives M[r0 + 4g + i][c0 + c], i = 0..3 (plain loads for 32-bit data)
+    static __device__ __forceinline__ F4 ldtr(const float* m, int pb, int r0, int c0, int lane) {
+        const int c = lane & 15, g = lane >> 4;
+        const float* p = (const float*)((const char*)m + (r0 + 4 * g) * pb) + c0 + c;
+        return F4{p[0], *(const float*)((const char*)p + pb), *(const float*)((const char*)p + 2 * pb),
+                  *(const float*)((const char*)p + 3 * pb)};
+    }
 };
 
 template <typename E> __device__ __forceinline__ float tof(E x) { return (float)x; }
@@ -152,6 +168,20 @@ template <typename E> __device__ __forceinline__ float tof(E x) { return (float)
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// Asynchronous global -> LDS copies (global_load_lds): lane l's `bytes` (4 or 16) from its
+// own global address land at lds_base + l * bytes; lanes with exec off write nothing.
+// Completion is counted by vmcnt, like a load.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)gsrc,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)gsrc,
+                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+// s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding: expcnt 7, lgkmcnt 15)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits for every
 // outstanding global load and store of the wave, which would stall register prefetches

@@ -2,6 +2,11 @@
 // anything is enqueued), workspace sizing and layout, and dispatch over (dtype, d) to the
 // kernel launchers.  Frames are processed in windows of at most kMaxUnits (b, h, frame)
 // units so the workspace never grows with the number of frames.
+//
+// All launches go to the caller's stream, window after window.  (Running the chain and
+// the readout of one window on other streams beside the next window's frame maps was
+// measured slower on MI355X: the frame-map kernel saturates instruction issue and its
+// LDS footprint keeps the chain's workgroups off the busy CUs.)
 #include "gdn.h"
 #include "common.hpp"
 #include "gdn_kernels.hpp"
@@ -28,13 +33,14 @@ long long window_units() {
 
 // Frames per group of the gated-delta-rule path: the serial chain steps once per group,
 // and groups of frames form the parallel work of the frame-map kernel, so groups grow
-// only while there are still >= ~4 workgroups per CU (GDN_GROUP_FRAMES overrides).
-int group_frames(long long BH, int nfw) {
+// only while there are still >= ~4 workgroups per CU over the whole call
+// (GDN_GROUP_FRAMES overrides).  Windows hold whole groups.
+int group_frames(long long BH, int n_frames) {
     long long G = env_ll("GDN_GROUP_FRAMES");
-    if (G <= 0) G = (BH * nfw) / 1024;
+    if (G <= 0) G = (BH * n_frames) / 1024;
     if (G < 1) G = 1;
     if (G > 8) G = 8;
-    if (G > nfw) G = nfw;
+    if (G > n_frames) G = n_frames;
     return (int)G;
 }
 constexpr size_t kAlign = 256;
@@ -78,24 +84,25 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
     // element count of q must fit comfortably in 63 bits
     if (p->T > ((long long)1 << 40) / (p->BH ? p->BH : 1) / d->d_k) return GDN_ERR_DIMS;
     if (p->BH == 0 || d->n_frames == 0) return GDN_OK;
-    long long nfw = window_units() / p->BH;
-    if (nfw < 1) nfw = 1;
+    const bool bc = entry == GDN_ENTRY_BLOCK_CAUSAL;
+    if (!bc) p->G = group_frames(p->BH, d->n_frames);
+    const long long G = p->G;
+    long long nfw = window_units() / p->BH / G * G;  // whole groups per window
+    if (nfw < G) nfw = G;
     if (nfw > d->n_frames) nfw = d->n_frames;
     p->nfw = (int)nfw;
     p->nwin = (int)((d->n_frames + nfw - 1) / nfw);
     const size_t units = (size_t)p->BH * (size_t)nfw;
     size_t a = 0, b = 0, c = 0, carry = 0;
-    if (entry == GDN_ENTRY_BLOCK_CAUSAL) {
+    if (bc) {
         bc_unit_bytes(p->nd, p->es, &a, &c);
         carry = (size_t)p->BH * p->nd * (p->nd + 1) * 256 * 4;
     } else {
         gdn_unit_bytes(p->nd, p->es, &a, &b, &c);
         carry = (size_t)p->BH * d->d_k * d->d_v * 4;
-        p->G = group_frames(p->BH, p->nfw);
     }
     // per-group (not per-frame) third region for the gated delta rule
-    const size_t units_c = entry == GDN_ENTRY_BLOCK_CAUSAL ? units
-                                                           : (size_t)p->BH * ((p->nfw + p->G - 1) / p->G);
+    const size_t units_c = bc ? units : (size_t)p->BH * ((p->nfw + p->G - 1) / p->G);
     p->off_a = 0;
     p->off_b = align_up(units * a);
     p->off_c = p->off_b + align_up(units * b);
@@ -131,17 +138,21 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
             const Plan& p, hipStream_t st) {
     char* ws = (char*)d->workspace;
     float* carry = (float*)(ws + p.off_carry);
+    const int BH = (int)p.BH;
+    void* apack = ws + p.off_a;
+    float* bt = (float*)(ws + p.off_b);
+    float* sgrp = (float*)(ws + p.off_c);
     for (int wi = 0; wi < p.nwin; ++wi) {
         const int f0 = wi * p.nfw;
         const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
         const bool last = wi == p.nwin - 1;
-        void* apack = ws + p.off_a;
-        float* bt = (float*)(ws + p.off_b);
-        float* sgrp = (float*)(ws + p.off_c);
-        P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, (int)p.BH, d->flags, apack, bt};
-        P2Args a2{apack, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
-        P3Args a3{q, out, apack, bt, sgrp, p.T, d->frame_len, f0, nf, p.G, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
-        if (launch_gdn_window<E, ND>(a1, a2, a3, st, wi == 0 ? d->phase_events : nullptr) != hipSuccess)
+        const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, apack, bt};
+        const P2Args a2{apack, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
+        const P3Args a3{q, out, apack, bt, sgrp, p.T, d->frame_len, f0, nf, p.G, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
+        void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
+        if (launch_gdn_phase<E, ND>(0, &a1, BH, st, ev) != hipSuccess ||
+            launch_gdn_phase<E, ND>(1, &a2, BH, st, ev) != hipSuccess ||
+            launch_gdn_phase<E, ND>(2, &a3, BH, st, ev) != hipSuccess)
             return GDN_ERR_HIP;
     }
     return GDN_OK;
@@ -162,7 +173,8 @@ int run_bc(const void* q, const void* k, const void* v, const float* s_in, const
                    wi == 0 ? nullptr : carry, last ? nullptr : carry, last ? s_out : nullptr,
                    last ? z_out : nullptr, ws + p.off_c, nf};
         BC3Args a3{q, out, ws + p.off_c, p.T, d->frame_len, f0, nf, relu, 1e-6f, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
-        if (launch_bc_window<E, ND>(a1, a2, a3, (int)p.BH, st, wi == 0 ? d->phase_events : nullptr) != hipSuccess)
+        void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
+        if (launch_bc_window<E, ND>(a1, a2, a3, (int)p.BH, st, ev) != hipSuccess)
             return GDN_ERR_HIP;
     }
     return GDN_OK;
@@ -287,6 +299,14 @@ GDN_API size_t gdn_workspace_bytes(const gdn_dims_t* dims, int entry) {
     Plan p;
     if (check_dims(dims, entry, &p) != GDN_OK) return 0;
     return p.total;
+}
+
+GDN_API int gdn_window_count(const gdn_dims_t* dims, int entry) {
+    if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_BLOCK_CAUSAL)
+        return GDN_ERR_UNSUPPORTED;
+    Plan p;
+    const int rc = check_dims(dims, entry, &p);
+    return rc != GDN_OK ? rc : p.nwin;
 }
 
 GDN_API const char* gdn_status_str(int status) {

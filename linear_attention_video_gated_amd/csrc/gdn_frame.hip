@@ -50,36 +50,38 @@ namespace gdn {
 template <typename E, int ND> struct P1 {
     using G = Geo<E, ND>;
     static constexpr bool PIPE = sizeof(E) == 2;
-    static constexpr int NB = PIPE ? 2 : 1;       // buffers of the per-chunk inputs
-    static constexpr int NCW = ND;                // chain waves
-    static constexpr int NW = ND + 1;             // + prep wave
+    static constexpr int NB = PIPE ? 2 : 1;       // buffers of the prepared per-chunk inputs
+    static constexpr int NBD = PIPE ? 3 : 1;      // buffers of the raw chunk (K, V, gates)
+    static constexpr int NW = ND + 1;             // chain waves + prep wave
     static constexpr int NT = 64 * NW;
-    static constexpr int KR_P = G::DP + G::EPV;   // row-major K pitch (elements)
-    static constexpr int KT_P = 64 + 4;           // transposed K / V pitch (tokens)
-    static constexpr int W_P = G::D + 4;          // W staging pitch
-    static constexpr int LD_P = 20;               // diagonal L blocks / scratch pitch (floats)
-    static constexpr int CB = G::D / G::EPV;      // 16-byte column blocks per row
+    static constexpr int RB = G::D * (int)sizeof(E);  // bytes of one K or V row
+    // LDS row pitch: a multiple of 32 bytes with an odd count of 32-byte units, so that the
+    // transposed reads (8 consecutive rows x 32 bytes per half-wave) hit distinct banks
+    static constexpr int KPB = ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
+    static constexpr int KG = KPB / 16;           // 16-byte granules per LDS row
+    static constexpr int DG = RB / 16;            // granules that hold data
+    static constexpr int W_P = G::D + 4;          // W staging pitch (elements)
+    static constexpr int LD_P = 20;               // diagonal L blocks pitch (floats)
     static constexpr int NFR = 10;                // fragments: 6 L_IJ, 4 (T_II - I)
     static constexpr int FR_E = NFR * 64 * 4;     // elements per fragment set
     static constexpr int al(int b) { return (b + 255) / 256 * 256; }
-    static constexpr int KT_B = al(G::D * KT_P * (int)sizeof(E));
+    static constexpr int KV_B = al(64 * KPB);
+    static constexpr int RAW_B = al(2 * 64 * 4);
     static constexpr int SC_B = al((3 * 64 + 16) * 4);
     static constexpr int FR_B = al(FR_E * (int)sizeof(E));
     static constexpr int W_B = al(64 * W_P * (int)sizeof(E));
-    static constexpr int KR_B = al(64 * KR_P * (int)sizeof(E));
     static constexpr int LD_B = al(4 * 16 * LD_P * 4);
-    static constexpr int RAW_B = al(2 * 64 * 4);
-    static constexpr int OFF_KT = 0;                       // [NB] transposed K
-    static constexpr int OFF_VT = OFF_KT + NB * KT_B;      // [NB] transposed V
-    static constexpr int OFF_SC = OFF_VT + NB * KT_B;      // [NB] per-token scales + gamma
+    static constexpr int OFF_K = 0;                        // [NBD] row-major K chunk
+    static constexpr int OFF_V = OFF_K + NBD * KV_B;       // [NBD] row-major V chunk
+    static constexpr int OFF_RAW = OFF_V + NBD * KV_B;     // [NBD] alpha[64], beta[64]
+    static constexpr int OFF_SC = OFF_RAW + NBD * RAW_B;   // [NB] per-token scales + gamma
     static constexpr int OFF_FR = OFF_SC + NB * SC_B;      // [NB] substitution fragments
     static constexpr int OFF_W = OFF_FR + NB * FR_B;       // W staging (chain waves)
-    static constexpr int OFF_KR = OFF_W + W_B;             // row-major K (prep wave)
-    static constexpr int OFF_LD = OFF_KR + KR_B;           // diagonal blocks of L (prep wave)
-    static constexpr int OFF_RAW = OFF_LD + LD_B;          // raw alpha, beta of the next chunk
-    static constexpr int OFF_TK = OFF_RAW + RAW_B;         // per-token scalars (prep wave)
+    static constexpr int OFF_LD = OFF_W + W_B;             // diagonal blocks of L (prep wave)
+    static constexpr int OFF_TK = OFF_LD + LD_B;           // per-token scalars (prep wave)
     static constexpr int LDS_B = OFF_TK + al(7 * 64 * 4);
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
+    static_assert(RB % 16 == 0, "rows are whole 16-byte granules");
     static constexpr int APK_E = G::ND * G::KB * G::FRAG;  // A fragments (elements)
 };
 
@@ -95,21 +97,18 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     using F8 = typename O::F8;
     using F4 = typename O::F4;
     using V16 = typename O::V16;
-    constexpr int D = L::G::D, KB = L::G::KB, DP = L::G::DP, EPV = L::G::EPV, CB = L::CB;
+    constexpr int D = L::G::D, KB = L::G::KB;
     constexpr int NS = SplitCount<E>::N;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
-    E* const sKT0 = (E*)(smem + L::OFF_KT);
-    E* const sVT0 = (E*)(smem + L::OFF_VT);
     float* const sSC0 = (float*)(smem + L::OFF_SC);
     E* const sFR0 = (E*)(smem + L::OFF_FR);
     E* const sW = (E*)(smem + L::OFF_W);
-    E* const sKR = (E*)(smem + L::OFF_KR);
     float* const sLD = (float*)(smem + L::OFF_LD);
-    float* const sRAW = (float*)(smem + L::OFF_RAW);
     float* const sTK = (float*)(smem + L::OFF_TK);
     constexpr int BM = L::NB - 1;
-    auto KT = [&](int p) { return (E*)((unsigned char*)sKT0 + (p & BM) * L::KT_B); };
-    auto VT = [&](int p) { return (E*)((unsigned char*)sVT0 + (p & BM) * L::KT_B); };
+    auto KB_ = [&](int p) { return (E*)(smem + L::OFF_K + (p % L::NBD) * L::KV_B); };
+    auto VB_ = [&](int p) { return (E*)(smem + L::OFF_V + (p % L::NBD) * L::KV_B); };
+    auto RAW = [&](int p) { return (float*)(smem + L::OFF_RAW + (p % L::NBD) * L::RAW_B); };
     auto SC = [&](int p) { return (float*)((unsigned char*)sSC0 + (p & BM) * L::SC_B); };
     auto FR = [&](int p) { return (E*)((unsigned char*)sFR0 + (p & BM) * L::FR_B); };
     // SC layout: [0,64) ws = b e^G n, [64,128) b, [128,192) kts = e^{G_C - G} n, [192] gamma_C
@@ -131,68 +130,33 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     auto chunk_t0 = [&](int q) { const int f = q / nch; return (long long)f * N + (q - f * nch) * 64; };
     auto chunk_len = [&](int q) { const int f = q / nch; return min(64, N - (q - f * nch) * 64); };
 
-    // ---- chunk loads: thread (p = tid % 32, column block cb) owns token rows 2p, 2p+1 of
-    //      one 16-byte column block; the chunk after next is fetched into registers while
-    //      the current one is computed
-    constexpr int NCB = L::NT / 32;
-    constexpr int NPASS = (CB + NCB - 1) / NCB;
-    const int pr = tid & 31, cb0 = tid >> 5;
-    V16 rk[NPASS][2], rv[NPASS][2];
-    float ra = 0.f, rb = 0.f;
-    auto fetch = [&](int q) {
-        const long long t0 = chunk_t0(q);
-        const int Cc = chunk_len(q);
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-            const int cb = cb0 + ps * NCB;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int row = 2 * pr + h;
-                if (cb < CB && row < Cc) {
-                    rk[ps][h] = *(const V16*)(kp + (t0 + row) * D + cb * EPV);
-                    rv[ps][h] = *(const V16*)(vp + (t0 + row) * D + cb * EPV);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < EPV; ++j) rk[ps][h][j] = rv[ps][h][j] = (E)0.f;
-                }
+    // ---- chunk loads: global -> LDS copies with no register staging.  K and V land
+    //      row-major (pitch KPB); each copy instruction moves 64 granules of 16 bytes and
+    //      instructions are dealt round-robin to all waves.  Rows past the chunk's end and
+    //      padding granules copy a valid in-bounds granule instead (their values are
+    //      finite and multiplied by zero scale factors, never used as data).
+    auto dma_chunk = [&](int p) {
+        const long long t0 = chunk_t0(p);
+        const int Cc = chunk_len(p);
+        for (int i = w; i < 2 * L::KG; i += L::NW) {
+            const bool isk = i < L::KG;
+            const int ii = isk ? i : i - L::KG;
+            const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
+            const long long el = (t0 + min(row, Cc - 1)) * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
+            const int dst = (isk ? L::OFF_K : L::OFF_V) + (p % L::NBD) * L::KV_B + ii * 1024;
+            if constexpr (L::PIPE) dma16((isk ? kp : vp) + el, smem + dst);
+            else *(u32x4*)(smem + dst + 16 * lane) = *(const u32x4*)((isk ? kp : vp) + el);  // same copy, synchronous
+        }
+        if (!additive && w == (2 * L::KG) % L::NW) {
+            const long long tt = tok0 + t0 + min(lane, Cc - 1);
+            const int dst = L::OFF_RAW + (p % L::NBD) * L::RAW_B;
+            if constexpr (L::PIPE) {
+                dma4(a.alpha + tt, smem + dst);
+                dma4(a.beta + tt, smem + dst + 256);
+            } else {
+                ((float*)(smem + dst))[lane] = a.alpha[tt];
+                ((float*)(smem + dst + 256))[lane] = a.beta[tt];
             }
-        }
-        if (tid < 64) {
-            ra = rb = 0.f;
-            if (tid < Cc && !additive) {
-                ra = a.alpha[tok0 + t0 + tid];
-                rb = a.beta[tok0 + t0 + tid];
-            }
-        }
-    };
-    // registers -> LDS for chunk p: row-major K (prep wave), transposed K and V (chain waves)
-    auto stash = [&](int p) {
-        E* kt = KT(p);
-        E* vt = VT(p);
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-            const int cb = cb0 + ps * NCB;
-            if (cb < CB) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) *(V16*)(sKR + (2 * pr + h) * L::KR_P + cb * EPV) = rk[ps][h];
-#pragma unroll
-                for (int j = 0; j < EPV; ++j) {
-                    O::st2(kt + (cb * EPV + j) * L::KT_P + 2 * pr, rk[ps][0][j], rk[ps][1][j]);
-                    O::st2(vt + (cb * EPV + j) * L::KT_P + 2 * pr, rv[ps][0][j], rv[ps][1][j]);
-                }
-            }
-        }
-        if constexpr (DP > D) {  // zero the padded K columns D..DP-1
-            constexpr int PADV = (DP - D) / EPV;
-            V16 z;
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) z[j] = (E)0.f;
-            for (int u = tid; u < 64 * PADV; u += L::NT)
-                *(V16*)(sKR + (u / PADV) * L::KR_P + D + (u % PADV) * EPV) = z;
-        }
-        if (tid < 64) {
-            sRAW[tid] = ra;
-            sRAW[64 + tid] = rb;
         }
     };
 
@@ -210,7 +174,10 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
 #pragma unroll
             for (int X = 0; X < 4; ++X)
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) kf[X][kb] = O::ld8(sKR + (16 * X + c) * L::KR_P + 32 * kb + 8 * g);
+                for (int kb = 0; kb < KB; ++kb)  // d_k columns past D are zero
+                    kf[X][kb] = (32 * kb + 8 * g < D)
+                                    ? O::ld8((const E*)((const char*)KB_(p) + (16 * X + c) * L::KPB) + 32 * kb + 8 * g)
+                                    : O::zero8();
 #pragma unroll
             for (int q = 0; q < 10; ++q) {
                 const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;  // lower-triangle tile (I, J)
@@ -253,8 +220,8 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             if (additive) {
                 be = 1.f;
             } else {
-                gl = hw_log2(fmaxf(sRAW[t], FLT_MIN));
-                be = sRAW[64 + t];
+                gl = hw_log2(fmaxf(RAW(p)[t], FLT_MIN));
+                be = RAW(p)[64 + t];
             }
         }
         const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
@@ -376,14 +343,15 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     auto subst = [&](int q, f32x4 (&Ur)[4]) {
         const float* sc = SC(q);
         const E* fr = FR(q);
-        const E* kt = KT(q) + (16 * w + c) * L::KT_P;
-        const E* vt = VT(q) + (16 * w + c) * L::KT_P;
+        const E* kb = KB_(q);
+        const E* vb = VB_(q);
         f32x4 XW[4];
         F4 pw[4], pu[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const f32x4 kcol = O::ld4f(kt + 16 * I + 4 * g);
-            const f32x4 vcol = O::ld4f(vt + 16 * I + 4 * g);
+            // lane (c, g): tokens 16I + 4g + i, column 16w + c
+            const f32x4 kcol = __builtin_convertvector(O::ldtr(kb, L::KPB, 16 * I, 16 * w, lane), f32x4);
+            const f32x4 vcol = __builtin_convertvector(O::ldtr(vb, L::KPB, 16 * I, 16 * w, lane), f32x4);
             const f32x4 ws = *(const f32x4*)(sc + 16 * I + 4 * g);
             const f32x4 bs = *(const f32x4*)(sc + 64 + 16 * I + 4 * g);
             f32x4 zw = ws * kcol, zu = bs * vcol;
@@ -418,7 +386,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     // apply the chunk to both slices:  X <- g_C X + K^T D',  D' = U~ + W~ X^T (chunk-start X)
     auto chain = [&](int q, f32x4 (&XA)[ND], f32x4 (&XB)[ND], const f32x4 (&Ur)[4]) {
         const float* sc = SC(q);
-        const E* kt = KT(q);
+        const E* kb = KB_(q);
         const float gam = sc[192];
         F8 xa[KB], xb[KB];
 #pragma unroll
@@ -460,8 +428,10 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             O::split8(PB[0], PB[1], dBh, dBl);
 #pragma unroll
             for (int m = 0; m < ND; ++m) {
-                const E* kr = kt + (16 * m + c) * L::KT_P + 4 * g + 32 * h;
-                const F8 kf = O::ld44(kr, kr + 16);
+                // K^T operand, PAIR slot map over the half's 32 tokens
+                const F8 kf = __builtin_shufflevector(O::ldtr(kb, L::KPB, 32 * h, 16 * m, lane),
+                                                      O::ldtr(kb, L::KPB, 32 * h + 16, 16 * m, lane), 0, 1, 2, 3,
+                                                      4, 5, 6, 7);
                 f32x4 xa2 = h == 0 ? XA[m] * gam : XA[m];
                 f32x4 xb2 = h == 0 ? XB[m] * gam : XB[m];
                 xa2 = O::mma32(kf, dA, xa2);
@@ -508,36 +478,38 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     };
 
     // The prep wave and the chain waves run separate loops with the same barriers, so
-    // that neither keeps the other's registers live.
+    // that neither keeps the other's registers live.  Pipelined schedule of iteration q:
+    //   chunk q+1 has landed (wait), copies of chunk q+2 are issued, [prep: inverses of q]
+    //   B1 | chain waves: substitution of q   | prep: Gram and norms of q+1
+    //   B2 | chain waves: state update of q   | prep: gates, L fragments of q+1
+    //   B3
     if (prep) {
         f32x4 gr[10];  // Gram tiles of the chunk being prepared
-        fetch(0);
         if constexpr (L::PIPE) {
-            stash(0);
-            if (nq > 1) fetch(1);
+            dma_chunk(0);
+            if (nq > 1) dma_chunk(1);
+            wait_vmem();
             lds_barrier();
             prep1(0, gr);
             lds_barrier();
             prep2(0, gr);
             prep3(0);
             lds_barrier();
-        }
-        for (int q = 0; q < nq; ++q) {
-            if constexpr (L::PIPE) {
+            for (int q = 0; q < nq; ++q) {
                 const bool more = q + 1 < nq;
-                if (more) {
-                    stash(q + 1);
-                    if (q + 2 < nq) fetch(q + 2);
-                }
+                wait_vmem();
+                if (q + 2 < nq) dma_chunk(q + 2);
                 if (q > 0) prep3(q);
                 lds_barrier();  // B1: chunk q+1 in LDS
                 if (more) prep1(q + 1, gr);
                 lds_barrier();  // B2: W of chunk q staged by the chain waves
                 if (more) prep2(q + 1, gr);
                 lds_barrier();  // B3: chunk q's buffers free
-            } else {
-                stash(q);
-                if (q + 1 < nq) fetch(q + 1);
+            }
+        } else {
+            for (int q = 0; q < nq; ++q) {
+                dma_chunk(q);
+                wait_vmem();
                 lds_barrier();
                 prep1(q, gr);
                 lds_barrier();
@@ -557,26 +529,24 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             XB[t] = zero4();
         }
         f32x4 Ur[4];  // U column tile w of the current chunk, pre-scaled by kts
-        fetch(0);
         if constexpr (L::PIPE) {
-            stash(0);
-            if (nq > 1) fetch(1);
+            dma_chunk(0);
+            if (nq > 1) dma_chunk(1);
+            wait_vmem();
             lds_barrier();
             lds_barrier();
             lds_barrier();
         }
         for (int q = 0; q < nq; ++q) {
             if constexpr (L::PIPE) {
-                if (q + 1 < nq) {
-                    stash(q + 1);
-                    if (q + 2 < nq) fetch(q + 2);
-                }
+                wait_vmem();
+                if (q + 2 < nq) dma_chunk(q + 2);
                 lds_barrier();  // B1
                 subst(q, Ur);
                 lds_barrier();  // B2
             } else {
-                stash(q);
-                if (q + 1 < nq) fetch(q + 1);
+                dma_chunk(q);
+                wait_vmem();
                 lds_barrier();
                 lds_barrier();
                 lds_barrier();
@@ -868,8 +838,7 @@ template <typename E, int ND> struct P3 {
 // launchers
 // -------------------------------------------------------------------------------------
 template <typename E, int ND>
-hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p3, hipStream_t st,
-                             void* const* ev) {
+hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev) {
     using L = P1<E, ND>;
     static bool attr_done = false;  // per instantiation
     if (!attr_done) {
@@ -884,25 +853,26 @@ hipError_t launch_gdn_window(const P1Args& p1, const P2Args& p2, const P3Args& p
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    const int BH = p1.BH;
-    const int ngw = (p1.nf + p1.G - 1) / p1.G;
-    hipError_t e = record(ev, 0, st);
+    hipError_t e = record(ev, 2 * phase, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gdn_frame_affine<E, ND>), dim3(ngw, BH), dim3(L::NT), L::LDS_B, st, p1);
-    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess) return e;
-    constexpr int lds2 = P2<E, ND>::LDS_B;
-    hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3((ND + P2<E, ND>::SPW - 1) / P2<E, ND>::SPW, BH), dim3(256), lds2,
-                       st, p2);
-    if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 2, st)) != hipSuccess) return e;
-    constexpr int lds3 = P3<E, ND>::LDS_B;
-    hipLaunchKernelGGL((gdn_frame_readout<E, ND>), dim3(p3.nf, BH), dim3(256), lds3, st, p3);
+    if (phase == 0) {
+        const P1Args& p1 = *(const P1Args*)args;
+        const int ngw = (p1.nf + p1.G - 1) / p1.G;
+        hipLaunchKernelGGL((gdn_frame_affine<E, ND>), dim3(ngw, BH), dim3(L::NT), L::LDS_B, st, p1);
+    } else if (phase == 1) {
+        constexpr int lds2 = P2<E, ND>::LDS_B;
+        hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3((ND + P2<E, ND>::SPW - 1) / P2<E, ND>::SPW, BH), dim3(256),
+                           lds2, st, *(const P2Args*)args);
+    } else {
+        const P3Args& p3 = *(const P3Args*)args;
+        constexpr int lds3 = P3<E, ND>::LDS_B;
+        hipLaunchKernelGGL((gdn_frame_readout<E, ND>), dim3(p3.nf, BH), dim3(256), lds3, st, p3);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return record(ev, 3, st);
+    return record(ev, 2 * phase + 1, st);
 }
 
-#define GDN_INST(E, ND) \
-    template hipError_t launch_gdn_window<E, ND>(const P1Args&, const P2Args&, const P3Args&, hipStream_t, \
-                                                 void* const*);
+#define GDN_INST(E, ND) template hipError_t launch_gdn_phase<E, ND>(int, const void*, int, hipStream_t, void* const*);
 GDN_INST(bf16, 1) GDN_INST(bf16, 2) GDN_INST(bf16, 4) GDN_INST(bf16, 7) GDN_INST(bf16, 8)
 GDN_INST(float, 1) GDN_INST(float, 2) GDN_INST(float, 4) GDN_INST(float, 7) GDN_INST(float, 8)
 

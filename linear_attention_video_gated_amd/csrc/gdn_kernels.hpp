@@ -91,9 +91,11 @@ struct BC3Args {
     int out_f32;
 };
 
-// ev: NULL or 4 events, recorded before the first launch and after each launch.
+// Launchers.  ev: NULL, or the 6 events of one window -- recorded before and after each
+// of the window's three launches, on the stream that launch goes to.
+// phase 0: frame maps (P1Args), 1: chain over groups (P2Args), 2: readout (P3Args).
 template <typename E, int ND>
-hipError_t launch_gdn_window(const P1Args&, const P2Args&, const P3Args&, hipStream_t, void* const* ev);
+hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev);
 template <typename E, int ND>
 hipError_t launch_bc_window(const BC1Args&, const BC2Args&, const BC3Args&, int BH, hipStream_t,
                             void* const* ev);

@@ -19,7 +19,7 @@ GDN_BF16, GDN_F32 = 0, 1
 NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32 = 1, 2, 4, 8
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL = 0, 1, 2
 EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "linear_attn_block_causal",
-           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version")
+           "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -36,7 +36,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("n_frames", ctypes.c_int32),
                 ("frame_len", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p),
+                ("phase_windows", ctypes.c_int32)]
 
 
 _lib = None
@@ -60,6 +61,8 @@ def lib():
         L.linear_attn_block_causal.restype = ctypes.c_int
         L.gdn_workspace_bytes.argtypes = [dp, ctypes.c_int]
         L.gdn_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_window_count.argtypes = [dp, ctypes.c_int]
+        L.gdn_window_count.restype = ctypes.c_int
         L.gdn_status_str.argtypes = [ctypes.c_int]
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -90,10 +93,20 @@ def _dtype_code(dt):
 
 
 def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0, events=None):
-    """events: None or a ctypes array of 4 hipEvent_t handles (per-kernel timing)."""
+    """events: None or a ctypes array of 6 * n hipEvent_t handles, recorded around the
+    three launches of each of the call's first n windows (per-kernel timing)."""
     return Dims(B, H, n_frames, frame_len, d, d, dtype_code, flags,
                 None if workspace is None else workspace.data_ptr(), nbytes,
-                None if events is None else ctypes.cast(events, ctypes.c_void_p).value)
+                None if events is None else ctypes.cast(events, ctypes.c_void_p).value,
+                0 if events is None else len(events) // 6)
+
+
+def window_count(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K, entry=ENTRY_FORWARD):
+    """gdn_window_count: the number of windows (three launches each) such a call makes."""
+    n = lib().gdn_window_count(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, _dtype_code(dtype), flags)),
+                               entry)
+    _check(min(n, 0))
+    return n
 
 
 def workspace_bytes(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K,

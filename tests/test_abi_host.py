@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 1
+    assert gdn.lib().gdn_abi_version() == 2
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
@@ -45,7 +45,7 @@ def test_abi_version_and_status_strings():
 
 
 def dims(B=1, H=2, F=3, N=16, d=32, dtype=gdn.GDN_BF16, flags=gdn.NORMALIZE_K, ws=None, nbytes=0):
-    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None)
+    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None, 0)
 
 
 def wsb(dm, entry=gdn.ENTRY_FORWARD):
@@ -58,11 +58,28 @@ def fwd(dm, q=FAKE, k=FAKE + 2 ** 28, v=FAKE + 2 ** 29, a=FAKE + 2 ** 30, b=FAKE
 
 
 def test_workspace_is_bounded_independently_of_frame_count():
-    sizes = [wsb(dims(B=1, H=20, F=F, N=880, d=112)) for F in (1, 100, 240, 1000, 100000)]
+    frames = (1, 100, 240, 1000, 100000, 200000)
+    sizes = [wsb(dims(B=1, H=20, F=F, N=880, d=112)) for F in frames]
     assert sizes[0] > 0
-    assert max(sizes) <= 1.05 * wsb(dims(B=1, H=20, F=8192 // 20 + 1, N=880, d=112))
+    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]  # stops growing once windows are full
+    # one window of at most 8192 (b, h, frame) units: bounded by 8192 / (B H) frames'
+    # worth of the one-frame workspace (which holds one frame per (b, h))
+    assert sizes[-1] <= (8192 / 20) * sizes[0]
     # and it does not depend on the frame length at all
     assert wsb(dims(F=240, N=880, d=112)) == wsb(dims(F=240, N=16, d=112))
+
+
+def test_window_plan():
+    """Windows hold whole groups of frames and at most 8192 (b, h, frame) units."""
+    L = gdn.lib()
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=20, F=240, N=880, d=112)), gdn.ENTRY_FORWARD) == 1
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=20, F=1000, N=880, d=112)), gdn.ENTRY_FORWARD) == 3
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=2, F=1, N=16, d=32)), gdn.ENTRY_FORWARD) == 1
+    assert L.gdn_window_count(ctypes.byref(dims(d=48)), gdn.ENTRY_FORWARD) == -7
+    assert L.gdn_window_count(ctypes.byref(dims()), 9) == -7
+    # block-causal calls are not cut beyond the workspace bound
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=20, F=21, N=390, d=112, flags=gdn.RELU_QK)),
+                              gdn.ENTRY_BLOCK_CAUSAL) == 1
 
 
 def test_workspace_zero_for_invalid_or_empty():
