@@ -51,7 +51,11 @@ template <typename E, int ND> struct P1 {
     using G = Geo<E, ND>;
     static constexpr bool PIPE = sizeof(E) == 2;
     static constexpr int NB = PIPE ? 2 : 1;       // buffers of the prepared per-chunk inputs
-    static constexpr int NBD = PIPE ? 3 : 1;      // buffers of the raw chunk (K, V, gates)
+    static constexpr int al_(int b) { return (b + 255) / 256 * 256; }
+    // buffers of the raw chunk (K, V, gates): copies run NBD - 1 chunks ahead; four when
+    // they fit in LDS beside everything else, else three
+    static constexpr int FIXED_B = al_(2 * 64 * 4) + 2 * al_((3 * 64 + 16) * 4) + 2 * al_(10 * 64 * 4 * (int)sizeof(E)) +
+                                   al_(64 * (G::D + 4) * (int)sizeof(E)) + al_(4 * 16 * 20 * 4) + al_(7 * 64 * 4);
     static constexpr int NW = ND + 1;             // chain waves + prep wave
     static constexpr int NT = 64 * NW;
     static constexpr int RB = G::D * (int)sizeof(E);  // bytes of one K or V row
@@ -59,6 +63,8 @@ template <typename E, int ND> struct P1 {
     // transposed reads (8 consecutive rows x 32 bytes per half-wave) hit distinct banks
     static constexpr int KPB = ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
     static constexpr int KG = KPB / 16;           // 16-byte granules per LDS row
+    static constexpr int NBD = !PIPE ? 1 : (4 * (2 * al_(64 * KPB) + al_(2 * 64 * 4)) + FIXED_B <= 160 * 1024 ? 4 : 3);
+    static constexpr int PD = NBD - 1;            // chunks the copies run ahead (pipelined)
     static constexpr int DG = RB / 16;            // granules that hold data
     static constexpr int W_P = G::D + 4;          // W staging pitch (elements)
     static constexpr int LD_P = 20;               // diagonal L blocks pitch (floats)
@@ -157,6 +163,23 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                 ((float*)(smem + dst))[lane] = a.alpha[tt];
                 ((float*)(smem + dst + 256))[lane] = a.beta[tt];
             }
+        }
+    };
+
+    // At iteration q chunk q+1 must have landed while the copies of chunks q+2 .. q+PD-1
+    // may still be in flight: wait until at most that many of this wave's copy
+    // instructions are outstanding (copies complete in issue order).
+    int ncopy = 0;  // copy instructions this wave issues per chunk
+    for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
+    if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
+    auto wait_dma_behind = [&](int q) {
+        const int ahead = min(L::PD - 2, nq - 2 - q);  // chunks q+2 .. issued and not needed yet
+        const int n = ahead > 0 ? ahead * ncopy : 0;
+        switch (n < 15 ? n : 15) {
+#define GDN_W(N) case N: __builtin_amdgcn_s_waitcnt(0x0F70 | N); break;
+            GDN_W(0) GDN_W(1) GDN_W(2) GDN_W(3) GDN_W(4) GDN_W(5) GDN_W(6) GDN_W(7)
+            GDN_W(8) GDN_W(9) GDN_W(10) GDN_W(11) GDN_W(12) GDN_W(13) GDN_W(14) GDN_W(15)
+#undef GDN_W
         }
     };
 
@@ -489,6 +512,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             dma_chunk(0);
             if (nq > 1) dma_chunk(1);
             wait_vmem();
+            for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
             lds_barrier();
             prep1(0, gr);
             lds_barrier();
@@ -497,8 +521,8 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             lds_barrier();
             for (int q = 0; q < nq; ++q) {
                 const bool more = q + 1 < nq;
-                wait_vmem();
-                if (q + 2 < nq) dma_chunk(q + 2);
+                wait_dma_behind(q);
+                if (q + L::PD < nq) dma_chunk(q + L::PD);
                 if (q > 0) prep3(q);
                 lds_barrier();  // B1: chunk q+1 in LDS
                 if (more) prep1(q + 1, gr);
@@ -533,14 +557,15 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             dma_chunk(0);
             if (nq > 1) dma_chunk(1);
             wait_vmem();
+            for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
             lds_barrier();
             lds_barrier();
             lds_barrier();
         }
         for (int q = 0; q < nq; ++q) {
             if constexpr (L::PIPE) {
-                wait_vmem();
-                if (q + 2 < nq) dma_chunk(q + 2);
+                wait_dma_behind(q);
+                if (q + L::PD < nq) dma_chunk(q + L::PD);
                 lds_barrier();  // B1
                 subst(q, Ur);
                 lds_barrier();  // B2
