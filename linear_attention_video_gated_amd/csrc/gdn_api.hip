@@ -31,17 +31,29 @@ long long window_units() {
     return v > 0 ? v : kMaxUnits;
 }
 
-// Frames per group of the gated-delta-rule path: the serial chain steps once per group,
-// and groups of frames form the parallel work of the frame-map kernel, so groups grow
-// only while there are still >= ~4 workgroups per CU over the whole call
-// (GDN_GROUP_FRAMES overrides).  Windows hold whole groups.
-int group_frames(long long BH, int n_frames) {
-    long long G = env_ll("GDN_GROUP_FRAMES");
-    if (G <= 0) G = (BH * n_frames) / 1024;
-    if (G < 1) G = 1;
-    if (G > 8) G = 8;
-    if (G > n_frames) G = n_frames;
-    return (int)G;
+// Frames per group of the gated-delta-rule path.  The frame-map kernel runs one
+// workgroup per (b, h, group) and one workgroup per CU (its LDS footprint), so its time
+// goes as (rounds of workgroups over the 256 CUs of an MI355X) x (frames per group);
+// the serial chain takes one step per group.  G minimises the sum of the two, with
+// about 0.066 us per token of a frame in the frame-map kernel and 3 us per chain step
+// (measured at d = 112).  GDN_GROUP_FRAMES overrides.  Windows hold whole groups.
+int group_frames(long long BH, int n_frames, int frame_len) {
+    const long long forced = env_ll("GDN_GROUP_FRAMES");
+    if (forced > 0) return (int)(forced < n_frames ? forced : n_frames);
+    constexpr long long kCUs = 256;
+    const double per_frame = 0.066 * frame_len, per_step = 3.0;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int G = 1; G <= n_frames && G <= 64; ++G) {
+        const long long groups = (n_frames + G - 1) / G;
+        const long long rounds = (BH * groups + kCUs - 1) / kCUs;
+        const double cost = rounds * G * per_frame + groups * per_step;
+        if (cost < best_cost * (1 - 1e-9)) {
+            best_cost = cost;
+            best = G;
+        }
+    }
+    return best;
 }
 constexpr size_t kAlign = 256;
 
@@ -85,7 +97,7 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
     if (p->T > ((long long)1 << 40) / (p->BH ? p->BH : 1) / d->d_k) return GDN_ERR_DIMS;
     if (p->BH == 0 || d->n_frames == 0) return GDN_OK;
     const bool bc = entry == GDN_ENTRY_BLOCK_CAUSAL;
-    if (!bc) p->G = group_frames(p->BH, d->n_frames);
+    if (!bc) p->G = group_frames(p->BH, d->n_frames, d->frame_len);
     const long long G = p->G;
     long long nfw = window_units() / p->BH / G * G;  // whole groups per window
     if (nfw < G) nfw = G;

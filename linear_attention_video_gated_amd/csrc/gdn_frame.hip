@@ -166,14 +166,15 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         }
     };
 
-    // At iteration q chunk q+1 must have landed while the copies of chunks q+2 .. q+PD-1
-    // may still be in flight: wait until at most that many of this wave's copy
-    // instructions are outstanding (copies complete in issue order).
+    // At the end of iteration q chunk q+2 must have landed (the prep wave reads it next)
+    // while the copies of chunks q+3 .. q+PD may still be in flight: wait until at most
+    // that many of this wave's copy instructions are outstanding (they complete in
+    // issue order).
     int ncopy = 0;  // copy instructions this wave issues per chunk
     for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
     if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
     auto wait_dma_behind = [&](int q) {
-        const int ahead = min(L::PD - 2, nq - 2 - q);  // chunks q+2 .. issued and not needed yet
+        const int ahead = min(L::PD - 2, nq - 3 - q);  // chunks q+3 .. issued and not needed yet
         const int n = ahead > 0 ? ahead * ncopy : 0;
         switch (n < 15 ? n : 15) {
 #define GDN_W(N) case N: __builtin_amdgcn_s_waitcnt(0x0F70 | N); break;
@@ -501,10 +502,11 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     };
 
     // The prep wave and the chain waves run separate loops with the same barriers, so
-    // that neither keeps the other's registers live.  Pipelined schedule of iteration q:
-    //   chunk q+1 has landed (wait), copies of chunk q+2 are issued, [prep: inverses of q]
-    //   B1 | chain waves: substitution of q   | prep: Gram and norms of q+1
-    //   B2 | chain waves: state update of q   | prep: gates, L fragments of q+1
+    // that neither keeps the other's registers live.  Pipelined schedule of iteration q
+    // (copies of chunk q+PD are issued at its start):
+    //      | chain waves: substitution of q   | prep: Gram and norms of q+1
+    //   B2 | chain waves: state update of q   | prep: gates, L, inverses of q+1
+    //      (wait for the copies of chunk q+2)
     //   B3
     if (prep) {
         f32x4 gr[10];  // Gram tiles of the chunk being prepared
@@ -513,22 +515,22 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             if (nq > 1) dma_chunk(1);
             wait_vmem();
             for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
-            lds_barrier();
+            lds_barrier();  // chunks 0 and 1 in LDS
             prep1(0, gr);
-            lds_barrier();
             prep2(0, gr);
             prep3(0);
-            lds_barrier();
+            lds_barrier();  // chunk 0 prepared
             for (int q = 0; q < nq; ++q) {
                 const bool more = q + 1 < nq;
-                wait_dma_behind(q);
                 if (q + L::PD < nq) dma_chunk(q + L::PD);
-                if (q > 0) prep3(q);
-                lds_barrier();  // B1: chunk q+1 in LDS
                 if (more) prep1(q + 1, gr);
                 lds_barrier();  // B2: W of chunk q staged by the chain waves
-                if (more) prep2(q + 1, gr);
-                lds_barrier();  // B3: chunk q's buffers free
+                if (more) {
+                    prep2(q + 1, gr);
+                    prep3(q + 1);
+                }
+                wait_dma_behind(q);
+                lds_barrier();  // B3: chunk q+1 prepared, chunk q+2 in LDS, chunk q's buffers free
             }
         } else {
             for (int q = 0; q < nq; ++q) {
@@ -560,13 +562,10 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
             lds_barrier();
             lds_barrier();
-            lds_barrier();
         }
         for (int q = 0; q < nq; ++q) {
             if constexpr (L::PIPE) {
-                wait_dma_behind(q);
                 if (q + L::PD < nq) dma_chunk(q + L::PD);
-                lds_barrier();  // B1
                 subst(q, Ur);
                 lds_barrier();  // B2
             } else {
@@ -581,6 +580,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             chain(q, XA, XB, Ur);
             const int fl = q / nch;
             if (q - fl * nch == nch - 1) emit(fl, XA, XB);
+            if constexpr (L::PIPE) wait_dma_behind(q);
             lds_barrier();  // B3
         }
     }

@@ -58,15 +58,17 @@ def fwd(dm, q=FAKE, k=FAKE + 2 ** 28, v=FAKE + 2 ** 29, a=FAKE + 2 ** 30, b=FAKE
 
 
 def test_workspace_is_bounded_independently_of_frame_count():
-    frames = (1, 100, 240, 1000, 100000, 200000)
+    frames = [1, 2, 3, 7, 21, 100, 240, 409, 410, 1000, 5000, 100000, 200000]
     sizes = [wsb(dims(B=1, H=20, F=F, N=880, d=112)) for F in frames]
-    assert sizes[0] > 0
-    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]  # stops growing once windows are full
+    assert min(sizes) > 0
     # one window of at most 8192 (b, h, frame) units: bounded by 8192 / (B H) frames'
-    # worth of the one-frame workspace (which holds one frame per (b, h))
-    assert sizes[-1] <= (8192 / 20) * sizes[0]
-    # and it does not depend on the frame length at all
-    assert wsb(dims(F=240, N=880, d=112)) == wsb(dims(F=240, N=16, d=112))
+    # worth of the one-frame workspace (which holds one frame per (b, h)), whatever F
+    assert max(sizes) <= (8192 / 20) * sizes[0]
+    # nor with the frame length (which only changes how frames are grouped)
+    one = wsb(dims(F=1, N=16, d=112))
+    assert one == wsb(dims(F=1, N=4000, d=112))
+    for N in (1, 16, 390, 880, 4000):
+        assert wsb(dims(F=240, N=N, d=112)) <= (8192 / 2) * one
 
 
 def test_window_plan():
