@@ -158,14 +158,21 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         const int f0 = wi * p.nfw;
         const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
         const bool last = wi == p.nwin - 1;
+        // a call that keeps no state and has a single group reads state_in directly (its
+        // layout is that of the per-group states with one group): no chain to run
+        const bool no_chain = !state_out && p.nwin == 1 && nf <= p.G;
+        const float* s_before = no_chain ? state_in : sgrp;
         const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, apack, bt};
         const P2Args a2{apack, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
-        const P3Args a3{q, out, apack, bt, sgrp, p.T, d->frame_len, f0, nf, p.G, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
+        const P3Args a3{q, out, apack, bt, s_before, p.T, d->frame_len, f0, nf, p.G, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
         void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
-        if (launch_gdn_phase<E, ND>(0, &a1, BH, st, ev) != hipSuccess ||
-            launch_gdn_phase<E, ND>(1, &a2, BH, st, ev) != hipSuccess ||
-            launch_gdn_phase<E, ND>(2, &a3, BH, st, ev) != hipSuccess)
+        if (launch_gdn_phase<E, ND>(0, &a1, BH, st, ev) != hipSuccess) return GDN_ERR_HIP;
+        if (no_chain) {
+            if (record(ev, 2, st) != hipSuccess || record(ev, 3, st) != hipSuccess) return GDN_ERR_HIP;
+        } else if (launch_gdn_phase<E, ND>(1, &a2, BH, st, ev) != hipSuccess) {
             return GDN_ERR_HIP;
+        }
+        if (launch_gdn_phase<E, ND>(2, &a3, BH, st, ev) != hipSuccess) return GDN_ERR_HIP;
     }
     return GDN_OK;
 }

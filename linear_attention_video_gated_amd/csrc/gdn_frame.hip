@@ -733,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
         const int sl = own[u] ? w + 4 * u : 0;
         const float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + (long long)(16 * sl + c) * D;
 #pragma unroll
-        for (int t = 0; t < ND; ++t) X[u][t] = *(const f32x4*)(sg + 16 * t + 4 * g);
+        for (int t = 0; t < ND; ++t) X[u][t] = a.Sgrp ? *(const f32x4*)(sg + 16 * t + 4 * g) : zero4();
     }
     F8 xh[NSL][KB], xl[NSL][KB];
 #pragma unroll

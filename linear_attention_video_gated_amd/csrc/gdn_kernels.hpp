@@ -46,7 +46,7 @@ struct P3Args {
     void* out;
     const void* Apack;
     const float* Bt;
-    const float* Sgrp;
+    const float* Sgrp;  // state before each group, or NULL for a zero state
     long long T;
     int frame_len;
     int f0;

@@ -111,6 +111,23 @@ def test_gdn_readonly_matches_forward_and_keeps_state():
     assert torch.equal(dv["state_in"], s_before)
 
 
+@pytest.mark.parametrize("with_state", [True, False])
+def test_gdn_readonly_single_frame(with_state):
+    """One frame, read-only: the path that reads state_in directly (no chain launch)."""
+    inp = gdn_inputs(3, 2, 1, 300, 112, workload_id=325, state_std=0.3 if with_state else None, gates="near_one")
+    dv = to_dev(inp)
+    out, st = gdn.frame_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 1, 300,
+                                state_in=dv["state_in"], out_dtype=torch.float32)
+    out_ro = gdn.frame_forward_readonly(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 1, 300,
+                                        state_in=dv["state_in"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out_ro, out)
+    ro, rs = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], 1, 300,
+                                state_in=inp["state_in"])
+    check("out", out_ro, ro, 2e-2)
+    check("state", st, rs, 2e-2)
+
+
 def test_gdn_state_in_place():
     inp = gdn_inputs(1, 2, 3, 70, 112, workload_id=330, state_std=0.2, gates="near_one")
     dv = to_dev(inp)
