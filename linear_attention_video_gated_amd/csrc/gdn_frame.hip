@@ -50,12 +50,7 @@ namespace gdn {
 template <typename E, int ND> struct P1 {
     using G = Geo<E, ND>;
     static constexpr bool PIPE = sizeof(E) == 2;
-    static constexpr int NB = PIPE ? 2 : 1;       // buffers of the prepared per-chunk inputs
-    static constexpr int al_(int b) { return (b + 255) / 256 * 256; }
-    // buffers of the raw chunk (K, V, gates): copies run NBD - 1 chunks ahead; four when
-    // they fit in LDS beside everything else, else three
-    static constexpr int FIXED_B = al_(2 * 64 * 4) + 2 * al_((3 * 64 + 16) * 4) + 2 * al_(10 * 64 * 4 * (int)sizeof(E)) +
-                                   al_(64 * (G::D + 4) * (int)sizeof(E)) + al_(4 * 16 * 20 * 4) + al_(7 * 64 * 4);
+    static constexpr int al(int b) { return (b + 255) / 256 * 256; }
     static constexpr int NW = ND + 1;             // chain waves + prep wave
     static constexpr int NT = 64 * NW;
     static constexpr int RB = G::D * (int)sizeof(E);  // bytes of one K or V row
@@ -63,29 +58,41 @@ template <typename E, int ND> struct P1 {
     // transposed reads (8 consecutive rows x 32 bytes per half-wave) hit distinct banks
     static constexpr int KPB = ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
     static constexpr int KG = KPB / 16;           // 16-byte granules per LDS row
-    static constexpr int NBD = !PIPE ? 1 : (4 * (2 * al_(64 * KPB) + al_(2 * 64 * 4)) + FIXED_B <= 160 * 1024 ? 4 : 3);
-    static constexpr int PD = NBD - 1;            // chunks the copies run ahead (pipelined)
     static constexpr int DG = RB / 16;            // granules that hold data
     static constexpr int W_P = G::D + 4;          // W staging pitch (elements)
     static constexpr int LD_P = 20;               // diagonal L blocks pitch (floats)
     static constexpr int NFR = 10;                // fragments: 6 L_IJ, 4 (T_II - I)
     static constexpr int FR_E = NFR * 64 * 4;     // elements per fragment set
-    static constexpr int al(int b) { return (b + 255) / 256 * 256; }
     static constexpr int KV_B = al(64 * KPB);
     static constexpr int RAW_B = al(2 * 64 * 4);
     static constexpr int SC_B = al((3 * 64 + 16) * 4);
     static constexpr int FR_B = al(FR_E * (int)sizeof(E));
     static constexpr int W_B = al(64 * W_P * (int)sizeof(E));
     static constexpr int LD_B = al(4 * 16 * LD_P * 4);
-    static constexpr int OFF_K = 0;                        // [NBD] row-major K chunk
-    static constexpr int OFF_V = OFF_K + NBD * KV_B;       // [NBD] row-major V chunk
-    static constexpr int OFF_RAW = OFF_V + NBD * KV_B;     // [NBD] alpha[64], beta[64]
-    static constexpr int OFF_SC = OFF_RAW + NBD * RAW_B;   // [NB] per-token scales + gamma
-    static constexpr int OFF_FR = OFF_SC + NB * SC_B;      // [NB] substitution fragments
-    static constexpr int OFF_W = OFF_FR + NB * FR_B;       // W staging (chain waves)
-    static constexpr int OFF_LD = OFF_W + W_B;             // diagonal blocks of L (prep wave)
+    static constexpr int TK_B = al(7 * 64 * 4);
+    // Buffer counts.  OV (overlapped): the chain waves run the state update of chunk q
+    // together with the substitution of chunk q+1, the prep wave prepares chunk q+2 and
+    // copies of chunk q+3 are in flight -- K for chunks q..q+3, V and gates for q+1..q+3,
+    // scalars for q..q+2, fragments and W for two chunks.  Used where it fits in LDS.
+    static constexpr int ov_bytes() {
+        return 4 * KV_B + 3 * KV_B + 3 * RAW_B + 3 * SC_B + 2 * FR_B + 2 * W_B + LD_B + TK_B;
+    }
+    static constexpr bool OV = PIPE && ov_bytes() <= 160 * 1024;
+    static constexpr int NB = PIPE ? 2 : 1;       // fragment sets
+    static constexpr int NBK = OV ? 4 : (!PIPE ? 1 : 3);   // K chunk buffers
+    static constexpr int NBV = OV ? 3 : NBK;      // V chunk and gate buffers
+    static constexpr int NBS = OV ? 3 : NB;       // per-token scalar sets
+    static constexpr int NBW = OV ? 2 : 1;        // W staging buffers
+    static constexpr int PD = PIPE ? (OV ? 3 : NBK - 1) : 0;  // chunks the copies run ahead
+    static constexpr int OFF_K = 0;                        // [NBK] row-major K chunk
+    static constexpr int OFF_V = OFF_K + NBK * KV_B;       // [NBV] row-major V chunk
+    static constexpr int OFF_RAW = OFF_V + NBV * KV_B;     // [NBV] alpha[64], beta[64]
+    static constexpr int OFF_SC = OFF_RAW + NBV * RAW_B;   // [NBS] per-token scales + gamma
+    static constexpr int OFF_FR = OFF_SC + NBS * SC_B;     // [NB] substitution fragments
+    static constexpr int OFF_W = OFF_FR + NB * FR_B;       // [NBW] W staging (chain waves)
+    static constexpr int OFF_LD = OFF_W + NBW * W_B;       // diagonal blocks of L (prep wave)
     static constexpr int OFF_TK = OFF_LD + LD_B;           // per-token scalars (prep wave)
-    static constexpr int LDS_B = OFF_TK + al(7 * 64 * 4);
+    static constexpr int LDS_B = OFF_TK + TK_B;
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
     static_assert(RB % 16 == 0, "rows are whole 16-byte granules");
     static constexpr int APK_E = G::ND * G::KB * G::FRAG;  // A fragments (elements)
@@ -108,15 +115,15 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
     float* const sSC0 = (float*)(smem + L::OFF_SC);
     E* const sFR0 = (E*)(smem + L::OFF_FR);
-    E* const sW = (E*)(smem + L::OFF_W);
     float* const sLD = (float*)(smem + L::OFF_LD);
     float* const sTK = (float*)(smem + L::OFF_TK);
     constexpr int BM = L::NB - 1;
-    auto KB_ = [&](int p) { return (E*)(smem + L::OFF_K + (p % L::NBD) * L::KV_B); };
-    auto VB_ = [&](int p) { return (E*)(smem + L::OFF_V + (p % L::NBD) * L::KV_B); };
-    auto RAW = [&](int p) { return (float*)(smem + L::OFF_RAW + (p % L::NBD) * L::RAW_B); };
-    auto SC = [&](int p) { return (float*)((unsigned char*)sSC0 + (p & BM) * L::SC_B); };
+    auto KB_ = [&](int p) { return (E*)(smem + L::OFF_K + (p % L::NBK) * L::KV_B); };
+    auto VB_ = [&](int p) { return (E*)(smem + L::OFF_V + (p % L::NBV) * L::KV_B); };
+    auto RAW = [&](int p) { return (float*)(smem + L::OFF_RAW + (p % L::NBV) * L::RAW_B); };
+    auto SC = [&](int p) { return (float*)((unsigned char*)sSC0 + (p % L::NBS) * L::SC_B); };
     auto FR = [&](int p) { return (E*)((unsigned char*)sFR0 + (p & BM) * L::FR_B); };
+    auto WB_ = [&](int p) { return (E*)(smem + L::OFF_W + (p % L::NBW) * L::W_B); };
     // SC layout: [0,64) ws = b e^G n, [64,128) b, [128,192) kts = e^{G_C - G} n, [192] gamma_C
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,13 +156,14 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const int ii = isk ? i : i - L::KG;
             const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
             const long long el = (t0 + min(row, Cc - 1)) * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
-            const int dst = (isk ? L::OFF_K : L::OFF_V) + (p % L::NBD) * L::KV_B + ii * 1024;
+            const int dst = isk ? L::OFF_K + (p % L::NBK) * L::KV_B + ii * 1024
+                                : L::OFF_V + (p % L::NBV) * L::KV_B + ii * 1024;
             if constexpr (L::PIPE) dma16((isk ? kp : vp) + el, smem + dst);
             else *(u32x4*)(smem + dst + 16 * lane) = *(const u32x4*)((isk ? kp : vp) + el);  // same copy, synchronous
         }
         if (!additive && w == (2 * L::KG) % L::NW) {
             const long long tt = tok0 + t0 + min(lane, Cc - 1);
-            const int dst = L::OFF_RAW + (p % L::NBD) * L::RAW_B;
+            const int dst = L::OFF_RAW + (p % L::NBV) * L::RAW_B;
             if constexpr (L::PIPE) {
                 dma4(a.alpha + tt, smem + dst);
                 dma4(a.beta + tt, smem + dst + 256);
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const f32x4 s = *(const f32x4*)(sc + 128 + 16 * I + 4 * g);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                sW[(16 * I + 4 * g + ii) * L::W_P + 16 * w + c] = O::cvt(-s[ii] * XW[I][ii]);
+                WB_(q)[(16 * I + 4 * g + ii) * L::W_P + 16 * w + c] = O::cvt(-s[ii] * XW[I][ii]);
                 Ur[I][ii] *= s[ii];
             }
         }
@@ -430,7 +438,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                 const int tt = 2 * h + u;
                 PA[u] = zero4();
                 PB[u] = Ur[tt];
-                const E* wr = sW + (16 * tt + c) * L::W_P + 4 * g;
+                const E* wr = WB_(q) + (16 * tt + c) * L::W_P + 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     F8 wf;
@@ -502,15 +510,51 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     };
 
     // The prep wave and the chain waves run separate loops with the same barriers, so
-    // that neither keeps the other's registers live.  Pipelined schedule of iteration q
-    // (copies of chunk q+PD are issued at its start):
+    // that neither keeps the other's registers live.
+    //
+    // Overlapped schedule (OV), one barrier per chunk.  Iteration q (copies of chunk q+3
+    // are issued at its start):
+    //      chain waves: state update of q, then substitution of q+1
+    //      prep wave:   Gram, norms, gates, L and diagonal inverses of q+2
+    //      (wait for the copies of chunk q+3)
+    //   B
+    //
+    // Two-phase schedule (where the OV buffers do not fit), iteration q (copies of chunk
+    // q+PD are issued at its start):
     //      | chain waves: substitution of q   | prep: Gram and norms of q+1
     //   B2 | chain waves: state update of q   | prep: gates, L, inverses of q+1
     //      (wait for the copies of chunk q+2)
     //   B3
     if (prep) {
         f32x4 gr[10];  // Gram tiles of the chunk being prepared
-        if constexpr (L::PIPE) {
+        if constexpr (L::OV) {
+            dma_chunk(0);
+            if (nq > 1) dma_chunk(1);
+            wait_vmem();
+            if (nq > 2) dma_chunk(2);
+            lds_barrier();  // chunks 0 and 1 in LDS
+            prep1(0, gr);
+            prep2(0, gr);
+            prep3(0);
+            lds_barrier();  // chunk 0 prepared
+            if (nq > 1) {
+                prep1(1, gr);
+                prep2(1, gr);
+                prep3(1);
+            }
+            wait_vmem();
+            lds_barrier();  // chunk 1 prepared, chunk 0 substituted, chunk 2 in LDS
+            for (int q = 0; q < nq; ++q) {
+                if (q + 3 < nq) dma_chunk(q + 3);
+                if (q + 2 < nq) {
+                    prep1(q + 2, gr);
+                    prep2(q + 2, gr);
+                    prep3(q + 2);
+                }
+                wait_vmem();
+                lds_barrier();  // chunk q+2 prepared, q+1 substituted, q+3 in LDS
+            }
+        } else if constexpr (L::PIPE) {
             dma_chunk(0);
             if (nq > 1) dma_chunk(1);
             wait_vmem();
@@ -554,34 +598,55 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             for (int i = 0; i < 4; ++i) XA[t][i] = (16 * w + c == 16 * t + 4 * g + i) ? 1.f : 0.f;
             XB[t] = zero4();
         }
-        f32x4 Ur[4];  // U column tile w of the current chunk, pre-scaled by kts
-        if constexpr (L::PIPE) {
+        f32x4 Ur[4];  // U column tile w of the chunk to be applied next, pre-scaled by kts
+        if constexpr (L::OV) {
             dma_chunk(0);
             if (nq > 1) dma_chunk(1);
             wait_vmem();
-            for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
+            if (nq > 2) dma_chunk(2);
             lds_barrier();
             lds_barrier();
-        }
-        for (int q = 0; q < nq; ++q) {
-            if constexpr (L::PIPE) {
-                if (q + L::PD < nq) dma_chunk(q + L::PD);
-                subst(q, Ur);
-                lds_barrier();  // B2
-            } else {
-                dma_chunk(q);
+            subst(0, Ur);
+            wait_vmem();
+            lds_barrier();
+            for (int q = 0; q < nq; ++q) {
+                if (q + 3 < nq) dma_chunk(q + 3);
+                chain(q, XA, XB, Ur);
+                const int fl = q / nch;
+                if (q - fl * nch == nch - 1) emit(fl, XA, XB);
+                if (q + 1 < nq) subst(q + 1, Ur);
                 wait_vmem();
                 lds_barrier();
+            }
+        } else {
+            if constexpr (L::PIPE) {
+                dma_chunk(0);
+                if (nq > 1) dma_chunk(1);
+                wait_vmem();
+                for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
                 lds_barrier();
-                lds_barrier();
-                subst(q, Ur);
                 lds_barrier();
             }
-            chain(q, XA, XB, Ur);
-            const int fl = q / nch;
-            if (q - fl * nch == nch - 1) emit(fl, XA, XB);
-            if constexpr (L::PIPE) wait_dma_behind(q);
-            lds_barrier();  // B3
+            for (int q = 0; q < nq; ++q) {
+                if constexpr (L::PIPE) {
+                    if (q + L::PD < nq) dma_chunk(q + L::PD);
+                    subst(q, Ur);
+                    lds_barrier();  // B2
+                } else {
+                    dma_chunk(q);
+                    wait_vmem();
+                    lds_barrier();
+                    lds_barrier();
+                    lds_barrier();
+                    subst(q, Ur);
+                    lds_barrier();
+                }
+                chain(q, XA, XB, Ur);
+                const int fl = q / nch;
+                if (q - fl * nch == nch - 1) emit(fl, XA, XB);
+                if constexpr (L::PIPE) wait_dma_behind(q);
+                lds_barrier();  // B3
+            }
         }
     }
 }
