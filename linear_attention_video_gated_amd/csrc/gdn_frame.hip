@@ -39,20 +39,25 @@ namespace gdn {
 // -------------------------------------------------------------------------------------
 // Phase 1: per-frame partial affine maps of each group of frames
 // -------------------------------------------------------------------------------------
-// Workgroup = ND "chain" waves + 1 "prep" wave, software-pipelined by one chunk: while
-// chain wave w (16-row slices w of A and of B) runs chunk q -- block substitution for W
-// column tile w and U column tile w, then the state update -- the prep wave prepares
-// chunk q+1: key norms, gate prefix, Gram matrix, scaled L, inverses of the diagonal
-// 16x16 blocks of (I + L), and the bf16 operand fragments the substitution consumes.
-// Three barriers per chunk; the per-chunk inputs of the chain waves are double-buffered.
-// fp32 inputs do not fit two buffers in LDS at d >= 112; they run the same stages
-// one after the other on single buffers (PIPE = false).
+// Workgroup = ND "chain" waves + "prep" waves, software-pipelined: chain wave w owns the
+// 16-row slices w of A and of B; per chunk it runs the block substitution for W column
+// tile w and U column tile w, then the state update.  The prep waves prepare chunks
+// ahead: key norms, gate prefix, Gram matrix, scaled L, inverses of the 16x16 diagonal
+// blocks of (I + L), and the bf16 operand fragments the substitution consumes.
+//  - OV (bf16 where the buffers fit in LDS): two prep waves, which also issue every
+//    global -> LDS copy so that the chain waves never stall on the memory pipeline; one
+//    barrier per chunk (schedule at the main loop).
+//  - otherwise one prep wave and two barriers per chunk (bf16, d = 128), or the same
+//    stages one after the other on single buffers (fp32 inputs, whose buffers do not fit
+//    twice in LDS at d >= 112).
+template <int V> struct RoleC {
+    static constexpr int value = V;
+};
+
 template <typename E, int ND> struct P1 {
     using G = Geo<E, ND>;
     static constexpr bool PIPE = sizeof(E) == 2;
     static constexpr int al(int b) { return (b + 255) / 256 * 256; }
-    static constexpr int NW = ND + 1;             // chain waves + prep wave
-    static constexpr int NT = 64 * NW;
     static constexpr int RB = G::D * (int)sizeof(E);  // bytes of one K or V row
     // LDS row pitch: a multiple of 32 bytes with an odd count of 32-byte units, so that the
     // transposed reads (8 consecutive rows x 32 bytes per half-wave) hit distinct banks
@@ -75,9 +80,12 @@ template <typename E, int ND> struct P1 {
     // copies of chunk q+3 are in flight -- K for chunks q..q+3, V and gates for q+1..q+3,
     // scalars for q..q+2, fragments and W for two chunks.  Used where it fits in LDS.
     static constexpr int ov_bytes() {
-        return 4 * KV_B + 3 * KV_B + 3 * RAW_B + 3 * SC_B + 2 * FR_B + 2 * W_B + LD_B + TK_B;
+        return 4 * KV_B + 3 * KV_B + 3 * RAW_B + 3 * SC_B + 2 * FR_B + 2 * W_B + LD_B + 2 * TK_B;
     }
     static constexpr bool OV = PIPE && ov_bytes() <= 160 * 1024;
+    static constexpr int NPW = OV ? 2 : 1;        // prep waves
+    static constexpr int NW = ND + NPW;           // chain waves + prep waves
+    static constexpr int NT = 64 * NW;
     static constexpr int NB = PIPE ? 2 : 1;       // fragment sets
     static constexpr int NBK = OV ? 4 : (!PIPE ? 1 : 3);   // K chunk buffers
     static constexpr int NBV = OV ? 3 : NBK;      // V chunk and gate buffers
@@ -91,8 +99,8 @@ template <typename E, int ND> struct P1 {
     static constexpr int OFF_FR = OFF_SC + NBS * SC_B;     // [NB] substitution fragments
     static constexpr int OFF_W = OFF_FR + NB * FR_B;       // [NBW] W staging (chain waves)
     static constexpr int OFF_LD = OFF_W + NBW * W_B;       // diagonal blocks of L (prep wave)
-    static constexpr int OFF_TK = OFF_LD + LD_B;           // per-token scalars (prep wave)
-    static constexpr int LDS_B = OFF_TK + TK_B;
+    static constexpr int OFF_TK = OFF_LD + LD_B;           // [NPW] per-token scalars (prep waves)
+    static constexpr int LDS_B = OFF_TK + NPW * TK_B;
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
     static_assert(RB % 16 == 0, "rows are whole 16-byte granules");
     static constexpr int APK_E = G::ND * G::KB * G::FRAG;  // A fragments (elements)
@@ -103,8 +111,10 @@ template <typename E, int ND> struct P1 {
 __host__ __device__ constexpr int frL(int I, int J) { return I * (I - 1) / 2 + J; }
 __host__ __device__ constexpr int frTm(int I) { return 6 + I; }
 
-template <typename E, int ND>
-__global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
+// MODE = the call's GDN_F_NORMALIZE_K (bit 0) and GDN_F_ADDITIVE (bit 1) flags, fixed at
+// compile time so that the per-tile choices they make are not branches.
+template <typename E, int ND, int MODE>
+__global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a) {
     using L = P1<E, ND>;
     using O = Ops<E>;
     using F8 = typename O::F8;
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     float* const sSC0 = (float*)(smem + L::OFF_SC);
     E* const sFR0 = (E*)(smem + L::OFF_FR);
     float* const sLD = (float*)(smem + L::OFF_LD);
-    float* const sTK = (float*)(smem + L::OFF_TK);
+    float* const sTK0 = (float*)(smem + L::OFF_TK);
     constexpr int BM = L::NB - 1;
     auto KB_ = [&](int p) { return (E*)(smem + L::OFF_K + (p % L::NBK) * L::KV_B); };
     auto VB_ = [&](int p) { return (E*)(smem + L::OFF_V + (p % L::NBV) * L::KV_B); };
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const bool prep = (w == ND);
+    const bool prep = (w >= ND);
     const int gi = blockIdx.x, bh = blockIdx.y;
     const int N = a.frame_len;
     const int fw0 = gi * a.G;                              // first frame (in window) of the group
@@ -136,8 +146,8 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw0) * N;
     const E* kp = (const E*)a.k + tok0 * D;
     const E* vp = (const E*)a.v + tok0 * D;
-    const bool additive = (a.flags & 2u) != 0;
-    const bool normalize = (a.flags & 1u) != 0;
+    constexpr bool additive = (MODE & 2) != 0;
+    constexpr bool normalize = (MODE & 1) != 0;
     const int nch = (N + 63) / 64;
     const int nq = nfg * nch;                   // chunks of the group, frame by frame
     auto chunk_t0 = [&](int q) { const int f = q / nch; return (long long)f * N + (q - f * nch) * 64; };
@@ -148,10 +158,13 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     //      instructions are dealt round-robin to all waves.  Rows past the chunk's end and
     //      padding granules copy a valid in-bounds granule instead (their values are
     //      finite and multiplied by zero scale factors, never used as data).
-    auto dma_chunk = [&](int p) {
+    // copy instructions dealt round-robin to the waves whose bits are set in `mask`
+    auto dma_chunk = [&](int p, unsigned mask) {
+        if (!((mask >> w) & 1u)) return;
+        const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
         const long long t0 = chunk_t0(p);
         const int Cc = chunk_len(p);
-        for (int i = w; i < 2 * L::KG; i += L::NW) {
+        for (int i = wi; i < 2 * L::KG; i += nw) {
             const bool isk = i < L::KG;
             const int ii = isk ? i : i - L::KG;
             const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             if constexpr (L::PIPE) dma16((isk ? kp : vp) + el, smem + dst);
             else *(u32x4*)(smem + dst + 16 * lane) = *(const u32x4*)((isk ? kp : vp) + el);  // same copy, synchronous
         }
-        if (!additive && w == (2 * L::KG) % L::NW) {
+        if (!additive && wi == (2 * L::KG) % nw) {
             const long long tt = tok0 + t0 + min(lane, Cc - 1);
             const int dst = L::OFF_RAW + (p % L::NBV) * L::RAW_B;
             if constexpr (L::PIPE) {
@@ -178,6 +191,14 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     // while the copies of chunks q+3 .. q+PD may still be in flight: wait until at most
     // that many of this wave's copy instructions are outstanding (they complete in
     // issue order).
+    constexpr unsigned kAll = (1u << L::NW) - 1u;
+    // Waves that issue the copies in the overlapped schedule's loop: chain waves 0..3 and
+    // both prep waves, five or so copy instructions each.  Measured at d = 112: a wave
+    // keeps only a few global -> LDS copies in flight and stalls at issue beyond that, so
+    // one or two issuing waves are far too slow, while all waves stall every chain wave;
+    // chain waves 0..3 are the first of the two chain waves on their SIMD and finish their
+    // chunk early, which hides their stall.
+    constexpr unsigned kCopy = L::OV ? (0xFu | (3u << ND)) : kAll;
     int ncopy = 0;  // copy instructions this wave issues per chunk
     for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
     if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
@@ -192,9 +213,15 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         }
     };
 
-    // ---- prep wave, first part (beside the substitution): Gram matrix on the matrix
-    //      cores and the key norms
-    auto prep1 = [&](int p, f32x4 (&gr)[10]) {
+    // Prep roles: with two prep waves, role 0 takes the diagonal blocks of L (and their
+    // inverses, prep3) and the per-token scalars the chain waves read, role 1 the
+    // off-diagonal blocks; each computes the key norms and gate prefix it needs itself.
+    // A single prep wave (role 2) does all of it.
+    auto has_diag = [](auto R) { return R.value != 1; };
+    auto has_off = [](auto R) { return R.value != 0; };
+    // ---- prep, first part: Gram matrix on the matrix cores and the key norms
+    auto prep1 = [&](int p, f32x4 (&gr)[10], auto R) {
+        float* const sTK = sTK0 + (R.value == 1 ? 7 * 64 : 0);
         const int Cc = chunk_len(p);
         const int t = lane;
         const bool valid = t < Cc;
@@ -215,6 +242,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
                 const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;  // lower-triangle tile (I, J)
                 const int J = q - I * (I + 1) / 2;
                 gr[q] = zero4();
+                if (I != J && !has_off(R)) continue;  // (diagonal tiles give the norms)
                 if (!additive || (normalize && I == J)) {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) gr[q] = O::mma32(kf[J][kb], kf[I][kb], gr[q]);
@@ -229,32 +257,35 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const f32x4 x = gr[I * (I + 3) / 2];
-                const float d = e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+                float d = x[0];  // x[e], as selects
+                d = e == 1 ? x[1] : d;
+                d = e == 2 ? x[2] : d;
+                d = e == 3 ? x[3] : d;
                 const float v = __shfl(d, src);
-                if ((t >> 4) == I) n2 = v;
+                n2 = (t >> 4) == I ? v : n2;
             }
         }
         const float nrm = valid ? (normalize ? hw_rsq(fmaxf(n2, 1e-12f)) : 1.f) : 0.f;
         sTK[64 + t] = nrm;
     };
-    // ---- prep wave, second part (beside the state update): gate prefix and per-token
-    //      scalars, L from the Gram tiles, its off-diagonal blocks as operand fragments,
-    //      its diagonal blocks to LDS
-    auto prep2 = [&](int p, f32x4 (&gr)[10]) {
+    // ---- prep, second part: gate prefix and per-token scalars, L from the Gram tiles, its
+    //      off-diagonal blocks as operand fragments, its diagonal blocks to LDS
+    auto prep2 = [&](int p, f32x4 (&gr)[10], auto R) {
+        float* const sTK = sTK0 + (R.value == 1 ? 7 * 64 : 0);
         E* fr = FR(p);
         const int Cc = chunk_len(p);
         float* sc = SC(p);
         const int t = lane;
         const bool valid = t < Cc;
         const float nrm = sTK[64 + t];
+        // (rows past the chunk's end hold finite copies: read them, then select)
         float gl = 0.f, be = 0.f;
-        if (valid) {
-            if (additive) {
-                be = 1.f;
-            } else {
-                gl = hw_log2(fmaxf(RAW(p)[t], FLT_MIN));
-                be = RAW(p)[64 + t];
-            }
+        if constexpr (additive) {
+            be = valid ? 1.f : 0.f;
+        } else {
+            const float al = RAW(p)[t], bl = RAW(p)[64 + t];
+            gl = valid ? hw_log2(fmaxf(al, FLT_MIN)) : 0.f;
+            be = valid ? bl : 0.f;
         }
         const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
         // (the lane-read builtins are integer-typed: move the bits, not the value)
@@ -262,10 +293,12 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
         };
         const float GC = lane_of(Gs, 63);
-        sc[t] = additive ? 0.f : be * hw_exp2(Gs) * nrm;
-        sc[64 + t] = be;
-        sc[128 + t] = hw_exp2(GC - Gs) * nrm;
-        if (t == 0) sc[192] = hw_exp2(GC);
+        if (has_diag(R)) {
+            sc[t] = additive ? 0.f : be * hw_exp2(Gs) * nrm;
+            sc[64 + t] = be;
+            sc[128 + t] = hw_exp2(GC - Gs) * nrm;
+            if (t == 0) sc[192] = hw_exp2(GC);
+        }
         // decay factors of L split at the end of 16-token block J (both factors <= 1):
         // e^{G_i - G_j} = e^{G_i - G_end(J)} e^{G_end(J) - G_j} for i in a later block
         const int Jt = t >> 4;
@@ -301,6 +334,7 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const int J = q - I * (I + 1) / 2;
             const int i = 16 * I + c;
             f32x4& acc = gr[q];
+            if (I != J ? !has_off(R) : !has_diag(R)) continue;
             if (additive) {
                 acc = zero4();
             } else if (I != J) {
@@ -319,31 +353,29 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
             const int I = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
             const int J = q - I * (I + 1) / 2;
             if (I != J) {
-                *(F4*)(fr + (frL(I, J) * 64 + lane) * 4) = O::pack4(gr[q]);
+                if (has_off(R)) *(F4*)(fr + (frL(I, J) * 64 + lane) * 4) = O::pack4(gr[q]);
             } else {
-                *(f32x4*)(sLD + (16 * I + c) * L::LD_P + 4 * g) = gr[q];
+                if (has_diag(R)) *(f32x4*)(sLD + (16 * I + c) * L::LD_P + 4 * g) = gr[q];
             }
         }
     };
-    // ---- prep wave, third part (beside the next chunk's stash): inverses of the diagonal
-    //      blocks of (I + L) -> (T_II - I) fragments
+    // ---- prep, third part (role 0 or 2): inverses of the diagonal blocks of (I + L) ->
+    //      (T_II - I) fragments
     auto prep3 = [&](int p) {
         E* fr = FR(p);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // sLD written by other lanes
         // lane (bb, r): row r of T_bb = (I + L_bb)^-1, from T (I + L) = I read backwards:
-        // T[r][j] = [r == j] - sum_{k > j} T[r][k] L[k][j].  The block is read into registers
-        // first; each solved entry then updates all earlier columns (independent FMAs).
+        // T[r][j] = [r == j] - sum_{k > j} T[r][k] L[k][j].  Each solved entry updates all
+        // earlier columns (independent FMAs) with row k of the block.
         const int bb = lane >> 4, r = lane & 15;
         const float* lb = sLD + (16 * bb) * L::LD_P;
-        float lr[16][16];
+        // rows 15..PRE are read up front, the others when the solve gets there (registers)
+        constexpr int PRE = L::OV ? 8 : 16;
+        f32x4 lr[16][4];
 #pragma unroll
-        for (int i = 1; i < 16; ++i)
+        for (int k = PRE; k < 16; ++k)
 #pragma unroll
-            for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
-                const f32x4 x = *(const f32x4*)(lb + i * L::LD_P + 4 * k4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) lr[i][4 * k4 + e] = x[e];
-            }
+            for (int k4 = 0; k4 < (k + 3) / 4; ++k4) lr[k][k4] = *(const f32x4*)(lb + k * L::LD_P + 4 * k4);
         float acc[16], tr[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc[k] = 0.f;
@@ -351,7 +383,12 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         for (int k = 15; k >= 0; --k) {
             tr[k] = (k == r) ? 1.f : (k < r ? -acc[k] : 0.f);
 #pragma unroll
-            for (int jj = 0; jj < k; ++jj) acc[jj] += tr[k] * lr[k][jj];
+            for (int k4 = 0; k4 < (k + 3) / 4; ++k4) {
+                const f32x4 x = k >= PRE ? lr[k][k4] : *(const f32x4*)(lb + k * L::LD_P + 4 * k4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * k4 + e < k) acc[4 * k4 + e] += tr[k] * x[e];
+            }
         }
         // (T_II - I) as K16 A operand: fragment lane (r, g) holds row r, columns 4g..4g+3.
         // -T_II = -(T_II - I) - I is formed by its users (exact, T's diagonal being 1).
@@ -512,11 +549,10 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     // The prep wave and the chain waves run separate loops with the same barriers, so
     // that neither keeps the other's registers live.
     //
-    // Overlapped schedule (OV), one barrier per chunk.  Iteration q (copies of chunk q+3
-    // are issued at its start):
+    // Overlapped schedule (OV), one barrier per chunk.  Iteration q:
     //      chain waves: state update of q, then substitution of q+1
-    //      prep wave:   Gram, norms, gates, L and diagonal inverses of q+2
-    //      (wait for the copies of chunk q+3)
+    //      prep waves:  (role 1) issue the copies of chunk q+3; Gram, norms, gates, L
+    //                   and diagonal inverses of q+2; wait for the copies of chunk q+3
     //   B
     //
     // Two-phase schedule (where the OV buffers do not fit), iteration q (copies of chunk
@@ -528,62 +564,65 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
     if (prep) {
         f32x4 gr[10];  // Gram tiles of the chunk being prepared
         if constexpr (L::OV) {
-            dma_chunk(0);
-            if (nq > 1) dma_chunk(1);
-            wait_vmem();
-            if (nq > 2) dma_chunk(2);
-            lds_barrier();  // chunks 0 and 1 in LDS
-            prep1(0, gr);
-            prep2(0, gr);
-            prep3(0);
-            lds_barrier();  // chunk 0 prepared
-            if (nq > 1) {
-                prep1(1, gr);
-                prep2(1, gr);
-                prep3(1);
-            }
-            wait_vmem();
-            lds_barrier();  // chunk 1 prepared, chunk 0 substituted, chunk 2 in LDS
-            for (int q = 0; q < nq; ++q) {
-                if (q + 3 < nq) dma_chunk(q + 3);
-                if (q + 2 < nq) {
-                    prep1(q + 2, gr);
-                    prep2(q + 2, gr);
-                    prep3(q + 2);
-                }
+            auto run = [&](auto R) {
+                auto prep_all = [&](int p) {
+                    prep1(p, gr, R);
+                    prep2(p, gr, R);
+                    if (has_diag(R)) prep3(p);
+                };
+                dma_chunk(0, kAll);
+                if (nq > 1) dma_chunk(1, kAll);
                 wait_vmem();
-                lds_barrier();  // chunk q+2 prepared, q+1 substituted, q+3 in LDS
-            }
+                if (nq > 2) dma_chunk(2, kAll);
+                lds_barrier();  // chunks 0 and 1 in LDS
+                prep_all(0);
+                lds_barrier();  // chunk 0 prepared
+                if (nq > 1) prep_all(1);
+                wait_vmem();
+                lds_barrier();  // chunk 1 prepared, chunk 0 substituted, chunk 2 in LDS
+                for (int q = 0; q < nq; ++q) {
+                    // one wave issues every copy: global -> LDS copies from several waves of
+                    // a workgroup at once were measured to move far less data per second
+                    if (q + 3 < nq) dma_chunk(q + 3, kCopy);
+                    if (q + 2 < nq) prep_all(q + 2);
+                    wait_vmem();
+                    lds_barrier();  // chunk q+2 prepared, q+1 substituted, q+3 in LDS
+                }
+            };
+            if (w == ND) run(RoleC<0>{});
+            else run(RoleC<1>{});
         } else if constexpr (L::PIPE) {
-            dma_chunk(0);
-            if (nq > 1) dma_chunk(1);
+            constexpr RoleC<2> R{};
+            dma_chunk(0, kAll);
+            if (nq > 1) dma_chunk(1, kAll);
             wait_vmem();
-            for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
+            for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2, kAll);
             lds_barrier();  // chunks 0 and 1 in LDS
-            prep1(0, gr);
-            prep2(0, gr);
+            prep1(0, gr, R);
+            prep2(0, gr, R);
             prep3(0);
             lds_barrier();  // chunk 0 prepared
             for (int q = 0; q < nq; ++q) {
                 const bool more = q + 1 < nq;
-                if (q + L::PD < nq) dma_chunk(q + L::PD);
-                if (more) prep1(q + 1, gr);
+                if (q + L::PD < nq) dma_chunk(q + L::PD, kAll);
+                if (more) prep1(q + 1, gr, R);
                 lds_barrier();  // B2: W of chunk q staged by the chain waves
                 if (more) {
-                    prep2(q + 1, gr);
+                    prep2(q + 1, gr, R);
                     prep3(q + 1);
                 }
                 wait_dma_behind(q);
                 lds_barrier();  // B3: chunk q+1 prepared, chunk q+2 in LDS, chunk q's buffers free
             }
         } else {
+            constexpr RoleC<2> R{};
             for (int q = 0; q < nq; ++q) {
-                dma_chunk(q);
+                dma_chunk(q, kAll);
                 wait_vmem();
                 lds_barrier();
-                prep1(q, gr);
+                prep1(q, gr, R);
                 lds_barrier();
-                prep2(q, gr);
+                prep2(q, gr, R);
                 prep3(q);
                 lds_barrier();
                 lds_barrier();
@@ -600,40 +639,41 @@ __global__ __launch_bounds__(64 * (ND + 1), 1) void gdn_frame_affine(P1Args a) {
         }
         f32x4 Ur[4];  // U column tile w of the chunk to be applied next, pre-scaled by kts
         if constexpr (L::OV) {
-            dma_chunk(0);
-            if (nq > 1) dma_chunk(1);
+            dma_chunk(0, kAll);
+            if (nq > 1) dma_chunk(1, kAll);
             wait_vmem();
-            if (nq > 2) dma_chunk(2);
+            if (nq > 2) dma_chunk(2, kAll);
             lds_barrier();
             lds_barrier();
             subst(0, Ur);
             wait_vmem();
             lds_barrier();
+            // (no copies here: the prep waves issue them and wait for them)
             for (int q = 0; q < nq; ++q) {
-                if (q + 3 < nq) dma_chunk(q + 3);
+                if (q + 3 < nq) dma_chunk(q + 3, kCopy);
                 chain(q, XA, XB, Ur);
                 const int fl = q / nch;
                 if (q - fl * nch == nch - 1) emit(fl, XA, XB);
                 if (q + 1 < nq) subst(q + 1, Ur);
-                wait_vmem();
+                if ((kCopy >> w) & 1u) wait_vmem();
                 lds_barrier();
             }
         } else {
             if constexpr (L::PIPE) {
-                dma_chunk(0);
-                if (nq > 1) dma_chunk(1);
+                dma_chunk(0, kAll);
+                if (nq > 1) dma_chunk(1, kAll);
                 wait_vmem();
-                for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2);
+                for (int c2 = 2; c2 < L::PD && c2 < nq; ++c2) dma_chunk(c2, kAll);
                 lds_barrier();
                 lds_barrier();
             }
             for (int q = 0; q < nq; ++q) {
                 if constexpr (L::PIPE) {
-                    if (q + L::PD < nq) dma_chunk(q + L::PD);
+                    if (q + L::PD < nq) dma_chunk(q + L::PD, kAll);
                     subst(q, Ur);
                     lds_barrier();  // B2
                 } else {
-                    dma_chunk(q);
+                    dma_chunk(q, kAll);
                     wait_vmem();
                     lds_barrier();
                     lds_barrier();
@@ -932,9 +972,12 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
     using L = P1<E, ND>;
     static bool attr_done = false;  // per instantiation
     if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void*)gdn_frame_affine<E, ND>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS_B);
-        if (e != hipSuccess) return e;
+        const void* aff[4] = {(const void*)gdn_frame_affine<E, ND, 0>, (const void*)gdn_frame_affine<E, ND, 1>,
+                              (const void*)gdn_frame_affine<E, ND, 2>, (const void*)gdn_frame_affine<E, ND, 3>};
+        hipError_t e = hipSuccess;
+        for (const void* f : aff)
+            if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS_B)) != hipSuccess)
+                return e;
         e = hipFuncSetAttribute((const void*)gdn_frame_chain<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 P2<E, ND>::LDS_B);
         if (e != hipSuccess) return e;
@@ -948,7 +991,13 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
     if (phase == 0) {
         const P1Args& p1 = *(const P1Args*)args;
         const int ngw = (p1.nf + p1.G - 1) / p1.G;
-        hipLaunchKernelGGL((gdn_frame_affine<E, ND>), dim3(ngw, BH), dim3(L::NT), L::LDS_B, st, p1);
+        const dim3 grid(ngw, BH);
+        switch (p1.flags & 3u) {
+        case 0: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 0>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        case 1: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 1>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        case 2: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 2>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        default: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 3>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        }
     } else if (phase == 1) {
         constexpr int lds2 = P2<E, ND>::LDS_B;
         hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3((ND + P2<E, ND>::SPW - 1) / P2<E, ND>::SPW, BH), dim3(256),
