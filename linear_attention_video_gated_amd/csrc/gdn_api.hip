@@ -35,13 +35,13 @@ long long window_units() {
 // workgroup per (b, h, group) and one workgroup per CU (its LDS footprint), so its time
 // goes as (rounds of workgroups over the 256 CUs of an MI355X) x (frames per group);
 // the serial chain takes one step per group.  G minimises the sum of the two, with
-// about 0.066 us per token of a frame in the frame-map kernel and 3 us per chain step
+// about 0.051 us per token of a frame in the frame-map kernel and 3 us per chain step
 // (measured at d = 112).  GDN_GROUP_FRAMES overrides.  Windows hold whole groups.
 int group_frames(long long BH, int n_frames, int frame_len) {
     const long long forced = env_ll("GDN_GROUP_FRAMES");
     if (forced > 0) return (int)(forced < n_frames ? forced : n_frames);
     constexpr long long kCUs = 256;
-    const double per_frame = 0.066 * frame_len, per_step = 3.0;
+    const double per_frame = 0.051 * frame_len, per_step = 3.0;
     int best = 1;
     double best_cost = 1e300;
     for (int G = 1; G <= n_frames && G <= 64; ++G) {
