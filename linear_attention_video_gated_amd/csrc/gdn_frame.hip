@@ -64,7 +64,10 @@ template <typename E, int ND> struct P1 {
     static constexpr int KPB = ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
     static constexpr int KG = KPB / 16;           // 16-byte granules per LDS row
     static constexpr int DG = RB / 16;            // granules that hold data
-    static constexpr int W_P = G::D + 4;          // W staging pitch (elements)
+    // W staged transposed (row = a d_k column of W, 64 tokens per row); pitch again an odd
+    // count of 32-byte units, for the transposed reads of the state update
+    static constexpr int WRB = 64 * (int)sizeof(E);
+    static constexpr int WPB = (WRB / 32 % 2 == 1) ? WRB : WRB + 32;
     static constexpr int LD_P = 20;               // diagonal L blocks pitch (floats)
     static constexpr int NFR = 10;                // fragments: 6 L_IJ, 4 (T_II - I)
     static constexpr int FR_E = NFR * 64 * 4;     // elements per fragment set
@@ -72,7 +75,7 @@ template <typename E, int ND> struct P1 {
     static constexpr int RAW_B = al(2 * 64 * 4);
     static constexpr int SC_B = al((3 * 64 + 16) * 4);
     static constexpr int FR_B = al(FR_E * (int)sizeof(E));
-    static constexpr int W_B = al(64 * W_P * (int)sizeof(E));
+    static constexpr int W_B = al(G::D * WPB);
     static constexpr int LD_B = al(4 * 16 * LD_P * 4);
     static constexpr int TK_B = al(7 * 64 * 4);
     // Buffer counts.  OV (overlapped): the chain waves run the state update of chunk q
@@ -441,14 +444,18 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
             pw[I] = O::pack4(XW[I]);
             pu[I] = O::pack4(Ur[I]);
         }
+        // W^T row 16w + c, tokens 16I + 4g .. +3: one 8-byte piece per lane and block
+        E* const wt = (E*)((char*)WB_(q) + (16 * w + c) * L::WPB) + 4 * g;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const f32x4 s = *(const f32x4*)(sc + 128 + 16 * I + 4 * g);
+            f32x4 wv;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                WB_(q)[(16 * I + 4 * g + ii) * L::W_P + 16 * w + c] = O::cvt(-s[ii] * XW[I][ii]);
+                wv[ii] = -s[ii] * XW[I][ii];
                 Ur[I][ii] *= s[ii];
             }
+            O::st4(wt + 16 * I, wv);
         }
     };
 
@@ -475,14 +482,16 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
                 const int tt = 2 * h + u;
                 PA[u] = zero4();
                 PB[u] = Ur[tt];
-                const E* wr = WB_(q) + (16 * tt + c) * L::W_P + 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
+                    // lane (c, g): W[16tt + c][32kb + 4g + j] and [32kb + 16 + 4g + j], j < 4
+                    const auto w0 = O::ldtr(WB_(q), L::WPB, 32 * kb, 16 * tt, lane);
                     F8 wf;
                     if (2 * kb + 1 < ND) {
-                        wf = O::ld44(wr + 32 * kb, wr + 32 * kb + 16);
+                        wf = __builtin_shufflevector(w0, O::ldtr(WB_(q), L::WPB, 32 * kb + 16, 16 * tt, lane), 0, 1,
+                                                     2, 3, 4, 5, 6, 7);
                     } else {  // d_k columns 32kb+16.. do not exist: zero half
-                        wf = O::ld44(wr + 32 * kb, wr + 32 * kb);
+                        wf = __builtin_shufflevector(w0, w0, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                         for (int j = 4; j < 8; ++j) wf[j] = (E)0.f;
                     }
