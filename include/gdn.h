@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -88,7 +88,7 @@ enum {
     GDN_F_OUT_F32 = 1u << 3      /* out is float32 whatever dtype is (all entries)        */
 };
 
-enum { GDN_ENTRY_FORWARD = 0, GDN_ENTRY_READONLY = 1, GDN_ENTRY_BLOCK_CAUSAL = 2 };
+enum { GDN_ENTRY_FORWARD = 0, GDN_ENTRY_READONLY = 1, GDN_ENTRY_BLOCK_CAUSAL = 2, GDN_ENTRY_TOKEN = 3 };
 
 typedef struct gdn_dims {
     int32_t B, H;                 /* batch (independent rollouts) and heads              */
@@ -132,6 +132,21 @@ int gdn_frame_forward_readonly(const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta,
                                const float* state_in, void* out,
                                const gdn_dims_t* dims, void* stream);
+
+/*
+ * Gated delta rule with a per-token causal readout: the general Gated DeltaNet that the
+ * frame-wise mixer specialises ("SANA-WM ... 720p video" news summary, section "hybrid
+ * architecture for long rollouts"; update as in Gated Delta Networks).  Every token t
+ * reads the state after its own update,  o_t = S_t q_t  -- the same as gdn_frame_forward
+ * with one-token frames.  Arguments, layouts, state semantics, flags and errors are those
+ * of gdn_frame_forward; n_frames and frame_len only set how T = n_frames * frame_len
+ * tokens are cut into chunks and windows (the result does not depend on them beyond
+ * rounding).
+ */
+int gdn_token_forward(const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta,
+                      const float* state_in, float* state_out, void* out,
+                      const gdn_dims_t* dims, void* stream);
 
 /*
  * Block-causal linear attention (bidirectional inside a frame, causal across frames).

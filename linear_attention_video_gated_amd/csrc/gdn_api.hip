@@ -144,10 +144,13 @@ int set_state(const float* src, float* dst, long long n, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// entry GDN_ENTRY_FORWARD / _READONLY: frame maps, chain, frame-end readout;
+// GDN_ENTRY_TOKEN: group-end maps, chain, per-token readout pass.
 template <typename E, int ND>
 int run_gdn(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
             const float* state_in, float* state_out, void* out, const gdn_dims_t* d,
-            const Plan& p, hipStream_t st) {
+            const Plan& p, hipStream_t st, int entry) {
+    const bool tok = entry == GDN_ENTRY_TOKEN;
     char* ws = (char*)d->workspace;
     float* carry = (float*)(ws + p.off_carry);
     const int BH = (int)p.BH;
@@ -162,9 +165,13 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         // layout is that of the per-group states with one group): no chain to run
         const bool no_chain = !state_out && p.nwin == 1 && nf <= p.G;
         const float* s_before = no_chain ? state_in : sgrp;
-        const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, apack, bt};
+        const int of32 = (d->flags & GDN_F_OUT_F32) ? 1 : 0;
+        const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, apack, bt,
+                        tok ? 0 : 1, nullptr, nullptr, nullptr, 0};
+        const P1Args a3t{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, nullptr, nullptr,
+                         0, q, out, s_before, of32};
         const P2Args a2{apack, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
-        const P3Args a3{q, out, apack, bt, s_before, p.T, d->frame_len, f0, nf, p.G, (d->flags & GDN_F_OUT_F32) ? 1 : 0};
+        const P3Args a3{q, out, apack, bt, s_before, p.T, d->frame_len, f0, nf, p.G, of32};
         void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
         if (launch_gdn_phase<E, ND>(0, &a1, BH, st, ev) != hipSuccess) return GDN_ERR_HIP;
         if (no_chain) {
@@ -172,7 +179,9 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         } else if (launch_gdn_phase<E, ND>(1, &a2, BH, st, ev) != hipSuccess) {
             return GDN_ERR_HIP;
         }
-        if (launch_gdn_phase<E, ND>(2, &a3, BH, st, ev) != hipSuccess) return GDN_ERR_HIP;
+        if ((tok ? launch_gdn_phase<E, ND>(3, &a3t, BH, st, ev) : launch_gdn_phase<E, ND>(2, &a3, BH, st, ev)) !=
+            hipSuccess)
+            return GDN_ERR_HIP;
     }
     return GDN_OK;
 }
@@ -233,7 +242,7 @@ int gdn_common(const void* q, const void* k, const void* v, const float* alpha, 
     if (p.BH == 0) return GDN_OK;
     if (d->n_frames == 0) {
         if (misaligned(state_in) || misaligned(state_out)) return GDN_ERR_ALIGN;
-        return entry == GDN_ENTRY_FORWARD ? set_state(state_in, state_out, nstate, st) : GDN_OK;
+        return entry != GDN_ENTRY_READONLY ? set_state(state_in, state_out, nstate, st) : GDN_OK;
     }
     const bool additive = (d->flags & GDN_F_ADDITIVE) != 0;
     if (!q || !k || !v || !out) return GDN_ERR_NULL;
@@ -255,8 +264,8 @@ int gdn_common(const void* q, const void* k, const void* v, const float* alpha, 
     if (state_out && state_out != state_in && overlap(state_out, sbytes, state_in, sbytes)) return GDN_ERR_ALIAS;
     for (int i = 0; i < 5; ++i)
         if (overlap(state_out, sbytes, ins[i], lens[i])) return GDN_ERR_ALIAS;
-    DISPATCH(run_gdn, q, k, v, alpha, beta, state_in, entry == GDN_ENTRY_FORWARD ? state_out : nullptr,
-             out, d, p, st);
+    DISPATCH(run_gdn, q, k, v, alpha, beta, state_in, entry != GDN_ENTRY_READONLY ? state_out : nullptr,
+             out, d, p, st, entry);
 }
 
 }  // namespace
@@ -268,6 +277,12 @@ GDN_API int gdn_frame_forward(const void* q, const void* k, const void* v, const
                               const float* beta, const float* state_in, float* state_out, void* out,
                               const gdn_dims_t* dims, void* stream) {
     return gdn_common(q, k, v, alpha, beta, state_in, state_out, out, dims, stream, GDN_ENTRY_FORWARD);
+}
+
+GDN_API int gdn_token_forward(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* state_in, float* state_out, void* out,
+                              const gdn_dims_t* dims, void* stream) {
+    return gdn_common(q, k, v, alpha, beta, state_in, state_out, out, dims, stream, GDN_ENTRY_TOKEN);
 }
 
 GDN_API int gdn_frame_forward_readonly(const void* q, const void* k, const void* v, const float* alpha,
@@ -314,14 +329,17 @@ GDN_API int linear_attn_block_causal(const void* q, const void* k, const void* v
 }
 
 GDN_API size_t gdn_workspace_bytes(const gdn_dims_t* dims, int entry) {
-    if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_BLOCK_CAUSAL) return 0;
+    if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_BLOCK_CAUSAL &&
+        entry != GDN_ENTRY_TOKEN)
+        return 0;
     Plan p;
     if (check_dims(dims, entry, &p) != GDN_OK) return 0;
     return p.total;
 }
 
 GDN_API int gdn_window_count(const gdn_dims_t* dims, int entry) {
-    if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_BLOCK_CAUSAL)
+    if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_BLOCK_CAUSAL &&
+        entry != GDN_ENTRY_TOKEN)
         return GDN_ERR_UNSUPPORTED;
     Plan p;
     const int rc = check_dims(dims, entry, &p);

@@ -54,28 +54,37 @@ template <int V> struct RoleC {
     static constexpr int value = V;
 };
 
-template <typename E, int ND> struct P1 {
+// TOK: the per-token readout pass (see gdn_token_readout below); otherwise the frame maps.
+template <typename E, int ND, bool TOK = false> struct P1 {
     using G = Geo<E, ND>;
-    static constexpr bool PIPE = sizeof(E) == 2;
+    static constexpr bool BF = sizeof(E) == 2;
     static constexpr int al(int b) { return (b + 255) / 256 * 256; }
-    static constexpr int RB = G::D * (int)sizeof(E);  // bytes of one K or V row
-    // LDS row pitch: a multiple of 32 bytes with an odd count of 32-byte units, so that the
-    // transposed reads (8 consecutive rows x 32 bytes per half-wave) hit distinct banks
-    static constexpr int KPB = ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
+    static constexpr int RB = G::D * (int)sizeof(E);  // bytes of one K, V or Q row
+    // LDS row pitch of bf16 tiles: a multiple of 32 bytes with an odd count of 32-byte
+    // units, so that the transposed reads (8 consecutive rows x 32 bytes per half-wave) hit
+    // distinct banks.  fp32 tiles are read with plain loads and keep their length.
+    static constexpr int pitch(int rb) {
+        return !BF ? rb : ((rb + 31) / 32 % 2 == 1) ? (rb + 31) / 32 * 32 : (rb + 31) / 32 * 32 + 32;
+    }
+    static constexpr int KPB = pitch(RB);
     static constexpr int KG = KPB / 16;           // 16-byte granules per LDS row
     static constexpr int DG = RB / 16;            // granules that hold data
-    // W staged transposed (row = a d_k column of W, 64 tokens per row); pitch again an odd
-    // count of 32-byte units, for the transposed reads of the state update
+    // W staged transposed (row = a d_k column of W, 64 tokens per row)
     static constexpr int WRB = 64 * (int)sizeof(E);
-    static constexpr int WPB = (WRB / 32 % 2 == 1) ? WRB : WRB + 32;
+    static constexpr int WPB = pitch(WRB);
     static constexpr int LD_P = 20;               // diagonal L blocks pitch (floats)
     static constexpr int NFR = 10;                // fragments: 6 L_IJ, 4 (T_II - I)
     static constexpr int FR_E = NFR * 64 * 4;     // elements per fragment set
     static constexpr int KV_B = al(64 * KPB);
     static constexpr int RAW_B = al(2 * 64 * 4);
-    static constexpr int SC_B = al((3 * 64 + 16) * 4);
+    // per-token scalars: [0,64) b e^G n, [64,128) b, [128,192) e^{G_C - G} n, [192] gamma_C;
+    // TOK adds [208,272) G (log2, inclusive), [272,336) n, [336,400) e^G
+    static constexpr int SC_N = TOK ? 400 : 208;
+    static constexpr int SC_B = al(SC_N * 4);
     static constexpr int FR_B = al(FR_E * (int)sizeof(E));
     static constexpr int W_B = al(G::D * WPB);
+    // TOK: the 10 lower-triangle 16x16 tiles of the decay-masked (K Q^T), hi (+ lo) fragments
+    static constexpr int AQ_B = TOK ? al(10 * SplitCount<E>::N * 64 * 4 * (int)sizeof(E)) : 0;
     static constexpr int LD_B = al(4 * 16 * LD_P * 4);
     static constexpr int TK_B = al(7 * 64 * 4);
     // Buffer counts.  OV (overlapped): the chain waves run the state update of chunk q
@@ -85,23 +94,32 @@ template <typename E, int ND> struct P1 {
     static constexpr int ov_bytes() {
         return 4 * KV_B + 3 * KV_B + 3 * RAW_B + 3 * SC_B + 2 * FR_B + 2 * W_B + LD_B + 2 * TK_B;
     }
-    static constexpr bool OV = PIPE && ov_bytes() <= 160 * 1024;
+    // TOK, two barriers per chunk: K and gates for chunks q..q+2, V and Q for q..q+1
+    static constexpr int tok_bytes() {
+        return 3 * KV_B + 4 * KV_B + 3 * RAW_B + 2 * SC_B + 2 * FR_B + W_B + AQ_B + LD_B + TK_B;
+    }
+    static constexpr bool OV = !TOK && BF && ov_bytes() <= 160 * 1024;
+    static constexpr bool PIPE = BF && (!TOK || tok_bytes() <= 160 * 1024);
     static constexpr int NPW = OV ? 2 : 1;        // prep waves
     static constexpr int NW = ND + NPW;           // chain waves + prep waves
     static constexpr int NT = 64 * NW;
     static constexpr int NB = PIPE ? 2 : 1;       // fragment sets
-    static constexpr int NBK = OV ? 4 : (!PIPE ? 1 : 3);   // K chunk buffers
-    static constexpr int NBV = OV ? 3 : NBK;      // V chunk and gate buffers
+    static constexpr int NBK = OV ? 4 : (!PIPE ? 1 : 3);                 // K chunk buffers
+    static constexpr int NBV = OV ? 3 : (TOK ? (PIPE ? 2 : 1) : NBK);    // V chunk buffers
+    static constexpr int NBQ = TOK ? (PIPE ? 2 : 1) : 0;                 // Q chunk buffers
+    static constexpr int NBR = OV ? 3 : NBK;      // gate buffers
     static constexpr int NBS = OV ? 3 : NB;       // per-token scalar sets
     static constexpr int NBW = OV ? 2 : 1;        // W staging buffers
-    static constexpr int PD = PIPE ? (OV ? 3 : NBK - 1) : 0;  // chunks the copies run ahead
+    static constexpr int PD = PIPE ? (OV ? 3 : NBK - 1) : 0;  // chunks the K copies run ahead
     static constexpr int OFF_K = 0;                        // [NBK] row-major K chunk
     static constexpr int OFF_V = OFF_K + NBK * KV_B;       // [NBV] row-major V chunk
-    static constexpr int OFF_RAW = OFF_V + NBV * KV_B;     // [NBV] alpha[64], beta[64]
-    static constexpr int OFF_SC = OFF_RAW + NBV * RAW_B;   // [NBS] per-token scales + gamma
+    static constexpr int OFF_Q = OFF_V + NBV * KV_B;       // [NBQ] row-major Q chunk (TOK)
+    static constexpr int OFF_RAW = OFF_Q + NBQ * KV_B;     // [NBR] alpha[64], beta[64]
+    static constexpr int OFF_SC = OFF_RAW + NBR * RAW_B;   // [NBS] per-token scalars
     static constexpr int OFF_FR = OFF_SC + NBS * SC_B;     // [NB] substitution fragments
     static constexpr int OFF_W = OFF_FR + NB * FR_B;       // [NBW] W staging (chain waves)
-    static constexpr int OFF_LD = OFF_W + NBW * W_B;       // diagonal blocks of L (prep wave)
+    static constexpr int OFF_AQ = OFF_W + NBW * W_B;       // masked (K Q^T) fragments (TOK)
+    static constexpr int OFF_LD = OFF_AQ + AQ_B;           // diagonal blocks of L (prep wave)
     static constexpr int OFF_TK = OFF_LD + LD_B;           // [NPW] per-token scalars (prep waves)
     static constexpr int LDS_B = OFF_TK + NPW * TK_B;
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
@@ -116,9 +134,9 @@ __host__ __device__ constexpr int frTm(int I) { return 6 + I; }
 
 // MODE = the call's GDN_F_NORMALIZE_K (bit 0) and GDN_F_ADDITIVE (bit 1) flags, fixed at
 // compile time so that the per-tile choices they make are not branches.
-template <typename E, int ND, int MODE>
-__global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a) {
-    using L = P1<E, ND>;
+template <typename E, int ND, int MODE, bool TOK = false>
+__global__ __launch_bounds__((P1<E, ND, TOK>::NT), 1) void gdn_frame_affine(P1Args a) {
+    using L = P1<E, ND, TOK>;
     using O = Ops<E>;
     using F8 = typename O::F8;
     using F4 = typename O::F4;
@@ -133,7 +151,9 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
     constexpr int BM = L::NB - 1;
     auto KB_ = [&](int p) { return (E*)(smem + L::OFF_K + (p % L::NBK) * L::KV_B); };
     auto VB_ = [&](int p) { return (E*)(smem + L::OFF_V + (p % L::NBV) * L::KV_B); };
-    auto RAW = [&](int p) { return (float*)(smem + L::OFF_RAW + (p % L::NBV) * L::RAW_B); };
+    auto RAW = [&](int p) { return (float*)(smem + L::OFF_RAW + (p % L::NBR) * L::RAW_B); };
+    constexpr int NBQ1 = L::NBQ ? L::NBQ : 1;
+    auto QB_ = [&](int p) { return (E*)(smem + L::OFF_Q + (p % NBQ1) * L::KV_B); };
     auto SC = [&](int p) { return (float*)((unsigned char*)sSC0 + (p % L::NBS) * L::SC_B); };
     auto FR = [&](int p) { return (E*)((unsigned char*)sFR0 + (p & BM) * L::FR_B); };
     auto WB_ = [&](int p) { return (E*)(smem + L::OFF_W + (p % L::NBW) * L::W_B); };
@@ -149,6 +169,7 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
     const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw0) * N;
     const E* kp = (const E*)a.k + tok0 * D;
     const E* vp = (const E*)a.v + tok0 * D;
+    const E* qp = TOK ? (const E*)a.q + tok0 * D : nullptr;
     constexpr bool additive = (MODE & 2) != 0;
     constexpr bool normalize = (MODE & 1) != 0;
     const int nch = (N + 63) / 64;
@@ -162,24 +183,36 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
     //      padding granules copy a valid in-bounds granule instead (their values are
     //      finite and multiplied by zero scale factors, never used as data).
     // copy instructions dealt round-robin to the waves whose bits are set in `mask`
-    auto dma_chunk = [&](int p, unsigned mask) {
+    // Copies of chunk p for the tiles tf .. tf+nt-1 of (K, V, Q) and, with `gates`, of
+    // alpha and beta; the copy instructions are dealt round-robin to the waves whose bits
+    // are set in `mask`.
+    auto dma_tiles = [&](int p, int tf, int nt, bool gates, unsigned mask) {
         if (!((mask >> w) & 1u)) return;
         const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
         const long long t0 = chunk_t0(p);
         const int Cc = chunk_len(p);
-        for (int i = wi; i < 2 * L::KG; i += nw) {
-            const bool isk = i < L::KG;
-            const int ii = isk ? i : i - L::KG;
-            const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
-            const long long el = (t0 + min(row, Cc - 1)) * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
-            const int dst = isk ? L::OFF_K + (p % L::NBK) * L::KV_B + ii * 1024
-                                : L::OFF_V + (p % L::NBV) * L::KV_B + ii * 1024;
-            if constexpr (L::PIPE) dma16((isk ? kp : vp) + el, smem + dst);
-            else *(u32x4*)(smem + dst + 16 * lane) = *(const u32x4*)((isk ? kp : vp) + el);  // same copy, synchronous
+        // instructions i = wi, wi + nw, ... over the tiles' KG instructions each
+        auto copy_tile = [&](const E* src, int dst0, int lo, int i0, int i1) {
+            for (int i = i0; i < i1; i += nw) {
+                const int ii = i - lo;
+                const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
+                const long long el = (t0 + min(row, Cc - 1)) * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
+                const int dst = dst0 + ii * 1024;
+                if constexpr (L::PIPE) dma16(src + el, smem + dst);
+                else *(u32x4*)(smem + dst + 16 * lane) = *(const u32x4*)(src + el);  // same copy, synchronous
+            }
+        };
+        for (int t = 0; t < nt; ++t) {
+            const int lo = t * L::KG, hi = lo + L::KG;
+            const int i0 = lo + ((wi - lo) % nw + nw) % nw;  // first of this wave's instructions in the tile
+            const int ts = tf + t;
+            if (ts == 0) copy_tile(kp, L::OFF_K + (p % L::NBK) * L::KV_B, lo, i0, hi);
+            else if (ts == 1) copy_tile(vp, L::OFF_V + (p % L::NBV) * L::KV_B, lo, i0, hi);
+            else copy_tile(qp, L::OFF_Q + (p % NBQ1) * L::KV_B, lo, i0, hi);
         }
-        if (!additive && wi == (2 * L::KG) % nw) {
+        if (gates && !additive && wi == (nt * L::KG) % nw) {
             const long long tt = tok0 + t0 + min(lane, Cc - 1);
-            const int dst = L::OFF_RAW + (p % L::NBV) * L::RAW_B;
+            const int dst = L::OFF_RAW + (p % L::NBR) * L::RAW_B;
             if constexpr (L::PIPE) {
                 dma4(a.alpha + tt, smem + dst);
                 dma4(a.beta + tt, smem + dst + 256);
@@ -189,6 +222,7 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
             }
         }
     };
+    auto dma_chunk = [&](int p, unsigned mask) { dma_tiles(p, 0, 2, true, mask); };
 
     // At the end of iteration q chunk q+2 must have landed (the prep wave reads it next)
     // while the copies of chunks q+3 .. q+PD may still be in flight: wait until at most
@@ -301,6 +335,11 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
             sc[64 + t] = be;
             sc[128 + t] = hw_exp2(GC - Gs) * nrm;
             if (t == 0) sc[192] = hw_exp2(GC);
+            if constexpr (TOK) {
+                sc[208 + t] = Gs;
+                sc[272 + t] = nrm;
+                sc[336 + t] = hw_exp2(Gs);
+            }
         }
         // decay factors of L split at the end of 16-token block J (both factors <= 1):
         // e^{G_i - G_j} = e^{G_i - G_end(J)} e^{G_end(J) - G_j} for i in a later block
@@ -448,14 +487,155 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
         E* const wt = (E*)((char*)WB_(q) + (16 * w + c) * L::WPB) + 4 * g;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const f32x4 s = *(const f32x4*)(sc + 128 + 16 * I + 4 * g);
             f32x4 wv;
+            if constexpr (TOK) {  // unscaled: the readout needs v' = U - W S0^T itself
+                wv = -XW[I];
+            } else {
+                const f32x4 s = *(const f32x4*)(sc + 128 + 16 * I + 4 * g);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                wv[ii] = -s[ii] * XW[I][ii];
-                Ur[I][ii] *= s[ii];
+                for (int ii = 0; ii < 4; ++ii) {
+                    wv[ii] = -s[ii] * XW[I][ii];
+                    Ur[I][ii] *= s[ii];
+                }
             }
             O::st4(wt + 16 * I, wv);
+        }
+    };
+
+    // Operand fragment of the row-major chunk tile `buf` (K or Q, pitch KPB): lane (c, g)
+    // gets row r0 + c, columns 32kb + 4g + j and 32kb + 16 + 4g + j (j < 4); columns past
+    // d_k are zero (the PAIR slot map of the K32 products).
+    auto rowfrag = [&](const E* buf, int r0, int kb) {
+        const E* r = (const E*)((const char*)buf + (r0 + c) * L::KPB) + 32 * kb + 4 * g;
+        F8 f;
+        if (2 * kb + 1 < ND) {
+            f = O::ld44(r, r + 16);
+        } else {
+            f = O::ld44(r, r);
+#pragma unroll
+            for (int j = 4; j < 8; ++j) f[j] = (E)0.f;
+        }
+        return f;
+    };
+
+    // ---- TOK, chain waves, beside the substitution: the ten lower-triangle tiles (tile T
+    //      of query tokens, tile J of key tokens, J <= T) of the intra-chunk weights
+    //          Aqk[t][i] = e^{G_t - G_i} n_i (q_t . k_i)   (i <= t, else 0),
+    //      computed as (K Q^T) so that lane (c, g) holds Aqk[16T + c][16J + 4g + i]: the B
+    //      operand of the readout's K16 product over key tokens.  Decay factors as in L:
+    //      one exp2 of a difference inside a block, split at the key block's end across
+    //      blocks (both factors <= 1).
+    auto aqk = [&](int q) {
+        const float* sc = SC(q);
+        E* const aq = (E*)(smem + L::OFF_AQ);
+        for (int x = w; x < 10; x += ND) {
+            const int T = x < 1 ? 0 : x < 3 ? 1 : x < 6 ? 2 : 3;
+            const int J = x - T * (T + 1) / 2;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) acc = O::mma32(rowfrag(KB_(q), 16 * J, kb), rowfrag(QB_(q), 16 * T, kb), acc);
+            const float gt = sc[208 + 16 * T + c];
+            const f32x4 gi4 = *(const f32x4*)(sc + 208 + 16 * J + 4 * g);
+            const f32x4 ni4 = *(const f32x4*)(sc + 272 + 16 * J + 4 * g);
+            if (T == J) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i <= c) ? acc[i] * ni4[i] * hw_exp2(gt - gi4[i]) : 0.f;
+            } else {
+                const float ge = sc[208 + 16 * J + 15];
+                const float rowf = hw_exp2(gt - ge);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] *= rowf * ni4[i] * hw_exp2(ge - gi4[i]);
+            }
+            F4 hi, lo;
+            O::split4(acc, hi, lo);
+            *(F4*)(aq + ((x * NS) * 64 + lane) * 4) = hi;
+            if constexpr (NS > 1) *(F4*)(aq + ((x * NS + 1) * 64 + lane) * 4) = lo;
+        }
+    };
+
+    // ---- TOK, chain waves: chunk q from its true start state S0 (slice XB), B part only.
+    //      v' = U - W S0^T (fp32), the state update with D' = diag(e^{G_C - G} n) v', and the
+    //      outputs of the chunk's tokens for this wave's 16 state rows, as O^T tiles:
+    //          O^T[r][t] = e^{G_t} (S0 q_t)[r] + sum_{i <= t} v'[i][r] Aqk[t][i]
+    //      (lane (c, g) of tile T: token 16T + c, rows 16w + 4g .. +3 -- 4 consecutive
+    //      outputs).  S0, v' and Aqk go to the matrix cores as hi + lo pairs.
+    auto chain_tok = [&](int q, f32x4 (&XB)[ND], const f32x4 (&Ur)[4]) {
+        const float* sc = SC(q);
+        const E* kbuf = KB_(q);
+        const float gam = sc[192];
+        F8 xh[KB], xl[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            O::split8(XB[2 * kb], (2 * kb + 1 < ND) ? XB[(2 * kb + 1) % ND] : zero4(), xh[kb], xl[kb]);
+        F4 vh[4], vl[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4 PB[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tt = 2 * h + u;
+                PB[u] = Ur[tt];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const auto w0 = O::ldtr(WB_(q), L::WPB, 32 * kb, 16 * tt, lane);
+                    F8 wf;
+                    if (2 * kb + 1 < ND) {
+                        wf = __builtin_shufflevector(w0, O::ldtr(WB_(q), L::WPB, 32 * kb + 16, 16 * tt, lane), 0, 1,
+                                                     2, 3, 4, 5, 6, 7);
+                    } else {
+                        wf = __builtin_shufflevector(w0, w0, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int j = 4; j < 8; ++j) wf[j] = (E)0.f;
+                    }
+                    PB[u] = O::mma32(wf, xh[kb], PB[u]);
+                }
+                O::split4(PB[u], vh[tt], vl[tt]);  // v' tile tt (rows 16w.., tokens 16tt..)
+                const f32x4 s = *(const f32x4*)(sc + 128 + 16 * tt + 4 * g);
+                PB[u] *= s;
+            }
+            F8 dBh, dBl;
+            O::split8(PB[0], PB[1], dBh, dBl);
+#pragma unroll
+            for (int m = 0; m < ND; ++m) {
+                const F8 kf = __builtin_shufflevector(O::ldtr(kbuf, L::KPB, 32 * h, 16 * m, lane),
+                                                      O::ldtr(kbuf, L::KPB, 32 * h + 16, 16 * m, lane), 0, 1, 2, 3,
+                                                      4, 5, 6, 7);
+                f32x4 xb2 = h == 0 ? XB[m] * gam : XB[m];
+                xb2 = O::mma32(kf, dBh, xb2);
+                if (O::kSplit) xb2 = O::mma32(kf, dBl, xb2);
+                XB[m] = xb2;
+            }
+        }
+        // outputs
+        const E* const aq = (const E*)(smem + L::OFF_AQ);
+        const int Cc = chunk_len(q);
+        const long long trow = tok0 + chunk_t0(q);
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            f32x4 o = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const F8 qf = rowfrag(QB_(q), 16 * T, kb);
+                o = O::mma32(xh[kb], qf, o);
+                if (O::kSplit) o = O::mma32(xl[kb], qf, o);
+            }
+            o *= sc[336 + 16 * T + c];
+#pragma unroll
+            for (int J = 0; J <= T; ++J) {
+                const int x = T * (T + 1) / 2 + J;
+                const F4 ah = *(const F4*)(aq + ((x * NS) * 64 + lane) * 4);
+                o = O::mma16(vh[J], ah, o);
+                if constexpr (NS > 1) {
+                    const F4 al = *(const F4*)(aq + ((x * NS + 1) * 64 + lane) * 4);
+                    o = O::mma16(vl[J], ah, o);
+                    o = O::mma16(vh[J], al, o);
+                }
+            }
+            if (16 * T + c < Cc) {
+                const long long off = (trow + 16 * T + c) * D + 16 * w + 4 * g;
+                if (a.out_f32) *(f32x4*)((float*)a.out + off) = o;
+                else O::st4((E*)a.out + off, o);
+            }
         }
     };
 
@@ -572,7 +752,47 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
     //   B3
     if (prep) {
         f32x4 gr[10];  // Gram tiles of the chunk being prepared
-        if constexpr (L::OV) {
+        if constexpr (TOK && L::PIPE) {
+            // K and gates run two chunks ahead, V and Q one
+            constexpr RoleC<2> R{};
+            dma_tiles(0, 0, 1, true, kAll);
+            dma_tiles(0, 1, 2, false, kAll);
+            if (nq > 1) dma_tiles(1, 0, 1, true, kAll);
+            wait_vmem();
+            lds_barrier();  // chunk 0 and chunk 1's K in LDS
+            prep1(0, gr, R);
+            prep2(0, gr, R);
+            prep3(0);
+            lds_barrier();  // chunk 0 prepared
+            for (int q = 0; q < nq; ++q) {
+                if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kAll);
+                if (q + 1 < nq) {
+                    dma_tiles(q + 1, 1, 2, false, kAll);
+                    prep1(q + 1, gr, R);
+                }
+                lds_barrier();  // B2: W and the intra-chunk weights of chunk q staged
+                if (q + 1 < nq) {
+                    prep2(q + 1, gr, R);
+                    prep3(q + 1);
+                }
+                wait_vmem();
+                lds_barrier();  // B3: chunk q+1 prepared and in LDS, chunk q+2's K in LDS
+            }
+        } else if constexpr (TOK) {
+            constexpr RoleC<2> R{};
+            for (int q = 0; q < nq; ++q) {
+                dma_tiles(q, 0, 3, true, kAll);
+                wait_vmem();
+                lds_barrier();
+                prep1(q, gr, R);
+                lds_barrier();
+                prep2(q, gr, R);
+                prep3(q);
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
+            }
+        } else if constexpr (L::OV) {
             auto run = [&](auto R) {
                 auto prep_all = [&](int p) {
                     prep1(p, gr, R);
@@ -647,7 +867,45 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
             XB[t] = zero4();
         }
         f32x4 Ur[4];  // U column tile w of the chunk to be applied next, pre-scaled by kts
-        if constexpr (L::OV) {
+        if constexpr (TOK) {
+            // the true state at the group start: S_before rows 16w.. (zero when NULL)
+            const int ngw = (a.nf + a.G - 1) / a.G;
+            const float* sg = a.Sgrp ? a.Sgrp + ((long long)bh * ngw + gi) * D * D + (long long)(16 * w + c) * D
+                                     : nullptr;
+#pragma unroll
+            for (int t = 0; t < ND; ++t) XB[t] = sg ? *(const f32x4*)(sg + 16 * t + 4 * g) : zero4();
+            if constexpr (L::PIPE) {
+                dma_tiles(0, 0, 1, true, kAll);
+                dma_tiles(0, 1, 2, false, kAll);
+                if (nq > 1) dma_tiles(1, 0, 1, true, kAll);
+                wait_vmem();
+                lds_barrier();
+                lds_barrier();
+                for (int q = 0; q < nq; ++q) {
+                    if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kAll);
+                    if (q + 1 < nq) dma_tiles(q + 1, 1, 2, false, kAll);
+                    subst(q, Ur);
+                    aqk(q);
+                    lds_barrier();  // B2
+                    chain_tok(q, XB, Ur);
+                    wait_vmem();
+                    lds_barrier();  // B3
+                }
+            } else {
+                for (int q = 0; q < nq; ++q) {
+                    dma_tiles(q, 0, 3, true, kAll);
+                    wait_vmem();
+                    lds_barrier();
+                    lds_barrier();
+                    lds_barrier();
+                    subst(q, Ur);
+                    aqk(q);
+                    lds_barrier();
+                    chain_tok(q, XB, Ur);
+                    lds_barrier();
+                }
+            }
+        } else if constexpr (L::OV) {
             dma_chunk(0, kAll);
             if (nq > 1) dma_chunk(1, kAll);
             wait_vmem();
@@ -662,7 +920,7 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
                 if (q + 3 < nq) dma_chunk(q + 3, kCopy);
                 chain(q, XA, XB, Ur);
                 const int fl = q / nch;
-                if (q - fl * nch == nch - 1) emit(fl, XA, XB);
+                if (q - fl * nch == nch - 1 && (a.emit_all || fl == nfg - 1)) emit(fl, XA, XB);
                 if (q + 1 < nq) subst(q + 1, Ur);
                 if ((kCopy >> w) & 1u) wait_vmem();
                 lds_barrier();
@@ -692,7 +950,7 @@ __global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a)
                 }
                 chain(q, XA, XB, Ur);
                 const int fl = q / nch;
-                if (q - fl * nch == nch - 1) emit(fl, XA, XB);
+                if (q - fl * nch == nch - 1 && (a.emit_all || fl == nfg - 1)) emit(fl, XA, XB);
                 if constexpr (L::PIPE) wait_dma_behind(q);
                 lds_barrier();  // B3
             }
@@ -979,13 +1237,19 @@ template <typename E, int ND> struct P3 {
 template <typename E, int ND>
 hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev) {
     using L = P1<E, ND>;
+    using LT = P1<E, ND, true>;
     static bool attr_done = false;  // per instantiation
     if (!attr_done) {
         const void* aff[4] = {(const void*)gdn_frame_affine<E, ND, 0>, (const void*)gdn_frame_affine<E, ND, 1>,
                               (const void*)gdn_frame_affine<E, ND, 2>, (const void*)gdn_frame_affine<E, ND, 3>};
+        const void* tok[4] = {(const void*)gdn_frame_affine<E, ND, 0, true>, (const void*)gdn_frame_affine<E, ND, 1, true>,
+                              (const void*)gdn_frame_affine<E, ND, 2, true>, (const void*)gdn_frame_affine<E, ND, 3, true>};
         hipError_t e = hipSuccess;
         for (const void* f : aff)
             if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS_B)) != hipSuccess)
+                return e;
+        for (const void* f : tok)
+            if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, LT::LDS_B)) != hipSuccess)
                 return e;
         e = hipFuncSetAttribute((const void*)gdn_frame_chain<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 P2<E, ND>::LDS_B);
@@ -995,9 +1259,19 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    hipError_t e = record(ev, 2 * phase, st);
+    const int slot = phase == 3 ? 2 : phase;  // the per-token readout is a window's third launch
+    hipError_t e = record(ev, 2 * slot, st);
     if (e != hipSuccess) return e;
-    if (phase == 0) {
+    if (phase == 3) {
+        const P1Args& p1 = *(const P1Args*)args;
+        const dim3 grid((p1.nf + p1.G - 1) / p1.G, BH);
+        switch (p1.flags & 3u) {
+        case 0: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 0, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        case 1: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 1, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        case 2: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 2, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        default: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 3, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        }
+    } else if (phase == 0) {
         const P1Args& p1 = *(const P1Args*)args;
         const int ngw = (p1.nf + p1.G - 1) / p1.G;
         const dim3 grid(ngw, BH);
@@ -1017,7 +1291,7 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
         hipLaunchKernelGGL((gdn_frame_readout<E, ND>), dim3(p3.nf, BH), dim3(256), lds3, st, p3);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return record(ev, 2 * phase + 1, st);
+    return record(ev, 2 * slot + 1, st);
 }
 
 #define GDN_INST(E, ND) template hipError_t launch_gdn_phase<E, ND>(int, const void*, int, hipStream_t, void* const*);

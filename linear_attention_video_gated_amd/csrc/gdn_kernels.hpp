@@ -29,6 +29,12 @@ struct P1Args {
     unsigned flags;     // bit 0: normalise k, bit 1: additive
     void* Apack;        // partial maps A of every frame of the window
     float* Bt;          // partial maps B
+    int emit_all;       // maps at every frame end (else only at each group's last frame)
+    // per-token readout pass only:
+    const void* q;
+    void* out;
+    const float* Sgrp;  // state before each group of the window [BH, groups, d, d], or NULL
+    int out_f32;
 };
 
 struct P2Args {
@@ -93,7 +99,8 @@ struct BC3Args {
 
 // Launchers.  ev: NULL, or the 6 events of one window -- recorded before and after each
 // of the window's three launches, on the stream that launch goes to.
-// phase 0: frame maps (P1Args), 1: chain over groups (P2Args), 2: readout (P3Args).
+// phase 0: frame maps (P1Args), 1: chain over groups (P2Args), 2: readout (P3Args),
+// 3: per-token readout (P1Args; recorded in the third launch's event slots).
 template <typename E, int ND>
 hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev);
 template <typename E, int ND>

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libgdn_mi355x.so")
 
 GDN_BF16, GDN_F32 = 0, 1
 NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32 = 1, 2, 4, 8
-ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL = 0, 1, 2
-EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "linear_attn_block_causal",
+ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
+EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
            "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
 
 
@@ -55,6 +55,8 @@ def lib():
         dp = ctypes.POINTER(Dims)
         L.gdn_frame_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
         L.gdn_frame_forward.restype = ctypes.c_int
+        L.gdn_token_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
+        L.gdn_token_forward.restype = ctypes.c_int
         L.gdn_frame_forward_readonly.argtypes = [vp, vp, vp, fp, fp, fp, vp, dp, vp]
         L.gdn_frame_forward_readonly.restype = ctypes.c_int
         L.linear_attn_block_causal.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
@@ -170,7 +172,7 @@ def _f32(t, shape, name):
 
 def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
                   out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
-                  events=None):
+                  events=None, _entry=ENTRY_FORWARD):
     """gdn_frame_forward.  Returns (out [B,H,T,d], state_out [B,H,d,d] float32 or None).
     out_dtype=torch.float32 (or a float32 ``out``) returns the unrounded float32 result."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
@@ -183,12 +185,23 @@ def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, stat
     state_out = _f32(state_out, (B, H, d, d), "state_out")
     code = _dtype_code(q.dtype)
     need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
-                                     ENTRY_FORWARD)
+                                     _entry)
     ws = _workspace(q.device, need)
     dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
-    _check(lib().gdn_frame_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
-                                   _ptr(state_out), _ptr(out), ctypes.byref(dims), _stream(q.device, stream)))
+    fn = lib().gdn_token_forward if _entry == ENTRY_TOKEN else lib().gdn_frame_forward
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+              ctypes.byref(dims), _stream(q.device, stream)))
     return out, state_out
+
+
+def token_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
+                  out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
+                  events=None):
+    """gdn_token_forward: every token reads the state after itself (o_t = S_t q_t).
+    Same arguments and returns as frame_forward."""
+    return frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=state_in, state_out=state_out,
+                         out=out, flags=flags, return_state=return_state, stream=stream, out_dtype=out_dtype,
+                         events=events, _entry=ENTRY_TOKEN)
 
 
 def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, out=None,

@@ -74,3 +74,31 @@ def gdn_chunked(q, k, v, alpha, beta, n_frames, frame_len, chunk=64, state_in=No
             S = S @ A + Bm
         out[t0:t0 + frame_len] = q[t0:t0 + frame_len].astype(np.float64) @ S.T
     return out, S
+
+
+def gdn_chunked_tokens(q, k, v, alpha, beta, chunk=64, state_in=None, normalize=True, additive=False):
+    """Per-token causal readout o_t = S_t q_t (S_t the state after token t) in chunk form,
+    for ONE head (float64).  Inside a chunk with start state S0 the prefix of the chunk is
+    itself a chunk whose factors are the prefix rows of U and W (T is lower triangular), so
+        S_t = exp(G_t) S0 + sum_{i<=t} exp(G_t - G_i) v'_i k^_i^T,   v'_i = U_i - W_i S0^T
+    and  O = diag(exp(G)) Q S0^T + (M * (Q K^^T)) V',  M_ti = exp(G_t - G_i) for i <= t.
+    Returns (out [T, d_v], final state)."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    kh = _norm_keys(k.astype(np.float64), normalize)
+    S = np.zeros((dv, dk)) if state_in is None else state_in.astype(np.float64).copy()
+    out = np.zeros((T, dv))
+    for c0 in range(0, T, chunk):
+        c1 = min(c0 + chunk, T)
+        C = c1 - c0
+        g, W, U, Kt = chunk_factors(kh[c0:c1], v[c0:c1].astype(np.float64),
+                                    None if additive else alpha[c0:c1].astype(np.float64),
+                                    None if additive else beta[c0:c1].astype(np.float64), additive)
+        G = np.zeros(C) if additive else np.cumsum(np.log(np.maximum(alpha[c0:c1].astype(np.float64),
+                                                                      np.finfo(np.float32).tiny)))
+        Vp = U - W @ S.T
+        M = np.tril(np.exp(G[:, None] - G[None, :]))
+        qc = q[c0:c1].astype(np.float64)
+        out[c0:c1] = np.exp(G)[:, None] * (qc @ S.T) + (M * (qc @ kh[c0:c1].T)) @ Vp
+        S = g * S + Vp.T @ Kt
+    return out, S

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 2
+    assert gdn.lib().gdn_abi_version() == 3
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"

@@ -1,0 +1,143 @@
+"""GPU parity of the per-token causal readout (gdn_token_forward: o_t = S_t q_t, S_t the
+state after token t) against the CPU oracle run with one-token frames, element by element
+on the same seeded inputs.  Tolerances as in test_gpu_parity: max |err| <= 2e-2 RMS (bf16
+inputs) or 1e-4 RMS (float32 inputs), the computed result compared in float32 and the
+bf16 output checked to be the round-to-nearest-even of it.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_video_gated_amd import gdn
+from linear_attention_video_gated_amd.inputs import gdn_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check(name, got, ref, tol):
+    got = got.detach().to("cpu", torch.float64).numpy()
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert np.all(np.isfinite(got)), name + ": non-finite values"
+    assert err <= tol * rms + 1e-30, "%s: max|err| %.3e > %.1e * RMS %.3e (ratio %.3e)" % (
+        name, err, tol, rms, err / max(rms, 1e-300))
+    return err / max(rms, 1e-300)
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+
+
+def oracle_tokens(inp, T, flags=oracle.NORMALIZE_K):
+    """Per-token readout from the oracle: T frames of one token."""
+    return oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], T, 1,
+                              state_in=inp["state_in"], flags=flags)
+
+
+def run_token_case(B, H, F, N, d, dtype, seed, gates="config", state_std=None, flags=gdn.NORMALIZE_K):
+    say("case token B=%d H=%d F=%d N=%d d=%d %s seed=%d gates=%s state=%s flags=%d" %
+        (B, H, F, N, d, dtype, seed, gates, state_std, flags))
+    inp = gdn_inputs(B, H, F, N, d, dtype=dtype, workload_id=seed, gates=gates, state_std=state_std)
+    dv = to_dev(inp)
+    additive = bool(flags & gdn.ADDITIVE)
+    a_, b_ = (None, None) if additive else (dv["alpha"], dv["beta"])
+    out, st = gdn.token_forward(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"], flags=flags,
+                                out_dtype=torch.float32)
+    if dtype == torch.bfloat16:
+        ob, sb = gdn.token_forward(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"], flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(ob, out.to(torch.bfloat16)), "bf16 out is not RNE of the float32 result"
+        assert torch.equal(sb, st)
+    torch.cuda.synchronize()
+    oflags = (oracle.NORMALIZE_K if flags & gdn.NORMALIZE_K else 0) | (oracle.ADDITIVE if additive else 0)
+    ro, rs = oracle_tokens(inp, F * N, oflags)
+    r1 = check("out", out, ro, TOL[dtype])
+    r2 = check("state", st, rs, TOL[dtype])
+    say("  out err/rms=%.2e state err/rms=%.2e" % (r1, r2))
+    return inp, dv, out, st
+
+
+@pytest.mark.parametrize("d", [112, 32, 16, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_token_ragged_multi_chunk(d, dtype):
+    # 150 tokens per frame = 2 full 64-token chunks + a 22-token tail
+    run_token_case(1, 2, 3, 150, d, dtype, seed=600 + d, state_std=0.2)
+
+
+@pytest.mark.parametrize("N", [1, 64, 65, 390, 880])
+def test_token_frame_lengths_d112(N):
+    F = 3 if N >= 390 else 5
+    run_token_case(1, 3, F, N, 112, torch.bfloat16, seed=620 + N, state_std=0.1)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_token_slow_gates_carry_state(dtype):
+    run_token_case(2, 2, 6, 130, 112 if dtype == torch.bfloat16 else 32, dtype, seed=640, gates="near_one",
+                   state_std=0.3)
+
+
+@pytest.mark.parametrize("normalize", [True, False])
+def test_token_additive_reduction(normalize):
+    flags = gdn.ADDITIVE | (gdn.NORMALIZE_K if normalize else 0)
+    run_token_case(1, 2, 4, 100, 112, torch.bfloat16, seed=650, state_std=0.2, flags=flags)
+
+
+def test_token_frame_end_rows_match_frame_readout():
+    """At a frame's last token the per-token and the frame-wise readouts read the same state."""
+    F, N = 4, 150
+    inp = gdn_inputs(1, 2, F, N, 112, workload_id=660, state_std=0.2, gates="near_one")
+    dv = to_dev(inp)
+    ot, st = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], F, N, state_in=dv["state_in"],
+                               out_dtype=torch.float32)
+    of, sf = gdn.frame_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], F, N, state_in=dv["state_in"],
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    last = torch.arange(1, F + 1, device=DEV) * N - 1
+    a, b = ot[:, :, last].double(), of[:, :, last].double()
+    rms = b.pow(2).mean().sqrt()
+    assert (a - b).abs().max() <= 2e-2 * rms
+    assert (st.double() - sf.double()).abs().max() <= 2e-2 * sf.double().pow(2).mean().sqrt()
+
+
+def test_token_multi_window_equals_single(monkeypatch):
+    inp = gdn_inputs(1, 2, 7, 90, 112, workload_id=670, state_std=0.2, gates="near_one")
+    dv = to_dev(inp)
+    o1, s1 = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 7, 90, state_in=dv["state_in"],
+                               out_dtype=torch.float32)
+    monkeypatch.setenv("GDN_WINDOW_UNITS", "4")  # 2 frames per window for B*H = 2
+    o2, s2 = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 7, 90, state_in=dv["state_in"],
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    ro, rs = oracle_tokens(inp, 7 * 90)
+    check("out", o2, ro, 2e-2)
+    check("state", s2, rs, 2e-2)
+
+
+def test_token_state_in_place_and_no_state_out():
+    inp = gdn_inputs(1, 2, 3, 70, 112, workload_id=680, state_std=0.2, gates="near_one")
+    dv = to_dev(inp)
+    ro, rs = oracle_tokens(inp, 3 * 70)
+    s = dv["state_in"].clone()
+    out, _ = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 3, 70, state_in=s, state_out=s,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check("out", out, ro, 2e-2)
+    check("state", s, rs, 2e-2)
+    # no state returned, a single group: the readout pass reads state_in directly
+    out2, none = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 3, 70,
+                                   state_in=dv["state_in"], return_state=False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert none is None
+    check("out (no state_out)", out2, ro, 2e-2)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from chunked_ref import gdn_chunked
+from chunked_ref import gdn_chunked, gdn_chunked_tokens
 from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "handworked_d2.json")
@@ -199,6 +199,23 @@ def test_chunked_form_equals_sequential(chunk, affine):
                              state_in=_np(inp["state_in"])[0, 0], affine=affine)
         scale = np.sqrt(np.mean(out ** 2))
         assert np.max(np.abs(o2 - out[0, 0])) <= 1e-11 * scale
+        assert np.max(np.abs(s2 - st[0, 0])) <= 1e-11 * np.sqrt(np.mean(st ** 2))
+
+
+@pytest.mark.parametrize("chunk", [64, 16, 7])
+def test_chunked_token_readout_equals_sequential(chunk):
+    """Per-token causal readout (every token reads the state after itself) in chunk form --
+    exp(G) Q S0^T plus the decay-masked intra-chunk product with v' = U - W S0^T -- equals
+    the token-by-token oracle run with one-token frames."""
+    T, d, dv = 150, 16, 12
+    for gates in ("config", "near_one"):
+        inp = _rand_gdn(B=1, H=1, F=1, N=T, d=d, dv=dv, seed=21, gates=gates, state_std=0.5)
+        out, st = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], T, 1,
+                                     state_in=inp["state_in"])
+        o2, s2 = gdn_chunked_tokens(_np(inp["q"])[0, 0], _np(inp["k"])[0, 0], _np(inp["v"])[0, 0],
+                                    _np(inp["alpha"])[0, 0], _np(inp["beta"])[0, 0], chunk=chunk,
+                                    state_in=_np(inp["state_in"])[0, 0])
+        assert np.max(np.abs(o2 - out[0, 0])) <= 1e-11 * np.sqrt(np.mean(out ** 2))
         assert np.max(np.abs(s2 - st[0, 0])) <= 1e-11 * np.sqrt(np.mean(st ** 2))
 
 
