@@ -39,13 +39,22 @@ KERNEL_SOURCES = ["linear_attention_video_gated_amd/csrc/gdn_frame.hip",
 #   bc_scan           per-frame sums only
 #   bc_readout        reads q, writes o:             2*d*es
 GDN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_frame_readout")
+TOKEN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_token_readout")
 BC_KERNELS = ("bc_partial", "bc_scan", "bc_readout")
 
 
 def kernel_bytes_per_token_head(kind, d, es):
+    """Algorithmic bytes per token-head each kernel must move (its own inputs and outputs)."""
     if kind == "block_causal":
         return {"bc_partial": 2 * d * es, "bc_scan": 0, "bc_readout": 2 * d * es}
+    if kind == "token":  # the readout pass reads k, v and the gates again, and q; writes o
+        return {"gdn_frame_affine": 2 * d * es + 8, "gdn_frame_chain": 0, "gdn_token_readout": 4 * d * es + 8}
     return {"gdn_frame_affine": 2 * d * es + 8, "gdn_frame_chain": 0, "gdn_frame_readout": 2 * d * es}
+
+
+def path_bytes_per_token_head(kind, d, es):
+    """Algorithmic bytes per token-head of the whole path: q, k, v, o (and the gates)."""
+    return 4 * d * es + (0 if kind == "block_causal" else 8)
 
 
 def kernel_source_hash():
@@ -117,6 +126,28 @@ def setup(wl, device):
                       device=device, state_std=wl.state_std)
 
 
+def near_one_timing(wl, device, ms_graded, steps=20, warmup=5):
+    """ms per step of the same workload with alpha = exp(-1e-3 softplus(x)) gates."""
+    import torch
+    from linear_attention_video_gated_amd.inputs import gdn_inputs
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    inp = gdn_inputs(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt, workload_id=wl.wid,
+                     device=device, state_std=wl.state_std, gates="near_one")
+    step = make_step(wl, inp)
+    for _ in range(warmup):
+        step()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del inp, step
+    return {"ms_per_step": round(ms, 4), "ratio_to_graded": round(ms / ms_graded, 3), "steps": steps}
+
+
 def make_step(wl, inp, events=None):
     """One pass of the hot path: a closure that enqueues it on the current stream."""
     from linear_attention_video_gated_amd import gdn
@@ -138,6 +169,9 @@ def make_step(wl, inp, events=None):
             gdn.frame_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
                               state_in=inp["state_in"], state_out=st, out=out)
         return step
+    if wl.kind == "token":
+        return lambda ev=None: gdn.token_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
+                                                 state_in=inp["state_in"], state_out=st, out=out, events=ev)
     return lambda ev=None: gdn.frame_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
                                              state_in=inp["state_in"], state_out=st, out=out, events=ev)
 
@@ -179,7 +213,10 @@ def cpu_baseline(wl, inp, budget_heads=16, frames=None):
     else:
         a, b = take(inp["alpha"]), take(inp["beta"])
         s_in = inp["state_in"][:1, :heads].float().cpu().numpy() if inp["state_in"] is not None else None
-        oracle.gdn_forward(q, k, v, a, b, frames, wl.frame_len, state_in=s_in, n_threads=cores)
+        if wl.kind == "token":  # every token reads out: one-token frames
+            oracle.gdn_forward(q, k, v, a, b, T, 1, state_in=s_in, n_threads=cores)
+        else:
+            oracle.gdn_forward(q, k, v, a, b, frames, wl.frame_len, state_in=s_in, n_threads=cores)
     dt = time.perf_counter() - t0
     # tokens/s of the whole workload: the sample covers heads/H of each token's work
     value = T * heads / wl.H / dt
@@ -224,8 +261,8 @@ def main():
     nk = 3
     import torch as _t
     dt = _t.bfloat16 if wl.dtype == "bf16" else _t.float32
-    entry = gdn.ENTRY_BLOCK_CAUSAL if wl.kind == "block_causal" else (
-        gdn.ENTRY_READONLY if wl.kind == "stream" else gdn.ENTRY_FORWARD)
+    entry = {"block_causal": gdn.ENTRY_BLOCK_CAUSAL, "stream": gdn.ENTRY_READONLY,
+             "token": gdn.ENTRY_TOKEN}.get(wl.kind, gdn.ENTRY_FORWARD)
     nwin = gdn.window_count(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
                             flags=gdn.RELU_QK if wl.kind == "block_causal" else gdn.NORMALIZE_K, entry=entry)
     ev = [hip.create(6 * nwin) for _ in range(args.steps)]
@@ -240,7 +277,7 @@ def main():
     t_wall = time.perf_counter() - t_wall0
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    names = BC_KERNELS if wl.kind == "block_causal" else GDN_KERNELS
+    names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS}.get(wl.kind, GDN_KERNELS)
     kms = [0.0] * nk  # per call, summed over the call's windows
     for e in ev:
         for wi in range(nwin):
@@ -271,12 +308,17 @@ def main():
                 "traffic": traffic, "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin,
                 "algorithmic_bytes": round(kbytes),
                 "all_kernels_ms_per_call": {n: round(x, 4) for n, x in zip(names, kms)}}
-    path_bytes = sum(per.values()) * th * calls
+    path_per = path_bytes_per_token_head(wl.kind, wl.d, es)
+    path_bytes = path_per * th * calls
     path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
-    path = {"algorithmic_bytes_per_call": sum(per.values()) * th, "achieved": round(path_gbps, 1),
+    path = {"algorithmic_bytes_per_call": path_per * th, "achieved": round(path_gbps, 1),
             "unit": "GB/s", "frac_of_8TBps": round(path_gbps / HBM_PEAK_GBPS, 4)}
 
     extra = {}
+    if wl.kind != "block_causal":
+        # the alpha ~ 1 stress variant (slow decay: the maps and states keep full range);
+        # the kernels do the same work whatever the gate values, so this should match
+        extra["alpha_near_one"] = near_one_timing(wl, dev, ms_step)
     if args.copy_calib:
         extra["hbm_copy_GBps"] = round(copy_bandwidth_gbps(dev), 1)
 

@@ -134,8 +134,8 @@ __host__ __device__ constexpr int frTm(int I) { return 6 + I; }
 
 // MODE = the call's GDN_F_NORMALIZE_K (bit 0) and GDN_F_ADDITIVE (bit 1) flags, fixed at
 // compile time so that the per-tile choices they make are not branches.
-template <typename E, int ND, int MODE, bool TOK = false>
-__global__ __launch_bounds__((P1<E, ND, TOK>::NT), 1) void gdn_frame_affine(P1Args a) {
+template <typename E, int ND, int MODE, bool TOK>
+__device__ __forceinline__ void affine_body(P1Args a) {
     using L = P1<E, ND, TOK>;
     using O = Ops<E>;
     using F8 = typename O::F8;
@@ -958,6 +958,19 @@ __global__ __launch_bounds__((P1<E, ND, TOK>::NT), 1) void gdn_frame_affine(P1Ar
     }
 }
 
+template <typename E, int ND, int MODE>
+__global__ __launch_bounds__((P1<E, ND>::NT), 1) void gdn_frame_affine(P1Args a) {
+    affine_body<E, ND, MODE, false>(a);
+}
+
+// Per-token readout pass: the same chunk pipeline run from each group's true start state
+// (the state before the group, from the chain), B part only, writing o_t = S_t q_t for
+// every token (TOK branches of the body above).
+template <typename E, int ND, int MODE>
+__global__ __launch_bounds__((P1<E, ND, true>::NT), 1) void gdn_token_readout(P1Args a) {
+    affine_body<E, ND, MODE, true>(a);
+}
+
 // -------------------------------------------------------------------------------------
 // Phase 2: the serial chain over groups, S_g = S_{g-1} A_g + B_g
 // -------------------------------------------------------------------------------------
@@ -1242,8 +1255,8 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
     if (!attr_done) {
         const void* aff[4] = {(const void*)gdn_frame_affine<E, ND, 0>, (const void*)gdn_frame_affine<E, ND, 1>,
                               (const void*)gdn_frame_affine<E, ND, 2>, (const void*)gdn_frame_affine<E, ND, 3>};
-        const void* tok[4] = {(const void*)gdn_frame_affine<E, ND, 0, true>, (const void*)gdn_frame_affine<E, ND, 1, true>,
-                              (const void*)gdn_frame_affine<E, ND, 2, true>, (const void*)gdn_frame_affine<E, ND, 3, true>};
+        const void* tok[4] = {(const void*)gdn_token_readout<E, ND, 0>, (const void*)gdn_token_readout<E, ND, 1>,
+                              (const void*)gdn_token_readout<E, ND, 2>, (const void*)gdn_token_readout<E, ND, 3>};
         hipError_t e = hipSuccess;
         for (const void* f : aff)
             if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS_B)) != hipSuccess)
@@ -1266,10 +1279,10 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
         const P1Args& p1 = *(const P1Args*)args;
         const dim3 grid((p1.nf + p1.G - 1) / p1.G, BH);
         switch (p1.flags & 3u) {
-        case 0: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 0, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
-        case 1: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 1, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
-        case 2: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 2, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
-        default: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 3, true>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        case 0: hipLaunchKernelGGL((gdn_token_readout<E, ND, 0>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        case 1: hipLaunchKernelGGL((gdn_token_readout<E, ND, 1>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        case 2: hipLaunchKernelGGL((gdn_token_readout<E, ND, 2>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        default: hipLaunchKernelGGL((gdn_token_readout<E, ND, 3>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
         }
     } else if (phase == 0) {
         const P1Args& p1 = *(const P1Args*)args;
