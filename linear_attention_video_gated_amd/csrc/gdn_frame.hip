@@ -518,36 +518,38 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         return f;
     };
 
-    // ---- TOK, chain waves, beside the substitution: the ten lower-triangle tiles (tile T
+    // ---- TOK, beside the substitution: the ten lower-triangle tiles (tile T
     //      of query tokens, tile J of key tokens, J <= T) of the intra-chunk weights
     //          Aqk[t][i] = e^{G_t - G_i} n_i (q_t . k_i)   (i <= t, else 0),
     //      computed as (K Q^T) so that lane (c, g) holds Aqk[16T + c][16J + 4g + i]: the B
     //      operand of the readout's K16 product over key tokens.  Decay factors as in L:
     //      one exp2 of a difference inside a block, split at the key block's end across
-    //      blocks (both factors <= 1).
-    auto aqk = [&](int q) {
+    //      blocks (both factors <= 1).  Each chain wave takes one tile, the prep wave the
+    //      rest.
+    // Tiles x in [x0, 10) with x = x0 (mod xs) go to the calling wave.
+    auto aqk = [&](int q, int x0, int xs) {
         const float* sc = SC(q);
         E* const aq = (E*)(smem + L::OFF_AQ);
-        for (int x = w; x < 10; x += ND) {
+        for (int x = x0; x < 10; x += xs) {
             const int T = x < 1 ? 0 : x < 3 ? 1 : x < 6 ? 2 : 3;
             const int J = x - T * (T + 1) / 2;
-            f32x4 acc = zero4();
+            f32x4 a4 = zero4();
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) acc = O::mma32(rowfrag(KB_(q), 16 * J, kb), rowfrag(QB_(q), 16 * T, kb), acc);
+            for (int kb = 0; kb < KB; ++kb) a4 = O::mma32(rowfrag(KB_(q), 16 * J, kb), rowfrag(QB_(q), 16 * T, kb), a4);
             const float gt = sc[208 + 16 * T + c];
             const f32x4 gi4 = *(const f32x4*)(sc + 208 + 16 * J + 4 * g);
             const f32x4 ni4 = *(const f32x4*)(sc + 272 + 16 * J + 4 * g);
             if (T == J) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i <= c) ? acc[i] * ni4[i] * hw_exp2(gt - gi4[i]) : 0.f;
+                for (int i = 0; i < 4; ++i) a4[i] = (4 * g + i <= c) ? a4[i] * ni4[i] * hw_exp2(gt - gi4[i]) : 0.f;
             } else {
                 const float ge = sc[208 + 16 * J + 15];
                 const float rowf = hw_exp2(gt - ge);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= rowf * ni4[i] * hw_exp2(ge - gi4[i]);
+                for (int i = 0; i < 4; ++i) a4[i] *= rowf * ni4[i] * hw_exp2(ge - gi4[i]);
             }
             F4 hi, lo;
-            O::split4(acc, hi, lo);
+            O::split4(a4, hi, lo);
             *(F4*)(aq + ((x * NS) * 64 + lane) * 4) = hi;
             if constexpr (NS > 1) *(F4*)(aq + ((x * NS + 1) * 64 + lane) * 4) = lo;
         }
@@ -770,6 +772,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     dma_tiles(q + 1, 1, 2, false, kAll);
                     prep1(q + 1, gr, R);
                 }
+                aqk(q, ND, 1);  // the tiles past the chain waves' one each
                 lds_barrier();  // B2: W and the intra-chunk weights of chunk q staged
                 if (q + 1 < nq) {
                     prep2(q + 1, gr, R);
@@ -789,6 +792,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 prep2(q, gr, R);
                 prep3(q);
                 lds_barrier();
+                aqk(q, ND, 1);
                 lds_barrier();
                 lds_barrier();
             }
@@ -885,7 +889,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kAll);
                     if (q + 1 < nq) dma_tiles(q + 1, 1, 2, false, kAll);
                     subst(q, Ur);
-                    aqk(q);
+                    aqk(q, w, 10);
                     lds_barrier();  // B2
                     chain_tok(q, XB, Ur);
                     wait_vmem();
@@ -899,7 +903,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     lds_barrier();
                     lds_barrier();
                     subst(q, Ur);
-                    aqk(q);
+                    aqk(q, w, 10);
                     lds_barrier();
                     chain_tok(q, XB, Ur);
                     lds_barrier();
