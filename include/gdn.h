@@ -85,7 +85,11 @@ enum {
     GDN_F_NORMALIZE_K = 1u << 0, /* L2-normalise k inside the kernel (float32)            */
     GDN_F_ADDITIVE = 1u << 1,    /* gated delta rule entries: S <- S + v k^T              */
     GDN_F_RELU_QK = 1u << 2,     /* block-causal entry: phi = ReLU on q and k (else id)  */
-    GDN_F_OUT_F32 = 1u << 3      /* out is float32 whatever dtype is (all entries)        */
+    GDN_F_OUT_F32 = 1u << 3,     /* out is float32 whatever dtype is (all entries)        */
+    GDN_F_GATE_LOGITS = 1u << 4  /* gated delta rule entries: alpha and beta hold logits a,
+                                    b; the gates are alpha = exp(-softplus(a)) (clamped
+                                    below at FLT_MIN) and beta = 1 / (1 + e^-b), formed in
+                                    float32 inside the kernels                            */
 };
 
 enum { GDN_ENTRY_FORWARD = 0, GDN_ENTRY_READONLY = 1, GDN_ENTRY_BLOCK_CAUSAL = 2, GDN_ENTRY_TOKEN = 3 };
@@ -111,6 +115,7 @@ typedef struct gdn_dims {
  *  q, k      [B,H,T,d_k] dtype      v, out [B,H,T,d_v] dtype
  *  alpha     [B,H,T] float32 gate in (0,1] (clamped below at FLT_MIN); may be NULL
  *            only with GDN_F_ADDITIVE.  beta [B,H,T] float32 in [0,1]; same rule.
+ *            With GDN_F_GATE_LOGITS both hold logits instead (any finite value).
  *  state_in  [B,H,d_v,d_k] float32, NULL = zero state.  Read only.
  *  state_out [B,H,d_v,d_k] float32, the state after the last frame; NULL = not
  *            written; may equal state_in.

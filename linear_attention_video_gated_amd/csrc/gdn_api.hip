@@ -86,7 +86,8 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
     if (d->d_k != d->d_v || nd_of(d->d_k) == 0) return GDN_ERR_UNSUPPORTED;
     const uint32_t allowed = (entry == GDN_ENTRY_BLOCK_CAUSAL)
                                  ? (uint32_t)(GDN_F_RELU_QK | GDN_F_OUT_F32)
-                                 : (uint32_t)(GDN_F_NORMALIZE_K | GDN_F_ADDITIVE | GDN_F_OUT_F32);
+                                 : (uint32_t)(GDN_F_NORMALIZE_K | GDN_F_ADDITIVE | GDN_F_OUT_F32 |
+                                              GDN_F_GATE_LOGITS);
     if (d->flags & ~allowed) return GDN_ERR_UNSUPPORTED;
     p->BH = (long long)d->B * d->H;
     p->T = (long long)d->n_frames * d->frame_len;

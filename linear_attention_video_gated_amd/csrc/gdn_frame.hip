@@ -321,8 +321,20 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             be = valid ? 1.f : 0.f;
         } else {
             const float al = RAW(p)[t], bl = RAW(p)[64 + t];
-            gl = valid ? hw_log2(fmaxf(al, FLT_MIN)) : 0.f;
-            be = valid ? bl : 0.f;
+            float l2a, bb;
+            if (a.flags & 16u) {
+                // gates given as logits: log2 alpha = -softplus(al) log2(e), beta = sigmoid(bl);
+                // softplus(x) = max(x, 0) + log(1 + e^{-|x|}); clamped as alpha >= FLT_MIN is
+                constexpr float kLog2e = 1.4426950408889634f;
+                const float sp2 = fmaxf(al, 0.f) * kLog2e + hw_log2(1.f + hw_exp2(-fabsf(al) * kLog2e));
+                l2a = fmaxf(-sp2, -126.f);
+                bb = 1.f / (1.f + hw_exp2(-bl * kLog2e));
+            } else {
+                l2a = hw_log2(fmaxf(al, FLT_MIN));
+                bb = bl;
+            }
+            gl = valid ? l2a : 0.f;
+            be = valid ? bb : 0.f;
         }
         const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
         // (the lane-read builtins are integer-typed: move the bits, not the value)

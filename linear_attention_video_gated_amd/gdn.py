@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdn_mi355x.so")
 
 GDN_BF16, GDN_F32 = 0, 1
-NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32 = 1, 2, 4, 8
+NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS = 1, 2, 4, 8, 16
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
 EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
            "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")

@@ -8,6 +8,7 @@ with the HIP path.  Every function here is "parity pinned" by the tests in
 from .oracle import (  # noqa: F401
     NORMALIZE_K,
     ADDITIVE,
+    GATE_LOGITS,
     build,
     gdn_forward,
     linear_attn_block_causal,

@@ -18,6 +18,7 @@ import numpy as np
 
 NORMALIZE_K = 1
 ADDITIVE = 2
+GATE_LOGITS = 4  # alpha, beta hold logits a, b: alpha = exp(-softplus(a)), beta = sigmoid(b)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle_gdn.c")

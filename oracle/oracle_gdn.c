@@ -57,6 +57,8 @@
 
 #define ORACLE_NORMALIZE_K 1u /* L2-normalise k before use                  */
 #define ORACLE_ADDITIVE    2u /* S += v k^T: no gate, no beta, no delta term */
+#define ORACLE_GATE_LOGITS 4u /* alpha, beta hold logits a, b: alpha = exp(-softplus(a)),
+                                 beta = 1 / (1 + exp(-b))                            */
 
 int oracle_abi_version(void) { return 1; }
 
@@ -68,6 +70,10 @@ int oracle_abi_version(void) { return 1; }
  * expanded without forming d x d matrices:  with s = S k,
  *   S <- a S + b (v - a s) k^T.
  * With ORACLE_ADDITIVE:  S <- S + v k^T.
+ * With ORACLE_GATE_LOGITS the gate arrays hold logits (the parameterisation the
+ * synthetic workloads draw the gates from): a = exp(-softplus(alpha_t)), with
+ * softplus(x) = log(1 + e^x) evaluated without overflow, clamped below at FLT_MIN
+ * as above; b = 1 / (1 + e^{-beta_t}).
  * After a frame's last token, o_t = S q_t for every token t of the frame.
  *
  * state_in may be NULL (zero state); state_out may be NULL.
@@ -124,8 +130,17 @@ int oracle_gdn_forward(const float* q, const float* k, const float* v,
                         for (int j = 0; j < dk; ++j)
                             S[(size_t)i * dk + j] += (double)vt[i] * kk[j];
                 } else {
-                    const double a = (double)(ah[t] > FLT_MIN ? ah[t] : FLT_MIN);
-                    const double b = (double)bth[t];
+                    double a, b;
+                    if (flags & ORACLE_GATE_LOGITS) {
+                        const double x = (double)ah[t], y = (double)bth[t];
+                        const double sp = x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+                        a = exp(-sp);
+                        if (a < (double)FLT_MIN) a = (double)FLT_MIN;
+                        b = 1.0 / (1.0 + exp(-y));
+                    } else {
+                        a = (double)(ah[t] > FLT_MIN ? ah[t] : FLT_MIN);
+                        b = (double)bth[t];
+                    }
                     for (int i = 0; i < dv; ++i) {
                         double acc = 0.0;
                         for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * kk[j];

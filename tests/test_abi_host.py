@@ -93,7 +93,7 @@ def test_workspace_zero_for_invalid_or_empty():
 
 @pytest.mark.parametrize("field,val,code", [
     ("dtype", 5, -3), ("B", -1, -2), ("frame_len", 0, -2), ("n_frames", -2, -2),
-    ("d_k", 48, -7), ("flags", 16, -7),
+    ("d_k", 48, -7), ("flags", 32, -7), ("flags", gdn.RELU_QK, -7),
 ])
 def test_bad_dims_rejected(field, val, code):
     dm = dims()
@@ -143,6 +143,9 @@ def test_block_causal_flag_rules():
     dm = dims(flags=gdn.RELU_QK)
     assert gdn.lib().linear_attn_block_causal(FAKE, FAKE + 2 ** 28, FAKE + 2 ** 29, None, None, None, None,
                                               FAKE + 2 ** 30, ctypes.byref(dm), None) == -6
+    dm = dims(flags=gdn.RELU_QK | gdn.GATE_LOGITS)  # gate logits belong to the gated delta rule
+    assert gdn.lib().linear_attn_block_causal(FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                              ctypes.byref(dm), None) == -7
 
 
 def test_empty_batch_is_a_noop():

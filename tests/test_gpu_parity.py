@@ -223,3 +223,32 @@ def test_block_causal_multi_window(monkeypatch):
     o2, s2, z2 = gdn.linear_attn_block_causal(dv["q"], dv["k"], dv["v"], 5, 40, state_in=dv["state_in"], z_in=dv["z_in"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(z1, z2)
+
+
+@pytest.mark.parametrize("entry", ["frame", "token"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gdn_gate_logits(entry, dtype):
+    """GDN_F_GATE_LOGITS: alpha and beta hold logits; the oracle forms the gates in float64."""
+    F, N, d = 3, 150, 112 if dtype == torch.bfloat16 else 64
+    say("case gate logits entry=%s %s" % (entry, dtype))
+    inp = gdn_inputs(1, 2, F, N, d, dtype=dtype, workload_id=360, state_std=0.2)
+    g = torch.Generator().manual_seed(360)
+    a = (2.0 * torch.randn(1, 2, F * N, generator=g)).contiguous()
+    b = (2.0 * torch.randn(1, 2, F * N, generator=g)).contiguous()
+    # alpha ~ 1 and a near reset (alpha = e^-8 per token for 20 tokens).  Harder resets
+    # inside one 64-token chunk push the chunk's log-gate prefix G past ~500 in magnitude,
+    # where fp32 differences G_t - G_i keep ~1e-4 absolute precision: the float32 bound
+    # of 1e-4 is then no longer met (bf16 inputs are unaffected).
+    a[0, 0, :20] = -30.0
+    a[0, 1, :20] = 8.0
+    dv = to_dev(inp)
+    fn = gdn.token_forward if entry == "token" else gdn.frame_forward
+    out, st = fn(dv["q"], dv["k"], dv["v"], a.to(DEV), b.to(DEV), F, N, state_in=dv["state_in"],
+                 flags=gdn.NORMALIZE_K | gdn.GATE_LOGITS, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    nf, fl = (F * N, 1) if entry == "token" else (F, N)
+    ro, rs = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], a, b, nf, fl, state_in=inp["state_in"],
+                                flags=oracle.NORMALIZE_K | oracle.GATE_LOGITS)
+    r1 = check("out", out, ro, TOL[dtype])
+    r2 = check("state", st, rs, TOL[dtype])
+    say("  out err/rms=%.2e state err/rms=%.2e" % (r1, r2))

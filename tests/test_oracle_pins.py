@@ -272,3 +272,48 @@ def test_oracle_threads_do_not_change_results():
     o1, s1 = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], 2, 9, n_threads=1)
     o4, s4 = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], 2, 9, n_threads=4)
     assert np.array_equal(o1, o4) and np.array_equal(s1, s4)
+
+
+# ---------------------------------------------------------------- gates given as logits
+def _np64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def test_gate_logits_equal_sigmoid_gates():
+    """exp(-softplus(a)) = 1 / (1 + e^a) and beta = 1 / (1 + e^-b): the logit mode equals the
+    plain mode fed with those gates (computed here by the other formula, in float64, then
+    rounded to float32 -- hence the 1e-5 bound)."""
+    T, d = 40, 8
+    inp = _rand_gdn(B=1, H=2, F=4, N=10, d=d, seed=31, state_std=0.3)
+    rng = np.random.default_rng(31)
+    a = rng.normal(0.0, 2.0, size=(1, 2, T)).astype(np.float32)
+    b = rng.normal(0.0, 2.0, size=(1, 2, T)).astype(np.float32)
+    al = (1.0 / (1.0 + np.exp(_np64(a)))).astype(np.float32)
+    be = (1.0 / (1.0 + np.exp(-_np64(b)))).astype(np.float32)
+    o1, s1 = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], a, b, 4, 10, state_in=inp["state_in"],
+                                flags=oracle.NORMALIZE_K | oracle.GATE_LOGITS)
+    o2, s2 = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], al, be, 4, 10, state_in=inp["state_in"])
+    assert np.max(np.abs(o1 - o2)) <= 1e-5 * np.sqrt(np.mean(o2 ** 2))
+    assert np.max(np.abs(s1 - s2)) <= 1e-5 * np.sqrt(np.mean(s2 ** 2))
+
+
+def test_gate_logits_limits():
+    """a = -60, b = +60: alpha = beta = 1 to float64 precision, so with one-token frames and
+    q_t = k^_t every token retrieves its own value exactly (S_t k^_t = v_t).  a = +60: the
+    state is wiped at every token (alpha ~ 1e-26), so S_t = v_t k^_t^T and o_t = v_t (k^_t . q_t)."""
+    T, d, dv = 12, 6, 5
+    rng = np.random.default_rng(32)
+    k = rng.normal(size=(1, 1, T, d)).astype(np.float32)
+    kh = _np64(k) / np.linalg.norm(_np64(k), axis=-1, keepdims=True)
+    q_eq = kh.astype(np.float32)
+    v = rng.normal(size=(1, 1, T, dv)).astype(np.float32)
+    big = np.full((1, 1, T), 60.0, dtype=np.float32)
+    flags = oracle.NORMALIZE_K | oracle.GATE_LOGITS
+    out, _ = oracle.gdn_forward(q_eq, k, v, -big, big, T, 1, state_in=0.5 * np.ones((1, 1, dv, d), np.float32),
+                                flags=flags)
+    # q is k^ rounded to float32: the retrieval error is that rounding, ~1e-7 relative
+    np.testing.assert_allclose(out[0, 0], _np64(v[0, 0]), rtol=0, atol=1e-6)
+    q = rng.normal(size=(1, 1, T, d)).astype(np.float32)
+    out, _ = oracle.gdn_forward(q, k, v, big, big, T, 1, state_in=np.ones((1, 1, dv, d), np.float32), flags=flags)
+    ref = _np64(v[0, 0]) * np.sum(kh[0, 0] * _np64(q[0, 0]), axis=-1, keepdims=True)
+    np.testing.assert_allclose(out[0, 0], ref, rtol=0, atol=1e-12 + 1e-9 * np.abs(ref).max())
