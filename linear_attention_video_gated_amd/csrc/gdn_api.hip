@@ -162,20 +162,29 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         const int f0 = wi * p.nfw;
         const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
         const bool last = wi == p.nwin - 1;
-        // a call that keeps no state and has a single group reads state_in directly (its
-        // layout is that of the per-group states with one group): no chain to run
-        const bool no_chain = !state_out && p.nwin == 1 && nf <= p.G;
-        const float* s_before = no_chain ? state_in : sgrp;
+        // A call with a single group per (b, h) knows the state at the group start:
+        // state_in (its layout is that of the per-group states with one group).  The frame
+        // maps then run from it (true start: no A part, the B maps are the states, state_out
+        // written by that pass), and there is no chain to run; the per-token readout pass
+        // needs neither the maps nor the chain.
+        const bool single = p.nwin == 1 && nf <= p.G;
+        const float* s_before = single ? state_in : sgrp;
         const int of32 = (d->flags & GDN_F_OUT_F32) ? 1 : 0;
         const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, apack, bt,
-                        tok ? 0 : 1, nullptr, nullptr, nullptr, 0};
+                        tok ? 0 : 1, nullptr, nullptr, single ? state_in : nullptr, 0, single ? 1 : 0,
+                        single ? state_out : nullptr};
         const P1Args a3t{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, nullptr, nullptr,
-                         0, q, out, s_before, of32};
+                         0, q, out, s_before, of32, 0, single ? state_out : nullptr};
         const P2Args a2{apack, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
-        const P3Args a3{q, out, apack, bt, s_before, p.T, d->frame_len, f0, nf, p.G, of32};
+        const P3Args a3{q, out, apack, bt, single ? nullptr : sgrp, p.T, d->frame_len, f0, nf, p.G, of32,
+                        single ? 1 : 0};
         void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
-        if (launch_gdn_phase<E, ND>(0, &a1, BH, st, ev) != hipSuccess) return GDN_ERR_HIP;
-        if (no_chain) {
+        if (tok && single) {  // the readout pass alone
+            if (record(ev, 0, st) != hipSuccess || record(ev, 1, st) != hipSuccess) return GDN_ERR_HIP;
+        } else if (launch_gdn_phase<E, ND>(0, &a1, BH, st, ev) != hipSuccess) {
+            return GDN_ERR_HIP;
+        }
+        if (single) {
             if (record(ev, 2, st) != hipSuccess || record(ev, 3, st) != hipSuccess) return GDN_ERR_HIP;
         } else if (launch_gdn_phase<E, ND>(1, &a2, BH, st, ev) != hipSuccess) {
             return GDN_ERR_HIP;

@@ -172,6 +172,10 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     const E* qp = TOK ? (const E*)a.q + tok0 * D : nullptr;
     constexpr bool additive = (MODE & 2) != 0;
     constexpr bool normalize = (MODE & 1) != 0;
+    // TS (true start, frame maps only): the call has one group per (b, h), so the state at
+    // the group start is known -- the B part starts from it, the A part is not formed,
+    // every frame end writes the true state S_f as its B map, and state_out is written here.
+    constexpr bool TS = !TOK && (MODE & 4) != 0;
     const int nch = (N + 63) / 64;
     const int nq = nfg * nch;                   // chunks of the group, frame by frame
     auto chunk_t0 = [&](int q) { const int f = q / nch; return (long long)f * N + (q - f * nch) * 64; };
@@ -663,7 +667,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         for (int kb = 0; kb < KB; ++kb) {
             const f32x4 hiA = (2 * kb + 1 < ND) ? XA[(2 * kb + 1) % ND] : zero4();
             const f32x4 hiB = (2 * kb + 1 < ND) ? XB[(2 * kb + 1) % ND] : zero4();
-            xa[kb] = O::pack8(XA[2 * kb], hiA);
+            if constexpr (!TS) xa[kb] = O::pack8(XA[2 * kb], hiA);
             xb[kb] = O::pack8(XB[2 * kb], hiB);
         }
         // token halves h = 0, 1: innovation D' for the half's two token tiles, then
@@ -689,13 +693,14 @@ __device__ __forceinline__ void affine_body(P1Args a) {
 #pragma unroll
                         for (int j = 4; j < 8; ++j) wf[j] = (E)0.f;
                     }
-                    PA[u] = O::mma32(wf, xa[kb], PA[u]);
+                    if constexpr (!TS) PA[u] = O::mma32(wf, xa[kb], PA[u]);
                     PB[u] = O::mma32(wf, xb[kb], PB[u]);
                 }
             }
             // the B part carries the state and gets a hi + lo innovation; the A part,
             // which only maps a carried state, a single bf16 one
-            const F8 dA = O::pack8(PA[0], PA[1]);
+            F8 dA;
+            if constexpr (!TS) dA = O::pack8(PA[0], PA[1]);
             F8 dBh, dBl;
             O::split8(PB[0], PB[1], dBh, dBl);
 #pragma unroll
@@ -704,12 +709,13 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 const F8 kf = __builtin_shufflevector(O::ldtr(kb, L::KPB, 32 * h, 16 * m, lane),
                                                       O::ldtr(kb, L::KPB, 32 * h + 16, 16 * m, lane), 0, 1, 2, 3,
                                                       4, 5, 6, 7);
-                f32x4 xa2 = h == 0 ? XA[m] * gam : XA[m];
                 f32x4 xb2 = h == 0 ? XB[m] * gam : XB[m];
-                xa2 = O::mma32(kf, dA, xa2);
+                if constexpr (!TS) {
+                    f32x4 xa2 = h == 0 ? XA[m] * gam : XA[m];
+                    XA[m] = O::mma32(kf, dA, xa2);
+                }
                 xb2 = O::mma32(kf, dBh, xb2);
                 if (O::kSplit) xb2 = O::mma32(kf, dBl, xb2);
-                XA[m] = xa2;
                 XB[m] = xb2;
             }
         }
@@ -726,6 +732,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         float* bt = a.Bt + unit * (ND * ND * 256) + (long long)w * ND * 256;
 #pragma unroll
         for (int t = 0; t < ND; ++t) *(f32x4*)(bt + t * 256 + lane * 4) = XB[t];
+        if constexpr (TS) return;  // B is the true state: no A map
         f32x4 eye;
 #pragma unroll
         for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 1.f : 0.f;
@@ -883,13 +890,15 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             XB[t] = zero4();
         }
         f32x4 Ur[4];  // U column tile w of the chunk to be applied next, pre-scaled by kts
-        if constexpr (TOK) {
+        if constexpr (TOK || TS) {
             // the true state at the group start: S_before rows 16w.. (zero when NULL)
             const int ngw = (a.nf + a.G - 1) / a.G;
             const float* sg = a.Sgrp ? a.Sgrp + ((long long)bh * ngw + gi) * D * D + (long long)(16 * w + c) * D
                                      : nullptr;
 #pragma unroll
             for (int t = 0; t < ND; ++t) XB[t] = sg ? *(const f32x4*)(sg + 16 * t + 4 * g) : zero4();
+        }
+        if constexpr (TOK) {
             if constexpr (L::PIPE) {
                 dma_tiles(0, 0, 1, true, kAll);
                 dma_tiles(0, 1, 2, false, kAll);
@@ -969,6 +978,14 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 if (q - fl * nch == nch - 1 && (a.emit_all || fl == nfg - 1)) emit(fl, XA, XB);
                 if constexpr (L::PIPE) wait_dma_behind(q);
                 lds_barrier();  // B3
+            }
+        }
+        // the state after the group's last token (one-group calls only)
+        if constexpr (TOK || TS) {
+            if (a.state_out) {
+                float* so = a.state_out + (long long)bh * D * D + (long long)(16 * w + c) * D;
+#pragma unroll
+                for (int t = 0; t < ND; ++t) *(f32x4*)(so + 16 * t + 4 * g) = XB[t];
             }
         }
     }
@@ -1127,8 +1144,18 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
 #pragma unroll
     for (int u = 0; u < NSL; ++u) own[u] = w + 4 * u < ND;
 
-    // ---- compose: X_u = Sgrp slice (w + 4u) A + Bt slice, A streamed tile by tile
+    // ---- compose: X_u = Sgrp slice (w + 4u) A + Bt slice, A streamed tile by tile (or,
+    //      after a true-start frame-maps pass, X_u = Bt slice: the B map is the state)
     f32x4 X[NSL][ND];
+    if (a.b_is_state) {
+        const float* bt = a.Bt + unit * (ND * ND * 256);
+#pragma unroll
+        for (int u = 0; u < NSL; ++u) {
+            const int sl = own[u] ? w + 4 * u : 0;
+#pragma unroll
+            for (int t = 0; t < ND; ++t) X[u][t] = *(const f32x4*)(bt + ((long long)sl * ND + t) * 256 + lane * 4);
+        }
+    } else {
 #pragma unroll
     for (int u = 0; u < NSL; ++u) {
         const int sl = own[u] ? w + 4 * u : 0;
@@ -1169,6 +1196,7 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
                 X[u][t] = acc;
             }
         }
+    }
     }
     // S_f slices as readout A fragments (hi, lo): slot (g, j) of k block kb holds
     // S[16 s + c][32 kb + 4g + j] (j < 4), S[16 s + c][32 kb + 16 + 4g + j - 4] (j >= 4)
@@ -1269,8 +1297,10 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
     using LT = P1<E, ND, true>;
     static bool attr_done = false;  // per instantiation
     if (!attr_done) {
-        const void* aff[4] = {(const void*)gdn_frame_affine<E, ND, 0>, (const void*)gdn_frame_affine<E, ND, 1>,
-                              (const void*)gdn_frame_affine<E, ND, 2>, (const void*)gdn_frame_affine<E, ND, 3>};
+        const void* aff[8] = {(const void*)gdn_frame_affine<E, ND, 0>, (const void*)gdn_frame_affine<E, ND, 1>,
+                              (const void*)gdn_frame_affine<E, ND, 2>, (const void*)gdn_frame_affine<E, ND, 3>,
+                              (const void*)gdn_frame_affine<E, ND, 4>, (const void*)gdn_frame_affine<E, ND, 5>,
+                              (const void*)gdn_frame_affine<E, ND, 6>, (const void*)gdn_frame_affine<E, ND, 7>};
         const void* tok[4] = {(const void*)gdn_token_readout<E, ND, 0>, (const void*)gdn_token_readout<E, ND, 1>,
                               (const void*)gdn_token_readout<E, ND, 2>, (const void*)gdn_token_readout<E, ND, 3>};
         hipError_t e = hipSuccess;
@@ -1304,11 +1334,15 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
         const P1Args& p1 = *(const P1Args*)args;
         const int ngw = (p1.nf + p1.G - 1) / p1.G;
         const dim3 grid(ngw, BH);
-        switch (p1.flags & 3u) {
+        switch ((p1.flags & 3u) | (p1.true_start ? 4u : 0u)) {
         case 0: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 0>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
         case 1: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 1>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
         case 2: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 2>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
-        default: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 3>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        case 3: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 3>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        case 4: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 4>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        case 5: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 5>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        case 6: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 6>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
+        default: hipLaunchKernelGGL((gdn_frame_affine<E, ND, 7>), grid, dim3(L::NT), L::LDS_B, st, p1); break;
         }
     } else if (phase == 1) {
         constexpr int lds2 = P2<E, ND>::LDS_B;

@@ -35,6 +35,10 @@ struct P1Args {
     void* out;
     const float* Sgrp;  // state before each group of the window [BH, groups, d, d], or NULL
     int out_f32;
+    // one-group calls: the start state is Sgrp (state_in, or NULL = zero), the frame maps
+    // pass runs in true-start mode, and the state after the group goes to state_out
+    int true_start;
+    float* state_out;
 };
 
 struct P2Args {
@@ -59,6 +63,7 @@ struct P3Args {
     int nf;
     int G;
     int out_f32;        // out is float32 (else the input dtype)
+    int b_is_state;     // the B maps are the true states (true-start frame maps): no compose
 };
 
 struct BC1Args {

@@ -252,3 +252,33 @@ def test_gdn_gate_logits(entry, dtype):
     r1 = check("out", out, ro, TOL[dtype])
     r2 = check("state", st, rs, TOL[dtype])
     say("  out err/rms=%.2e state err/rms=%.2e" % (r1, r2))
+
+
+@pytest.mark.parametrize("entry", ["frame", "readonly", "token"])
+@pytest.mark.parametrize("group", ["1", "4000"])
+def test_gdn_group_paths(entry, group, monkeypatch):
+    """Both organisations of a call: one frame per group (maps, chain over groups, readout)
+    and a single group per (b, h) (maps from the known start state, no chain)."""
+    monkeypatch.setenv("GDN_GROUP_FRAMES", group)
+    F, N = 5, 100
+    inp = gdn_inputs(2, 2, F, N, 112, workload_id=370, state_std=0.2, gates="near_one")
+    dv = to_dev(inp)
+    say("case groups=%s entry=%s" % (group, entry))
+    s = dv["state_in"].clone()
+    if entry == "readonly":
+        out = gdn.frame_forward_readonly(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], F, N, state_in=s,
+                                         out_dtype=torch.float32)
+        st = None
+    else:
+        fn = gdn.token_forward if entry == "token" else gdn.frame_forward
+        out, st = fn(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], F, N, state_in=s, state_out=s,
+                     out_dtype=torch.float32)  # state updated in place
+    torch.cuda.synchronize()
+    nf, fl = (F * N, 1) if entry == "token" else (F, N)
+    ro, rs = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], nf, fl,
+                                state_in=inp["state_in"])
+    check("out", out, ro, 2e-2)
+    if st is not None:
+        check("state", s, rs, 2e-2)
+    else:
+        assert torch.equal(s, dv["state_in"]), "read-only call wrote the state"
