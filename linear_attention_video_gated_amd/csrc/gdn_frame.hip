@@ -12,12 +12,16 @@
 //     its WY/UT factors (Gram matrix K K^T, unit-lower-triangular inverse T = (I + L)^-1,
 //     W and U) on bf16 matrix cores with fp32 accumulation, and is applied to a stacked
 //     state [A ; B] that starts at [I ; 0] at the group start.  At every frame end the
-//     partial map (A_{g,<=f}, B_{g,<=f}) of the group so far is written out.
-//  2. gdn_frame_chain   -- one wave per (b, h, 16-row slice of S): the serial part, one
-//     d x d product per GROUP:  S_g = S_{g-1} A_g + B_g.  Writes the state before every
-//     group and the final state.
+//     partial map (A_{g,<=f}, B_{g,<=f}) of the group so far is written out.  With a
+//     single group per (b, h) the start state is known and the pass runs from it (true
+//     start: B only, the B maps are the states).
+//  2. gdn_frame_chain   -- one 4-wave workgroup per (b, h, 4 row slices of S): the serial
+//     part, one d x d product per GROUP:  S_g = S_{g-1} A_g + B_g.  Writes the state
+//     before every group and the final state.
 //  3. gdn_frame_readout -- one workgroup per (b, h, frame): composes
 //     S_f = S_{g-1} A_{g,<=f} + B_{g,<=f}, then streams Q in and O = Q S_f^T out.
+//     For the per-token readout the third launch is gdn_token_readout instead: the same
+//     chunk pipeline rerun from each group's true start state, writing o_t = S_t q_t.
 // Chunk algebra (derivation from the recurrence, restated; G_t = sum_{i<=t} log a_i in
 // the chunk, k^ the normalised keys):
 //   L_ti = b_t e^{G_t - G_i} k^_t.k^_i (i < t),  T = (I + L)^-1,
@@ -28,8 +32,8 @@
 // Precision (bf16 inputs).  Inputs q, k, v are exact bf16 operands.  Quantities that carry
 // the state (the chunk innovation Kt-scaled (U - W S^T), the maps A and the states S) are
 // sent to the matrix cores as bf16 hi + lo pairs, which keeps ~16 significant bits; W and
-// U are formed in correction form, X = R + Y with Y = (T_II - I) R_I - T_II sum_J L_IJ X_J,
-// so only the small correction Y is rounded.
+// U are formed block by block as X_I = Z_I + (T_II - I) Z_I with Z_I = R_I - sum_{J<I}
+// L_IJ X_J kept in fp32, so only the operand of the correction (T_II - I) Z_I is rounded.
 #include "common.hpp"
 #include "gdn_kernels.hpp"
 #include <float.h>
@@ -44,9 +48,9 @@ namespace gdn {
 // tile w and U column tile w, then the state update.  The prep waves prepare chunks
 // ahead: key norms, gate prefix, Gram matrix, scaled L, inverses of the 16x16 diagonal
 // blocks of (I + L), and the bf16 operand fragments the substitution consumes.
-//  - OV (bf16 where the buffers fit in LDS): two prep waves, which also issue every
-//    global -> LDS copy so that the chain waves never stall on the memory pipeline; one
-//    barrier per chunk (schedule at the main loop).
+//  - OV (bf16 where the buffers fit in LDS): two prep waves and one barrier per chunk
+//    (schedule at the main loop); the global -> LDS copies are issued by the prep waves
+//    and the first four chain waves.
 //  - otherwise one prep wave and two barriers per chunk (bf16, d = 128), or the same
 //    stages one after the other on single buffers (fp32 inputs, whose buffers do not fit
 //    twice in LDS at d >= 112).

@@ -29,7 +29,7 @@
  *       delta rule recurrence):  S_t = a_t S_{t-1} (I - b_t k_t k_t^T)
  *       + b_t v_t k_t^T, with S of shape d_v x d_k and L2-normalised k.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - frame-wise readout: every token of frame f reads o_t = S_f q_t where S_f
  *    is the state after frame f's last token (bidirectional inside a frame,
  *    causal across frames), which is what [V]'s "block i uses S_i = S_{i-1} +
