@@ -239,7 +239,8 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // one or two issuing waves are far too slow, while all waves stall every chain wave;
     // chain waves 0..3 are the first of the two chain waves on their SIMD and finish their
     // chunk early, which hides their stall.
-    constexpr unsigned kCopy = L::OV ? (0xFu | (3u << ND)) : kAll;
+    // (at d = 16 the workgroup has three waves: the mask keeps to the waves that exist)
+    constexpr unsigned kCopy = L::OV ? ((0xFu | (3u << ND)) & kAll) : kAll;
     int ncopy = 0;  // copy instructions this wave issues per chunk
     for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
     if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
