@@ -256,8 +256,9 @@ def test_gdn_gate_logits(entry, dtype):
 
 @pytest.mark.parametrize("entry", ["frame", "readonly", "token"])
 @pytest.mark.parametrize("group", ["1", "4000"])
-@pytest.mark.parametrize("d,dtype", [(112, torch.bfloat16), (16, torch.bfloat16), (128, torch.bfloat16),
-                                     (32, torch.float32), (128, torch.float32)])
+@pytest.mark.parametrize("d,dtype", [(112, torch.bfloat16), (16, torch.bfloat16), (32, torch.bfloat16),
+                                     (64, torch.bfloat16), (128, torch.bfloat16), (16, torch.float32),
+                                     (32, torch.float32), (64, torch.float32), (128, torch.float32)])
 def test_gdn_group_paths(entry, group, d, dtype, monkeypatch):
     """Both organisations of a call: one frame per group (maps, chain over groups, readout)
     and a single group per (b, h) (maps from the known start state, no chain)."""
