@@ -32,8 +32,29 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) { return __builtin_convertvector(x, f16x4); }  // RNE
+
+// Stores through a raw buffer resource: address = base + soffset + voffset with base and
+// soffset uniform (SGPRs) and voffset the lane's byte offset, so that a run of stores to
+// different places shares one per-lane VGPR instead of a 64-bit address each.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+}
+template <typename V> __device__ __forceinline__ void buf_st(V x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (sizeof(V) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, voff, soff, 0);
+    else __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 0);
+}
+
+// maximum over the 64 lanes of a wave (every lane receives it)
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
 
 template <typename E> struct Ops;
 

@@ -723,11 +723,14 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     };
 
     // frame end: the partial map of the group so far.  B as accumulator tiles.  A goes out
-    // as the A operand of the map application (PAIR slot map over A's rows), hi then lo;
-    // that needs A's tiles transposed, which one K16 product with the identity does
-    // exactly (a bf16 or fp32 operand times 1, accumulated in fp32): it turns lane (c, g)
-    // into the owner of A[16w + 4g + i][16t + c], i.e. of 4 consecutive slots of its own
-    // fragment lane, written as one 8-byte piece.
+    // as the A operand of the map application (PAIR slot map over A's rows); that needs
+    // A's tiles transposed, which one K16 product with the identity does exactly (an
+    // operand times 1, accumulated in fp32): it turns lane (c, g) into the owner of
+    // A[16w + 4g + i][16t + c], i.e. of 4 consecutive slots of its own fragment lane,
+    // written as one piece.  Two copies of A: every frame's, for the readout (fp32
+    // inputs: fp32; bf16 inputs: fp16, this wave's rows scaled by a power of two that
+    // puts their largest magnitude in [2^14, 2^15), the exponent stored beside), and the
+    // group's last one, for the chain over groups (the operand dtype, bf16 as hi and lo).
     auto emit = [&](int fl, const f32x4 (&XA)[ND], const f32x4 (&XB)[ND]) {
         const long long unit = (long long)bh * a.nf + fw0 + fl;
         float* bt = a.Bt + unit * (ND * ND * 256) + (long long)w * ND * 256;
@@ -737,11 +740,13 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         f32x4 eye;
 #pragma unroll
         for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? 1.f : 0.f;
-        const F4 eyef = O::pack4(eye);
         const int kbw = w >> 1, half = w & 1;
-#pragma unroll
-        for (int part = 0; part < NS; ++part) {
-            E* ap = (E*)a.Apack + (unit * NS + part) * L::APK_E;
+        // this lane's piece of fragment (t, kbw): element offset (t KB + kbw) 512 + fo
+        const int fo = lane * 8 + 4 * half;
+        const bool pad = (ND & 1) && w == ND - 1;  // also zero the slots of rows past d_k
+        auto put = [&](E* ap, int part) {          // part 1: the lo set of a bf16 split
+            const F4 eyef = O::pack4(eye);
+            const auto r = buf_rsrc(ap);
 #pragma unroll
             for (int t = 0; t < ND; ++t) {
                 f32x4 x = XA[t];
@@ -750,10 +755,41 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     for (int i = 0; i < 4; ++i) x[i] = O::lo_of(x[i]);
                 }
                 const f32x4 xt = O::mma16(O::pack4(x), eyef, zero4());
-                E* frg = ap + ((t * KB + kbw) * 64 + lane) * 8;
-                O::st4(frg + 4 * half, xt);
-                if ((ND & 1) && w == ND - 1) O::st4(frg + 4, zero4());  // rows past d_k
+                const int so = (t * KB + kbw) * 512 * (int)sizeof(E);
+                buf_st(O::pack4(xt), r, fo * (int)sizeof(E), so);
+                if (pad) buf_st(O::pack4(zero4()), r, (fo + 4) * (int)sizeof(E), so);
             }
+        };
+        if (a.emit_all) {
+            if constexpr (L::BF) {
+                float m = 0.f;
+#pragma unroll
+                for (int t = 0; t < ND; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(XA[t][i]));
+                m = wave_max(m);
+                const int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+                const f16x4 eyeh = to_f16x4(eye);
+                const auto r = buf_rsrc((_Float16*)a.Afr + unit * L::APK_E);
+#pragma unroll
+                for (int t = 0; t < ND; ++t) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_ldexpf(XA[t][i], -e);
+                    const f32x4 xt = __builtin_amdgcn_mfma_f32_16x16x16f16(to_f16x4(x), eyeh, zero4(), 0, 0, 0);
+                    const int so = (t * KB + kbw) * 512 * 2;
+                    buf_st(to_f16x4(xt), r, fo * 2, so);
+                    if (pad) buf_st(to_f16x4(zero4()), r, (fo + 4) * 2, so);
+                }
+                if (lane == 0) a.Aexp[unit * 8 + w] = e;
+            } else {
+                put((E*)a.Afr + unit * L::APK_E, 0);
+            }
+        }
+        if (fl == nfg - 1) {
+            const long long grp = (long long)bh * ((a.nf + a.G - 1) / a.G) + gi;
+#pragma unroll
+            for (int part = 0; part < NS; ++part) put((E*)a.Agr + (grp * NS + part) * L::APK_E, part);
         }
     };
 
@@ -1039,7 +1075,7 @@ __global__ __launch_bounds__(256, 1) void gdn_frame_chain(P2Args a) {
 
     u32x4 pa[P::NV];
     auto loadA = [&](int gi) {
-        const u32x4* src = (const u32x4*)((const E*)a.Apack + unit_of(gi) * NS * APK_E);
+        const u32x4* src = (const u32x4*)((const E*)a.Agr + ((long long)bh * ngw + gi) * NS * APK_E);
 #pragma unroll
         for (int k = 0; k < P::NV; ++k)
             if (tid + 256 * k < P::TOTV) pa[k] = src[tid + 256 * k];
@@ -1164,6 +1200,19 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
 #pragma unroll
         for (int t = 0; t < ND; ++t) X[u][t] = a.Sgrp ? *(const f32x4*)(sg + 16 * t + 4 * g) : zero4();
     }
+    if constexpr (O::kSplit) {
+        // bf16 inputs: row slice t of the stored map is A's rows 16t.. scaled by 2^-e_t, so
+        // the columns 16t.. of S (the same k_in) are scaled by 2^e_t
+        const int* ex = a.Aexp + unit * 8;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+            const int e = ex[t];
+#pragma unroll
+            for (int u = 0; u < NSL; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[u][t][i] = __builtin_amdgcn_ldexpf(X[u][t][i], e);
+        }
+    }
     F8 xh[NSL][KB], xl[NSL][KB];
 #pragma unroll
     for (int u = 0; u < NSL; ++u)
@@ -1171,7 +1220,6 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
         for (int kb = 0; kb < KB; ++kb)
             O::split8(X[u][2 * kb], (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4(), xh[u][kb], xl[u][kb]);
     {
-        const E* ah = (const E*)a.Apack + unit * NS * APK_E;
         const float* bt = a.Bt + unit * (ND * ND * 256);
 #pragma unroll
         for (int t = 0; t < ND; ++t) {
@@ -1179,8 +1227,16 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const int off = ((t * KB + kb) * 64 + lane) * 8;
-                fh[kb] = O::ld8(ah + off);
-                fl[kb] = O::kSplit ? O::ld8(ah + APK_E + off) : O::zero8();
+                if constexpr (O::kSplit) {
+                    // fp16 (11 significant bits) -> a bf16 hi + lo pair, exactly
+                    const f16x8 h = *(const f16x8*)((const _Float16*)a.Afr + unit * APK_E + off);
+                    O::split8(__builtin_convertvector(__builtin_shufflevector(h, h, 0, 1, 2, 3), f32x4),
+                              __builtin_convertvector(__builtin_shufflevector(h, h, 4, 5, 6, 7), f32x4), fh[kb],
+                              fl[kb]);
+                } else {
+                    fh[kb] = O::ld8((const E*)a.Afr + unit * APK_E + off);
+                    fl[kb] = O::zero8();
+                }
             }
 #pragma unroll
             for (int u = 0; u < NSL; ++u) {
@@ -1362,13 +1418,14 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
 GDN_INST(bf16, 1) GDN_INST(bf16, 2) GDN_INST(bf16, 4) GDN_INST(bf16, 7) GDN_INST(bf16, 8)
 GDN_INST(float, 1) GDN_INST(float, 2) GDN_INST(float, 4) GDN_INST(float, 7) GDN_INST(float, 8)
 
-size_t gdn_unit_bytes(int nd, int esize, size_t* apack, size_t* bt, size_t* sgrp) {
-    const int kb = (nd + 1) / 2;
-    const int nsplit = esize == 2 ? 2 : 1;  // bf16 operands are stored as hi + lo
-    *apack = (size_t)nsplit * nd * kb * 64 * 8 * esize;
+void gdn_region_bytes(int nd, int esize, size_t* afr, size_t* aexp, size_t* bt, size_t* agr, size_t* sgrp) {
+    const size_t frag = (size_t)nd * ((nd + 1) / 2) * 64 * 8;  // elements of one set of A fragments
+    const bool bf = esize == 2;
+    *afr = frag * (bf ? 2 : 4);               // fp16 (bf16 inputs) or fp32
+    *aexp = bf ? 8 * sizeof(int) : 0;
     *bt = (size_t)nd * nd * 256 * 4;
-    *sgrp = (size_t)16 * nd * 16 * nd * 4;  // a d x d fp32 state, per group
-    return *apack + *bt + *sgrp;
+    *agr = frag * esize * (bf ? 2 : 1);       // bf16 operands are stored as hi + lo
+    *sgrp = (size_t)16 * nd * 16 * nd * 4;    // a d x d fp32 state
 }
 
 }  // namespace gdn

@@ -1,11 +1,17 @@
 // gdn_kernels.hpp -- argument blocks and launcher declarations shared by the kernel
 // sources and the C ABI layer.  Workspace formats (per (b, h, frame) "unit", frames of
-// one window stored contiguously per (b, h)):
-//   Apack  A_f^T as K32 A-operand fragments, PAIR slot map over k_in: ND x KB fragments
-//          of 64 lanes x 8 elements (dtype of the inputs); for bf16 a hi set then a lo set.
-//   Bt     B_f as accumulator tiles: ND slices x ND tiles x 64 lanes x 4 fp32.
+// one window stored contiguously per (b, h); per (b, h, group) likewise):
+//   Afr    per unit, the frame's A map for the readout: A_f^T as K32 A-operand
+//          fragments, PAIR slot map over k_in, ND x KB fragments of 64 lanes x 8
+//          elements.  fp32 inputs: fp32.  bf16 inputs: fp16, row slice w of A (rows
+//          16w..16w+15, the k_in of the map) scaled by 2^-Aexp[w] so that its largest
+//          magnitude lies in [2^14, 2^15).
+//   Aexp   per unit (bf16 inputs), 8 ints: the exponents of the row slices of Afr.
+//   Bt     per unit, B_f as accumulator tiles: ND slices x ND tiles x 64 lanes x 4 fp32.
 //   (A_f, B_f) of a frame is the partial map of its group up to that frame's end.
-//   Sgrp   the state before each group of frames, fp32 [d_v][d_k] row-major.
+//   Agr    per group, the group's whole map A for the chain over groups: the fragments of
+//          Afr in the dtype of the inputs; for bf16 a hi set then a lo set.
+//   Sgrp   per group, the state before the group, fp32 [d_v][d_k] row-major.
 //   BCpart block-causal per-frame sums phi(K)^T [V | 1]: ND x (ND+1) accumulator tiles.
 //   BCpack block-causal S_f^T and z_f as K32 A-operand fragments: (ND+1) x KB fragments
 //          (bf16: hi set then lo set).
@@ -27,7 +33,7 @@ struct P1Args {
     int G;              // frames per group
     int BH;
     unsigned flags;     // bit 0: normalise k, bit 1: additive
-    void* Apack;        // partial maps A of every frame of the window
+    void* Agr;          // whole-group maps A (chain operand)
     float* Bt;          // partial maps B
     int emit_all;       // maps at every frame end (else only at each group's last frame)
     // per-token readout pass only:
@@ -39,10 +45,13 @@ struct P1Args {
     // pass runs in true-start mode, and the state after the group goes to state_out
     int true_start;
     float* state_out;
+    // frame mode: the readout's per-frame A maps and, for bf16, their slice exponents
+    void* Afr;
+    int* Aexp;
 };
 
 struct P2Args {
-    const void* Apack;
+    const void* Agr;
     const float* Bt;
     const float* state_src;  // [BH, d, d] or NULL (zero state)
     float* state_dst;        // [BH, d, d] or NULL
@@ -54,7 +63,8 @@ struct P2Args {
 struct P3Args {
     const void* q;
     void* out;
-    const void* Apack;
+    const void* Afr;
+    const int* Aexp;
     const float* Bt;
     const float* Sgrp;  // state before each group, or NULL for a zero state
     long long T;
@@ -116,7 +126,8 @@ inline hipError_t record(void* const* ev, int i, hipStream_t st) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
 }
 
-size_t gdn_unit_bytes(int nd, int esize, size_t* apack, size_t* bt, size_t* sgrp);
+// bytes per unit (afr, aexp, bt) and per group (agr, sgrp) of the workspace regions
+void gdn_region_bytes(int nd, int esize, size_t* afr, size_t* aexp, size_t* bt, size_t* agr, size_t* sgrp);
 size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack);
 
 }  // namespace gdn
