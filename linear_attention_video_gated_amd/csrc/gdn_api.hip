@@ -76,7 +76,9 @@ int esize_of(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
 struct Plan {
     long long BH = 0, T = 0;
     int nd = 0, es = 0, nfw = 0, nwin = 0, G = 1;
-    size_t off_a = 0, off_x = 0, off_b = 0, off_g = 0, off_c = 0, off_carry = 0, total = 0;
+    // block-causal: off_a per-frame sums, off_c prefix operands; gated delta rule: the
+    // regions of GdnRegions
+    size_t off_a = 0, off_b = 0, off_x = 0, off_ga = 0, off_gb = 0, off_c = 0, off_carry = 0, total = 0;
 };
 
 int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
@@ -106,22 +108,25 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
     p->nfw = (int)nfw;
     p->nwin = (int)((d->n_frames + nfw - 1) / nfw);
     const size_t units = (size_t)p->BH * (size_t)nfw;
-    size_t a = 0, x = 0, b = 0, ag = 0, c = 0, carry = 0, groups = units;
+    size_t carry = 0;
+    GdnRegions r{0, 0, 0, 0, 0, 0};
+    size_t groups = 0;
     if (bc) {
-        bc_unit_bytes(p->nd, p->es, &a, &c);
+        bc_unit_bytes(p->nd, p->es, &r.afr, &r.sgrp);
         carry = (size_t)p->BH * p->nd * (p->nd + 1) * 256 * 4;
+        groups = units;
     } else {
-        // per unit: readout maps, their exponents, B maps; per group: chain maps, states
-        gdn_region_bytes(p->nd, p->es, &a, &x, &b, &ag, &c);
+        r = gdn_region_bytes(p->nd, p->es);
         carry = (size_t)p->BH * d->d_k * d->d_v * 4;
         groups = (size_t)p->BH * ((p->nfw + p->G - 1) / p->G);
     }
     p->off_a = 0;
-    p->off_x = align_up(units * a);
-    p->off_b = p->off_x + align_up(units * x);
-    p->off_g = p->off_b + align_up(units * b);
-    p->off_c = p->off_g + align_up(groups * ag);
-    p->off_carry = p->off_c + align_up(groups * c);
+    p->off_b = align_up(units * r.afr);
+    p->off_x = p->off_b + align_up(units * r.bfr);
+    p->off_ga = p->off_x + align_up(units * r.xexp);
+    p->off_gb = p->off_ga + align_up(groups * r.agr);
+    p->off_c = p->off_gb + align_up(groups * r.bgr);
+    p->off_carry = p->off_c + align_up(groups * r.sgrp);
     p->total = p->off_carry + (p->nwin > 1 ? align_up(carry) : 0);
     return GDN_OK;
 }
@@ -158,9 +163,10 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
     float* carry = (float*)(ws + p.off_carry);
     const int BH = (int)p.BH;
     void* afr = ws + p.off_a;
-    int* aexp = (int*)(ws + p.off_x);
-    float* bt = (float*)(ws + p.off_b);
-    void* agr = ws + p.off_g;
+    void* bfr = ws + p.off_b;
+    int* xexp = (int*)(ws + p.off_x);
+    void* agr = ws + p.off_ga;
+    float* bgr = (float*)(ws + p.off_gb);
     float* sgrp = (float*)(ws + p.off_c);
     for (int wi = 0; wi < p.nwin; ++wi) {
         const int f0 = wi * p.nfw;
@@ -174,13 +180,13 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         const bool single = p.nwin == 1 && nf <= p.G;
         const float* s_before = single ? state_in : sgrp;
         const int of32 = (d->flags & GDN_F_OUT_F32) ? 1 : 0;
-        const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, agr, bt,
+        const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, agr, bgr,
                         tok ? 0 : 1, nullptr, nullptr, single ? state_in : nullptr, 0, single ? 1 : 0,
-                        single ? state_out : nullptr, afr, aexp};
+                        single ? state_out : nullptr, afr, bfr, xexp};
         const P1Args a3t{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, nullptr, nullptr,
-                         0, q, out, s_before, of32, 0, single ? state_out : nullptr, nullptr, nullptr};
-        const P2Args a2{agr, bt, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
-        const P3Args a3{q, out, afr, aexp, bt, single ? nullptr : sgrp, p.T, d->frame_len, f0, nf, p.G, of32,
+                         0, q, out, s_before, of32, 0, single ? state_out : nullptr, nullptr, nullptr, nullptr};
+        const P2Args a2{agr, bgr, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
+        const P3Args a3{q, out, afr, bfr, xexp, single ? nullptr : sgrp, p.T, d->frame_len, f0, nf, p.G, of32,
                         single ? 1 : 0};
         void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
         if (tok && single) {  // the readout pass alone

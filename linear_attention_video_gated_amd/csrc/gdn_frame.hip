@@ -722,20 +722,53 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         }
     };
 
-    // frame end: the partial map of the group so far.  B as accumulator tiles.  A goes out
-    // as the A operand of the map application (PAIR slot map over A's rows); that needs
-    // A's tiles transposed, which one K16 product with the identity does exactly (an
-    // operand times 1, accumulated in fp32): it turns lane (c, g) into the owner of
-    // A[16w + 4g + i][16t + c], i.e. of 4 consecutive slots of its own fragment lane,
-    // written as one piece.  Two copies of A: every frame's, for the readout (fp32
-    // inputs: fp32; bf16 inputs: fp16, this wave's rows scaled by a power of two that
-    // puts their largest magnitude in [2^14, 2^15), the exponent stored beside), and the
-    // group's last one, for the chain over groups (the operand dtype, bf16 as hi and lo).
+    // frame end: the partial map of the group so far, in two copies -- every frame's, for
+    // the readout, and the group's last one, for the chain over groups.  The readout's
+    // copy is fp32 for fp32 inputs; for bf16 inputs it is fp16, this wave's rows (of A and
+    // of B) scaled by a power of two that puts their largest magnitude in [2^14, 2^15),
+    // the exponent stored beside.  The chain's copy is fp32 for B and the operand dtype
+    // for A (bf16 as hi and lo).  B goes out as accumulator tiles, A as the A operand of
+    // the map application (PAIR slot map over A's rows); that needs A's tiles
+    // transposed, which one K16 product with the identity does exactly (an operand times
+    // 1, accumulated in fp32): it turns lane (c, g) into the owner of A[16w + 4g + i][16t
+    // + c], i.e. of 4 consecutive slots of its own fragment lane, written as one piece.
+    auto slice_exp = [&](const f32x4 (&X)[ND]) {  // exponent e: max |X 2^-e| in [2^14, 2^15)
+        float m = 0.f;
+#pragma unroll
+        for (int t = 0; t < ND; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(X[t][i]));
+        m = wave_max(m);
+        return m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+    };
     auto emit = [&](int fl, const f32x4 (&XA)[ND], const f32x4 (&XB)[ND]) {
         const long long unit = (long long)bh * a.nf + fw0 + fl;
-        float* bt = a.Bt + unit * (ND * ND * 256) + (long long)w * ND * 256;
+        const long long grp = (long long)bh * ((a.nf + a.G - 1) / a.G) + gi;
+        const bool last = fl == nfg - 1 && !TS;  // the group's map, for the chain
+        const int bso = w * ND * 256;            // this wave's B tiles (elements)
+        if (a.emit_all) {
+            if constexpr (L::BF) {
+                const int e = slice_exp(XB);
+                const auto r = buf_rsrc((_Float16*)a.Bfr + unit * (ND * ND * 256));
 #pragma unroll
-        for (int t = 0; t < ND; ++t) *(f32x4*)(bt + t * 256 + lane * 4) = XB[t];
+                for (int t = 0; t < ND; ++t) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_ldexpf(XB[t][i], -e);
+                    buf_st(to_f16x4(x), r, lane * 8, (bso + t * 256) * 2);
+                }
+                if (lane == 0) a.Xexp[unit * 16 + 8 + w] = e;
+            } else {
+                const auto r = buf_rsrc((float*)a.Bfr + unit * (ND * ND * 256));
+#pragma unroll
+                for (int t = 0; t < ND; ++t) buf_st(XB[t], r, lane * 16, (bso + t * 256) * 4);
+            }
+        }
+        if (last) {
+            const auto r = buf_rsrc(a.Bgr + grp * (ND * ND * 256));
+#pragma unroll
+            for (int t = 0; t < ND; ++t) buf_st(XB[t], r, lane * 16, (bso + t * 256) * 4);
+        }
         if constexpr (TS) return;  // B is the true state: no A map
         f32x4 eye;
 #pragma unroll
@@ -762,13 +795,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         };
         if (a.emit_all) {
             if constexpr (L::BF) {
-                float m = 0.f;
-#pragma unroll
-                for (int t = 0; t < ND; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(XA[t][i]));
-                m = wave_max(m);
-                const int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+                const int e = slice_exp(XA);
                 const f16x4 eyeh = to_f16x4(eye);
                 const auto r = buf_rsrc((_Float16*)a.Afr + unit * L::APK_E);
 #pragma unroll
@@ -781,13 +808,12 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     buf_st(to_f16x4(xt), r, fo * 2, so);
                     if (pad) buf_st(to_f16x4(zero4()), r, (fo + 4) * 2, so);
                 }
-                if (lane == 0) a.Aexp[unit * 8 + w] = e;
+                if (lane == 0) a.Xexp[unit * 16 + w] = e;
             } else {
                 put((E*)a.Afr + unit * L::APK_E, 0);
             }
         }
-        if (fl == nfg - 1) {
-            const long long grp = (long long)bh * ((a.nf + a.G - 1) / a.G) + gi;
+        if (last) {
 #pragma unroll
             for (int part = 0; part < NS; ++part) put((E*)a.Agr + (grp * NS + part) * L::APK_E, part);
         }
@@ -1071,7 +1097,6 @@ __global__ __launch_bounds__(256, 1) void gdn_frame_chain(P2Args a) {
     const bool active = s < ND;
     const int bh = blockIdx.y;
     const int ngw = (a.nf + a.G - 1) / a.G;
-    auto unit_of = [&](int gi) { return (long long)bh * a.nf + min(gi * a.G + a.G, a.nf) - 1; };  // group end
 
     u32x4 pa[P::NV];
     auto loadA = [&](int gi) {
@@ -1089,7 +1114,7 @@ __global__ __launch_bounds__(256, 1) void gdn_frame_chain(P2Args a) {
     f32x4 bt[ND], btn[ND];
     auto loadB = [&](int gi, f32x4 (&b)[ND]) {
         if (!active) return;
-        const float* p = a.Bt + unit_of(gi) * (ND * ND * 256) + (long long)s * ND * 256;
+        const float* p = a.Bgr + ((long long)bh * ngw + gi) * (ND * ND * 256) + (long long)s * ND * 256;
 #pragma unroll
         for (int t = 0; t < ND; ++t) b[t] = *(const f32x4*)(p + t * 256 + lane * 4);
     };
@@ -1181,16 +1206,29 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
 #pragma unroll
     for (int u = 0; u < NSL; ++u) own[u] = w + 4 * u < ND;
 
-    // ---- compose: X_u = Sgrp slice (w + 4u) A + Bt slice, A streamed tile by tile (or,
-    //      after a true-start frame-maps pass, X_u = Bt slice: the B map is the state)
+    // ---- compose: X_u = Sgrp slice (w + 4u) A + B slice, A streamed tile by tile (or,
+    //      after a true-start frame-maps pass, X_u = B slice: the B map is the state).
+    //      bf16 inputs: the stored maps are fp16 with each row slice scaled by 2^-e (A's
+    //      exponents in Xexp[0..8), B's in Xexp[8..16)).
+    const int* ex = O::kSplit ? a.Xexp + unit * 16 : nullptr;
+    auto ldB = [&](int sl, int t) -> f32x4 {  // tile t of row slice sl of B
+        const long long o = unit * (ND * ND * 256) + ((long long)sl * ND + t) * 256 + lane * 4;
+        if constexpr (O::kSplit) {
+            const f32x4 x = __builtin_convertvector(*(const f16x4*)((const _Float16*)a.Bfr + o), f32x4);
+            const int e = ex[8 + sl];
+            return f32x4{__builtin_amdgcn_ldexpf(x[0], e), __builtin_amdgcn_ldexpf(x[1], e),
+                         __builtin_amdgcn_ldexpf(x[2], e), __builtin_amdgcn_ldexpf(x[3], e)};
+        } else {
+            return *(const f32x4*)((const float*)a.Bfr + o);
+        }
+    };
     f32x4 X[NSL][ND];
     if (a.b_is_state) {
-        const float* bt = a.Bt + unit * (ND * ND * 256);
 #pragma unroll
         for (int u = 0; u < NSL; ++u) {
             const int sl = own[u] ? w + 4 * u : 0;
 #pragma unroll
-            for (int t = 0; t < ND; ++t) X[u][t] = *(const f32x4*)(bt + ((long long)sl * ND + t) * 256 + lane * 4);
+            for (int t = 0; t < ND; ++t) X[u][t] = ldB(sl, t);
         }
     } else {
 #pragma unroll
@@ -1201,9 +1239,8 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
         for (int t = 0; t < ND; ++t) X[u][t] = a.Sgrp ? *(const f32x4*)(sg + 16 * t + 4 * g) : zero4();
     }
     if constexpr (O::kSplit) {
-        // bf16 inputs: row slice t of the stored map is A's rows 16t.. scaled by 2^-e_t, so
-        // the columns 16t.. of S (the same k_in) are scaled by 2^e_t
-        const int* ex = a.Aexp + unit * 8;
+        // row slice t of the stored A is A's rows 16t.. scaled by 2^-e_t, so the columns
+        // 16t.. of S (the same k_in) are scaled by 2^e_t
 #pragma unroll
         for (int t = 0; t < ND; ++t) {
             const int e = ex[t];
@@ -1219,39 +1256,34 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             O::split8(X[u][2 * kb], (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4(), xh[u][kb], xl[u][kb]);
-    {
-        const float* bt = a.Bt + unit * (ND * ND * 256);
 #pragma unroll
-        for (int t = 0; t < ND; ++t) {
-            F8 fh[KB], fl[KB];
+    for (int t = 0; t < ND; ++t) {
+        F8 fh[KB], fl[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int off = ((t * KB + kb) * 64 + lane) * 8;
+            if constexpr (O::kSplit) {
+                // fp16 (11 significant bits) -> a bf16 hi + lo pair, exactly
+                const f16x8 h = *(const f16x8*)((const _Float16*)a.Afr + unit * APK_E + off);
+                O::split8(__builtin_convertvector(__builtin_shufflevector(h, h, 0, 1, 2, 3), f32x4),
+                          __builtin_convertvector(__builtin_shufflevector(h, h, 4, 5, 6, 7), f32x4), fh[kb], fl[kb]);
+            } else {
+                fh[kb] = O::ld8((const E*)a.Afr + unit * APK_E + off);
+                fl[kb] = O::zero8();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NSL; ++u) {
+            f32x4 acc = ldB(own[u] ? w + 4 * u : 0, t);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int off = ((t * KB + kb) * 64 + lane) * 8;
-                if constexpr (O::kSplit) {
-                    // fp16 (11 significant bits) -> a bf16 hi + lo pair, exactly
-                    const f16x8 h = *(const f16x8*)((const _Float16*)a.Afr + unit * APK_E + off);
-                    O::split8(__builtin_convertvector(__builtin_shufflevector(h, h, 0, 1, 2, 3), f32x4),
-                              __builtin_convertvector(__builtin_shufflevector(h, h, 4, 5, 6, 7), f32x4), fh[kb],
-                              fl[kb]);
-                } else {
-                    fh[kb] = O::ld8((const E*)a.Afr + unit * APK_E + off);
-                    fl[kb] = O::zero8();
+                acc = O::mma32(fh[kb], xh[u][kb], acc);
+                if (O::kSplit) {
+                    acc = O::mma32(fl[kb], xh[u][kb], acc);
+                    acc = O::mma32(fh[kb], xl[u][kb], acc);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < NSL; ++u) {
-                const int sl = own[u] ? w + 4 * u : 0;
-                f32x4 acc = *(const f32x4*)(bt + ((long long)sl * ND + t) * 256 + lane * 4);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    acc = O::mma32(fh[kb], xh[u][kb], acc);
-                    if (O::kSplit) {
-                        acc = O::mma32(fl[kb], xh[u][kb], acc);
-                        acc = O::mma32(fh[kb], xl[u][kb], acc);
-                    }
-                }
-                X[u][t] = acc;
-            }
+            X[u][t] = acc;
         }
     }
     }
@@ -1418,14 +1450,18 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
 GDN_INST(bf16, 1) GDN_INST(bf16, 2) GDN_INST(bf16, 4) GDN_INST(bf16, 7) GDN_INST(bf16, 8)
 GDN_INST(float, 1) GDN_INST(float, 2) GDN_INST(float, 4) GDN_INST(float, 7) GDN_INST(float, 8)
 
-void gdn_region_bytes(int nd, int esize, size_t* afr, size_t* aexp, size_t* bt, size_t* agr, size_t* sgrp) {
+GdnRegions gdn_region_bytes(int nd, int esize) {
     const size_t frag = (size_t)nd * ((nd + 1) / 2) * 64 * 8;  // elements of one set of A fragments
+    const size_t tiles = (size_t)nd * nd * 256;                // elements of the B tiles
     const bool bf = esize == 2;
-    *afr = frag * (bf ? 2 : 4);               // fp16 (bf16 inputs) or fp32
-    *aexp = bf ? 8 * sizeof(int) : 0;
-    *bt = (size_t)nd * nd * 256 * 4;
-    *agr = frag * esize * (bf ? 2 : 1);       // bf16 operands are stored as hi + lo
-    *sgrp = (size_t)16 * nd * 16 * nd * 4;    // a d x d fp32 state
+    GdnRegions r;
+    r.afr = frag * (bf ? 2 : 4);         // fp16 (bf16 inputs) or fp32
+    r.bfr = tiles * (bf ? 2 : 4);
+    r.xexp = bf ? 16 * sizeof(int) : 0;
+    r.agr = frag * esize * (bf ? 2 : 1);  // bf16 operands are stored as hi + lo
+    r.bgr = tiles * 4;
+    r.sgrp = (size_t)16 * nd * 16 * nd * 4;  // a d x d fp32 state
+    return r;
 }
 
 }  // namespace gdn

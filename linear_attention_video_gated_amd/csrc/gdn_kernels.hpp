@@ -4,13 +4,16 @@
 //   Afr    per unit, the frame's A map for the readout: A_f^T as K32 A-operand
 //          fragments, PAIR slot map over k_in, ND x KB fragments of 64 lanes x 8
 //          elements.  fp32 inputs: fp32.  bf16 inputs: fp16, row slice w of A (rows
-//          16w..16w+15, the k_in of the map) scaled by 2^-Aexp[w] so that its largest
+//          16w..16w+15, the k_in of the map) scaled by 2^-Xexp[w] so that its largest
 //          magnitude lies in [2^14, 2^15).
-//   Aexp   per unit (bf16 inputs), 8 ints: the exponents of the row slices of Afr.
-//   Bt     per unit, B_f as accumulator tiles: ND slices x ND tiles x 64 lanes x 4 fp32.
+//   Bfr    per unit, the frame's B map for the readout as accumulator tiles: ND slices x
+//          ND tiles x 64 lanes x 4 values.  fp32 inputs: fp32.  bf16 inputs: fp16, row
+//          slice w scaled by 2^-Xexp[8 + w] like Afr.
+//   Xexp   per unit (bf16 inputs), 16 ints: the slice exponents of Afr, then of Bfr.
 //   (A_f, B_f) of a frame is the partial map of its group up to that frame's end.
 //   Agr    per group, the group's whole map A for the chain over groups: the fragments of
 //          Afr in the dtype of the inputs; for bf16 a hi set then a lo set.
+//   Bgr    per group, the group's whole map B for the chain: the tiles of Bfr in fp32.
 //   Sgrp   per group, the state before the group, fp32 [d_v][d_k] row-major.
 //   BCpart block-causal per-frame sums phi(K)^T [V | 1]: ND x (ND+1) accumulator tiles.
 //   BCpack block-causal S_f^T and z_f as K32 A-operand fragments: (ND+1) x KB fragments
@@ -33,8 +36,8 @@ struct P1Args {
     int G;              // frames per group
     int BH;
     unsigned flags;     // bit 0: normalise k, bit 1: additive
-    void* Agr;          // whole-group maps A (chain operand)
-    float* Bt;          // partial maps B
+    void* Agr;          // whole-group maps A and B (chain operands)
+    float* Bgr;
     int emit_all;       // maps at every frame end (else only at each group's last frame)
     // per-token readout pass only:
     const void* q;
@@ -45,14 +48,15 @@ struct P1Args {
     // pass runs in true-start mode, and the state after the group goes to state_out
     int true_start;
     float* state_out;
-    // frame mode: the readout's per-frame A maps and, for bf16, their slice exponents
+    // frame mode: the readout's per-frame maps and, for bf16, their slice exponents
     void* Afr;
-    int* Aexp;
+    void* Bfr;
+    int* Xexp;
 };
 
 struct P2Args {
     const void* Agr;
-    const float* Bt;
+    const float* Bgr;
     const float* state_src;  // [BH, d, d] or NULL (zero state)
     float* state_dst;        // [BH, d, d] or NULL
     float* Sgrp;             // [BH, groups, d, d]: state before each group
@@ -64,8 +68,8 @@ struct P3Args {
     const void* q;
     void* out;
     const void* Afr;
-    const int* Aexp;
-    const float* Bt;
+    const void* Bfr;
+    const int* Xexp;
     const float* Sgrp;  // state before each group, or NULL for a zero state
     long long T;
     int frame_len;
@@ -126,8 +130,11 @@ inline hipError_t record(void* const* ev, int i, hipStream_t st) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
 }
 
-// bytes per unit (afr, aexp, bt) and per group (agr, sgrp) of the workspace regions
-void gdn_region_bytes(int nd, int esize, size_t* afr, size_t* aexp, size_t* bt, size_t* agr, size_t* sgrp);
+// bytes of the workspace regions: per unit (afr, bfr, xexp), per group (agr, bgr, sgrp)
+struct GdnRegions {
+    size_t afr, bfr, xexp, agr, bgr, sgrp;
+};
+GdnRegions gdn_region_bytes(int nd, int esize);
 size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack);
 
 }  // namespace gdn
