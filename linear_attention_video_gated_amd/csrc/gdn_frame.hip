@@ -244,6 +244,10 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // chunk early, which hides their stall.
     // (at d = 16 the workgroup has three waves: the mask keeps to the waves that exist)
     constexpr unsigned kCopy = L::OV ? ((0xFu | (3u << ND)) & kAll) : kAll;
+    // the per-token pass's loop likewise: chain waves 0..3 and the prep wave (the second
+    // chain wave on each SIMD finishes last and was measured stalling ~1,500 cycles per
+    // chunk on its share of the copies)
+    constexpr unsigned kCopyT = (TOK && L::PIPE) ? ((0xFu | (1u << ND)) & kAll) : kAll;
     int ncopy = 0;  // copy instructions this wave issues per chunk
     for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
     if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
@@ -853,9 +857,9 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             prep3(0);
             lds_barrier();  // chunk 0 prepared
             for (int q = 0; q < nq; ++q) {
-                if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kAll);
+                if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kCopyT);
                 if (q + 1 < nq) {
-                    dma_tiles(q + 1, 1, 2, false, kAll);
+                    dma_tiles(q + 1, 1, 2, false, kCopyT);
                     prep1(q + 1, gr, R);
                 }
                 aqk(q, ND, 1);  // the tiles past the chain waves' one each
@@ -974,8 +978,8 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 lds_barrier();
                 lds_barrier();
                 for (int q = 0; q < nq; ++q) {
-                    if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kAll);
-                    if (q + 1 < nq) dma_tiles(q + 1, 1, 2, false, kAll);
+                    if (q + 2 < nq) dma_tiles(q + 2, 0, 1, true, kCopyT);
+                    if (q + 1 < nq) dma_tiles(q + 1, 1, 2, false, kCopyT);
                     subst(q, Ur);
                     aqk(q, w, 10);
                     lds_barrier();  // B2
