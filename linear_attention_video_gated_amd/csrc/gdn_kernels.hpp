@@ -78,6 +78,8 @@ struct P3Args {
     int G;
     int out_f32;        // out is float32 (else the input dtype)
     int b_is_state;     // the B maps are the true states (true-start frame maps): no compose
+    int parts;          // workgroups per frame, each over a range of its 64-token chunks (set
+                        // by the launcher)
 };
 
 struct BC1Args {
