@@ -203,6 +203,19 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
 }
 // s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding: expcnt 7, lgkmcnt 15)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n): wait until at most n of the wave's vector memory operations are
+// outstanding (they complete in issue order); n wave-uniform, clamped to [0, 31]
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt and lgkmcnt left at their maximum)
+__device__ __forceinline__ void wait_vmem_le(int n) {
+    switch (n < 0 ? 0 : n > 31 ? 31 : n) {
+#define GDN_WV(N) case N: __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); break;
+        GDN_WV(0) GDN_WV(1) GDN_WV(2) GDN_WV(3) GDN_WV(4) GDN_WV(5) GDN_WV(6) GDN_WV(7)
+        GDN_WV(8) GDN_WV(9) GDN_WV(10) GDN_WV(11) GDN_WV(12) GDN_WV(13) GDN_WV(14) GDN_WV(15)
+        GDN_WV(16) GDN_WV(17) GDN_WV(18) GDN_WV(19) GDN_WV(20) GDN_WV(21) GDN_WV(22) GDN_WV(23)
+        GDN_WV(24) GDN_WV(25) GDN_WV(26) GDN_WV(27) GDN_WV(28) GDN_WV(29) GDN_WV(30) GDN_WV(31)
+#undef GDN_WV
+    }
+}
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits for every
 // outstanding global load and store of the wave, which would stall register prefetches

@@ -116,6 +116,7 @@ struct BC3Args {
     unsigned relu;
     float eps;
     int out_f32;
+    int parts;  // workgroups per frame (set by the launcher)
 };
 
 // Launchers.  ev: NULL, or the 6 events of one window -- recorded before and after each
