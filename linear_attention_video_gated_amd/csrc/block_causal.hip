@@ -88,10 +88,13 @@ __global__ __launch_bounds__(256, 2) void bc_partial(BC1Args a) {
                 kf[u] = __builtin_shufflevector(O::ldtr(kb, L::KPB, 32 * h, 16 * m, lane),
                                                 O::ldtr(kb, L::KPB, 32 * h + 16, 16 * m, lane), 0, 1, 2, 3, 4, 5,
                                                 6, 7);
+                if (a.relu) kf[u] = O::relu8(kf[u]);
+                if (Cc < 64) {  // tokens past the frame's end
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int tk = 32 * h + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                    if (tk >= Cc || (a.relu && !((float)kf[u][j] > 0.f))) kf[u][j] = (E)0.f;
+                    for (int j = 0; j < 8; ++j) {
+                        const int tk = 32 * h + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+                        if (tk >= Cc) kf[u][j] = (E)0.f;
+                    }
                 }
             }
 #pragma unroll
@@ -248,11 +251,7 @@ __global__ __launch_bounds__(256) void bc_readout(BC3Args a) {
             for (int kb = 0; kb < KB; ++kb) {
                 const int col = 32 * kb + 8 * g;
                 qb[kb] = col < D ? O::ld8((const E*)(qb0 + (16 * tl + c) * L::KPB) + col) : O::zero8();
-                if (a.relu) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (!((float)qb[kb][j] > 0.f)) qb[kb][j] = 0.f;
-                }
+                if (a.relu) qb[kb] = O::relu8(qb[kb]);
             }
             f32x4 den = zero4();
 #pragma unroll
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(256) void bc_readout(BC3Args a) {
                 if (O::kSplit) den = O::mma32(zl[kb], qb[kb], den);
             }
             const float dn = __shfl(den[0], c, 64) + a.eps;  // row 0 of the z tile, token c
-            const float inv = 1.f / dn;
+            const float inv = __builtin_amdgcn_rcpf(dn);  // hardware reciprocal, about 1 ulp
 #pragma unroll
             for (int u = 0; u < NSL; ++u) {
                 if (w + 4 * u >= ND) continue;

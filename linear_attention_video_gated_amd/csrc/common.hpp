@@ -113,6 +113,14 @@ template <> struct Ops<bf16> {
         lo = pack4(a - __builtin_convertvector(hi, f32x4));
     }
     static __device__ __forceinline__ float lo_of(float x) { return x - (float)(bf16)x; }
+    // ReLU of 8 values: a bf16 is sign-magnitude, so max(x, 0) is the signed 16-bit
+    // integer max of its bits with 0 (negative values and -0 become +0), two per
+    // v_pk_max_i16
+    static __device__ __forceinline__ F8 relu8(F8 x) {
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v = __builtin_bit_cast(s16x8, x);
+        return __builtin_bit_cast(F8, __builtin_elementwise_max(v, s16x8{0, 0, 0, 0, 0, 0, 0, 0}));
+    }
     // LDS transpose load (ds_read_b64_tr_b16): from a row-major 16-bit matrix M in LDS
     // (row pitch pb bytes), lane (c, g) receives M[r0 + 4g + i][c0 + c], i = 0..3 -- a K16
     // operand fragment whose k runs along M's rows.  In each 16-lane group, source lane s
@@ -173,6 +181,11 @@ template <> struct Ops<float> {
         lo = zero4();
     }
     static __device__ __forceinline__ float lo_of(float) { return 0.f; }
+    static __device__ __forceinline__ F8 relu8(F8 x) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = x[j] > 0.f ? x[j] : 0.f;
+        return x;
+    }
     // lane (c, g) receives M[r0 + 4g + i][c0 + c], i = 0..3 (plain loads for 32-bit data)
     static __device__ __forceinline__ F4 ldtr(const float* m, int pb, int r0, int c0, int lane) {
         const int c = lane & 15, g = lane >> 4;
