@@ -8,8 +8,8 @@
 // Three launches per window of frames:
 //   bc_partial  -- one workgroup per (b, h, frame): phi(K_f)^T [V_f | 1] on bf16 matrix
 //                  cores (the extra ones-column yields the key sums that form z); K and
-//                  V chunks copied global -> LDS one chunk ahead, operands taken with
-//                  transposed LDS reads.
+//                  V copied global -> LDS in 32-token sub-chunks, four in flight, operands
+//                  taken with transposed LDS reads.
 //   bc_scan     -- one wave per (b, h, 16x16 tile): running sum over frames in fp32,
 //                  written as readout operand fragments.
 //   bc_readout  -- one workgroup per (b, h, frame) or part of one: Q chunks copied
@@ -21,17 +21,20 @@
 
 namespace gdn {
 
-// bc_partial layout: K and V chunks of 64 tokens row-major in LDS, double-buffered.
-// bf16 rows span an odd number of 32-byte units (conflict-free transposed reads); the
-// global -> LDS copies fill padding granules with a copy of a data granule.
+// Row layout of K, V (bc_partial) and Q (bc_readout) tiles in LDS: bf16 rows span an odd
+// number of 32-byte units (conflict-free transposed reads); the global -> LDS copies fill
+// padding granules with a copy of a data granule.
 template <typename E, int ND> struct BCP {
     static constexpr bool BF = sizeof(E) == 2;
-    static constexpr int RB = 16 * ND * (int)sizeof(E);  // bytes of one K or V row
+    static constexpr int RB = 16 * ND * (int)sizeof(E);  // bytes of one K, V or Q row
     static constexpr int KPB = !BF ? RB : ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
     static constexpr int KG = KPB / 16, DG = RB / 16;    // granules per LDS row / with data
-    static constexpr int TILE_B = 64 * KPB;              // one K or V chunk
-    static constexpr int NI = 2 * KG;                    // 1 KB copy instructions per chunk
-    static constexpr int LDS_B = 2 * 2 * TILE_B;
+    static constexpr int TILE_B = 64 * KPB;              // 64 rows (a bc_readout Q chunk)
+    // bc_partial: K and V in 32-token sub-chunks, NB buffers, NB - 1 sub-chunks in flight
+    static constexpr int SUB_B = 32 * KPB;               // one K or V sub-chunk
+    static constexpr int NB = BF ? 5 : 4;
+    static constexpr int NI = 2 * SUB_B / 1024;          // 1 KB copy instructions per sub-chunk
+    static constexpr int LDS_B = NB * 2 * SUB_B;
 };
 
 template <typename E, int ND>
@@ -45,72 +48,66 @@ __global__ __launch_bounds__(256, 2) void bc_partial(BC1Args a) {
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
     const int fw = blockIdx.x, bh = blockIdx.y;
-    const int N = a.frame_len, nch = (N + 63) / 64;
+    const int N = a.frame_len, nsub = (N + 31) / 32;
     const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw) * N;
     const E* kp = (const E*)a.k + tok0 * D;
     const E* vp = (const E*)a.v + tok0 * D;
-    auto buf = [&](int ch, int which) { return smem + ((ch & 1) * 2 + which) * L::TILE_B; };
-    // copies of chunk ch: instruction i moves 1 KB row block i / 2 of K (i even) or V;
+    auto buf = [&](int sc, int which) { return smem + ((sc % L::NB) * 2 + which) * L::SUB_B; };
+    // copies of sub-chunk sc: instruction i moves 1 KB row block i / 2 of K (i even) or V;
     // rows past the frame copy its last row (finite values, masked out of the sums)
-    auto copy = [&](int ch) {
-        const int r0 = 64 * ch, Cc = min(64, N - r0);
+    auto copy = [&](int sc) {
+        const int r0 = 32 * sc, Cc = min(32, N - r0);
         for (int i = w; i < L::NI; i += 4) {
             const int which = i & 1, ii = i >> 1;
             const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
             const E* src = (which ? vp : kp) + (long long)(r0 + min(row, Cc - 1)) * D +
                            min(piece, L::DG - 1) * (16 / (int)sizeof(E));
-            dma16(src, buf(ch, which) + ii * 1024);
+            dma16(src, buf(sc, which) + ii * 1024);
         }
     };
+    const int ncp = (L::NI - w + 3) / 4;  // this wave's copy instructions per sub-chunk
     // acc[u][n]: rows 16(w + 4u) + 4g + i (features of phi(K)), columns 16n + c of [V | 1]
     f32x4 acc[MW][ND + 1];
 #pragma unroll
     for (int u = 0; u < MW; ++u)
 #pragma unroll
         for (int n = 0; n <= ND; ++n) acc[u][n] = zero4();
-    copy(0);
-    for (int ch = 0; ch < nch; ++ch) {
-        wait_vmem();    // this wave's copies of chunk ch
-        lds_barrier();  // every wave's copies visible; chunk ch-1's buffer free
-        if (ch + 1 < nch) copy(ch + 1);
-        const E* kb = (const E*)buf(ch, 0);
-        const E* vb = (const E*)buf(ch, 1);
-        const int Cc = min(64, N - 64 * ch);
+    for (int sc = 0; sc < L::NB - 1 && sc < nsub; ++sc) copy(sc);
+    for (int sc = 0; sc < nsub; ++sc) {
+        // this wave's copies of sub-chunk sc done; those of the next ones may be in flight
+        wait_vmem_le(ncp * min(L::NB - 2, nsub - 1 - sc));
+        lds_barrier();  // every wave's copies visible; sub-chunk sc-1's buffer free
+        if (sc + L::NB - 1 < nsub) copy(sc + L::NB - 1);
+        const E* kb = (const E*)buf(sc, 0);
+        const E* vb = (const E*)buf(sc, 1);
+        const int Cc = min(32, N - 32 * sc);
+        // K32 operands over the sub-chunk's 32 tokens, PAIR slot map: slot (g, j) is token
+        // 4g + j (j < 4) or 16 + 4g + j - 4
+        F8 kf[MW];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (32 * h >= Cc) break;
-            // K32 operands over the half's 32 tokens, PAIR slot map: slot (g, j) is token
-            // 32h + 4g + j (j < 4) or 32h + 16 + 4g + j - 4
-            F8 kf[MW];
+        for (int u = 0; u < MW; ++u) {
+            const int m = min(w + 4 * u, ND - 1);
+            kf[u] = __builtin_shufflevector(O::ldtr(kb, L::KPB, 0, 16 * m, lane), O::ldtr(kb, L::KPB, 16, 16 * m, lane),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+            if (a.relu) kf[u] = O::relu8(kf[u]);
+            if (Cc < 32) {  // tokens past the frame's end
 #pragma unroll
-            for (int u = 0; u < MW; ++u) {
-                const int m = min(w + 4 * u, ND - 1);
-                kf[u] = __builtin_shufflevector(O::ldtr(kb, L::KPB, 32 * h, 16 * m, lane),
-                                                O::ldtr(kb, L::KPB, 32 * h + 16, 16 * m, lane), 0, 1, 2, 3, 4, 5,
-                                                6, 7);
-                if (a.relu) kf[u] = O::relu8(kf[u]);
-                if (Cc < 64) {  // tokens past the frame's end
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int tk = 32 * h + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                        if (tk >= Cc) kf[u][j] = (E)0.f;
-                    }
-                }
+                for (int j = 0; j < 8; ++j)
+                    if ((j < 4 ? 4 * g + j : 16 + 4 * g + j - 4) >= Cc) kf[u][j] = (E)0.f;
             }
-#pragma unroll
-            for (int n = 0; n < ND; ++n) {
-                const F8 vf = __builtin_shufflevector(O::ldtr(vb, L::KPB, 32 * h, 16 * n, lane),
-                                                      O::ldtr(vb, L::KPB, 32 * h + 16, 16 * n, lane), 0, 1, 2, 3,
-                                                      4, 5, 6, 7);
-#pragma unroll
-                for (int u = 0; u < MW; ++u) acc[u][n] = O::mma32(kf[u], vf, acc[u][n]);
-            }
-            F8 of;  // the ones column (column 0 of block ND): key sums
-#pragma unroll
-            for (int j = 0; j < 8; ++j) of[j] = (E)(c == 0 ? 1.f : 0.f);
-#pragma unroll
-            for (int u = 0; u < MW; ++u) acc[u][ND] = O::mma32(kf[u], of, acc[u][ND]);
         }
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+            const F8 vf = __builtin_shufflevector(O::ldtr(vb, L::KPB, 0, 16 * n, lane),
+                                                  O::ldtr(vb, L::KPB, 16, 16 * n, lane), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int u = 0; u < MW; ++u) acc[u][n] = O::mma32(kf[u], vf, acc[u][n]);
+        }
+        F8 of;  // the ones column (column 0 of block ND): key sums
+#pragma unroll
+        for (int j = 0; j < 8; ++j) of[j] = (E)(c == 0 ? 1.f : 0.f);
+#pragma unroll
+        for (int u = 0; u < MW; ++u) acc[u][ND] = O::mma32(kf[u], of, acc[u][ND]);
     }
     const long long unit = (long long)bh * a.nf + fw;
     float* pp = a.part + unit * (ND * (ND + 1) * 256);

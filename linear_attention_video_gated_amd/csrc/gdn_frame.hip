@@ -58,9 +58,6 @@ template <int V> struct RoleC {
     static constexpr int value = V;
 };
 
-// Slice exponent of an fp16 map slice that is exactly zero (ldexp by it gives zero).
-constexpr int kZeroSlice = -1024;
-
 // TOK: the per-token readout pass (see gdn_token_readout below); otherwise the frame maps.
 template <typename E, int ND, bool TOK = false> struct P1 {
     using G = Geo<E, ND>;
@@ -739,15 +736,14 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // transposed, which one K16 product with the identity does exactly (an operand times
     // 1, accumulated in fp32): it turns lane (c, g) into the owner of A[16w + 4g + i][16t
     // + c], i.e. of 4 consecutive slots of its own fragment lane, written as one piece.
-    // exponent e: max |X 2^-e| in [2^14, 2^15); kZeroSlice when the slice is exactly zero
-    auto slice_exp = [&](const f32x4 (&X)[ND]) {
+    auto slice_exp = [&](const f32x4 (&X)[ND]) {  // exponent e: max |X 2^-e| in [2^14, 2^15)
         float m = 0.f;
 #pragma unroll
         for (int t = 0; t < ND; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(X[t][i]));
         m = wave_max(m);
-        return m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : kZeroSlice;
+        return m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
     };
     auto emit = [&](int fl, const f32x4 (&XA)[ND], const f32x4 (&XB)[ND]) {
         const long long unit = (long long)bh * a.nf + fw0 + fl;
@@ -1234,18 +1230,8 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
             return *(const f32x4*)((const float*)a.Bfr + o);
         }
     };
-    // A map exactly zero (the state before the group has decayed below the smallest float
-    // by this frame's end): S_f = B_f
-    bool azero = false;
-    if constexpr (O::kSplit && ND <= 7) {  // (at d = 128 the second path costs occupancy)
-        if (!a.b_is_state) {
-            azero = true;
-#pragma unroll
-            for (int t = 0; t < ND; ++t) azero = azero && ex[t] == kZeroSlice;
-        }
-    }
     f32x4 X[NSL][ND];
-    if (a.b_is_state || azero) {
+    if (a.b_is_state) {
 #pragma unroll
         for (int u = 0; u < NSL; ++u) {
             const int sl = own[u] ? w + 4 * u : 0;
