@@ -18,8 +18,9 @@
 //  2. gdn_frame_chain   -- one 4-wave workgroup per (b, h, 4 row slices of S): the serial
 //     part, one d x d product per GROUP:  S_g = S_{g-1} A_g + B_g.  Writes the state
 //     before every group and the final state.
-//  3. gdn_frame_readout -- one workgroup per (b, h, frame): composes
-//     S_f = S_{g-1} A_{g,<=f} + B_{g,<=f}, then streams Q in and O = Q S_f^T out.
+//  3. gdn_frame_readout -- one workgroup per (b, h, frame), or per part of a frame's
+//     chunks when a call has few frames: composes S_f = S_{g-1} A_{g,<=f} + B_{g,<=f},
+//     then streams Q in and O = Q S_f^T out.
 //     For the per-token readout the third launch is gdn_token_readout instead: the same
 //     chunk pipeline rerun from each group's true start state, writing o_t = S_t q_t.
 // Chunk algebra (derivation from the recurrence, restated; G_t = sum_{i<=t} log a_i in
@@ -34,6 +35,9 @@
 // sent to the matrix cores as bf16 hi + lo pairs, which keeps ~16 significant bits; W and
 // U are formed block by block as X_I = Z_I + (T_II - I) Z_I with Z_I = R_I - sum_{J<I}
 // L_IJ X_J kept in fp32, so only the operand of the correction (T_II - I) Z_I is rounded.
+// The per-frame maps that only the readout composes with are kept in fp16 with a power
+// of two per 16-row slice (11 significant bits, below the rounding of the bf16 output);
+// the group maps that the chain carries keep the hi + lo pair (A) and fp32 (B).
 #include "common.hpp"
 #include "gdn_kernels.hpp"
 #include <float.h>
@@ -1144,7 +1148,7 @@ __global__ __launch_bounds__(256, 1) void gdn_frame_chain(P2Args a) {
             float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + srow;
 #pragma unroll
             for (int t = 0; t < ND; ++t) *(f32x4*)(sg + 16 * t + 4 * g) = X[t];
-            // X <- Bt + A^T X, A streamed from LDS tile by tile
+            // X <- B + A^T X (the group's maps), A streamed from LDS tile by tile
             const E* ah = sA + (gi & 1) * NS * APK_E;
             F8 xh[KB], xl[KB];
 #pragma unroll
