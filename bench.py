@@ -27,9 +27,17 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN fwd tokens/s (720p 60s, H=20 d=112) + % of MFMA/HBM roofline"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["linear_attention_video_gated_amd/csrc/gdn_frame.hip",
-                  "linear_attention_video_gated_amd/csrc/block_causal.hip",
-                  "linear_attention_video_gated_amd/csrc/common.hpp"]
+# Sources each kernel family is built and launched from: a counter summary under profiles/
+# is used only while its family's sources hash to the value recorded in it.
+_CSRC = "linear_attention_video_gated_amd/csrc/"
+KERNEL_SOURCES = {
+    "gdn": [_CSRC + f for f in ("gdn_frame.hip", "gdn_api.hip", "gdn_kernels.hpp", "common.hpp")],
+    "block_causal": [_CSRC + f for f in ("block_causal.hip", "common.hpp")],
+}
+
+
+def kernel_family(kind):
+    return "block_causal" if kind == "block_causal" else "gdn"
 
 # Per-kernel algorithmic bytes per token-head (d, element size es):
 #   gdn_frame_affine  reads k, v and the two gates:  2*d*es + 8
@@ -57,9 +65,9 @@ def path_bytes_per_token_head(kind, d, es):
     return 4 * d * es + (0 if kind == "block_causal" else 8)
 
 
-def kernel_source_hash():
+def kernel_source_hash(kind):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel_family(kind)]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -96,7 +104,7 @@ class HipEvents:
             self.rt.hipEventDestroy(h)
 
 
-def read_counters(workload):
+def read_counters(workload, kind):
     """HBM bytes per launch of the dominant kernel from a committed rocprofv3 counter
     summary, if it was taken on the current kernel sources (else None)."""
     path = os.path.join(PROFILES, "counters_%s.txt" % workload)
@@ -107,7 +115,7 @@ def read_counters(workload):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_hash():
+    if kv.get("kernel_source_sha") != kernel_source_hash(kind):
         return None
     try:
         return {"kernel": kv["kernel"], "bytes": float(kv["hbm_bytes_per_launch"])}
@@ -332,7 +340,7 @@ def main():
     kbytes = per[kname] * th / nwin
     kms_launch = kms[j] / nwin
     achieved = kbytes / (kms_launch * 1e-3) / 1e9
-    counters = read_counters(args.workload)
+    counters = read_counters(args.workload, wl.kind)
     traffic = counters["bytes"] if counters and counters["kernel"] == kname else None
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -366,7 +374,7 @@ def main():
                    "frame_len": wl.frame_len, "tokens": wl.T, "calls_per_step": calls,
                    "parallelism": "single GPU"},
         "roofline": roofline, "path": path, "cpu_baseline": cpu,
-        "wall_s_timed": round(t_wall, 3), "kernel_source_sha": kernel_source_hash(),
+        "wall_s_timed": round(t_wall, 3), "kernel_source_sha": kernel_source_hash(wl.kind),
         "cache": "1 GiB read before each timed step" if scrub else "working set above the caches",
     }
     line.update(extra)
