@@ -84,3 +84,16 @@ def block_causal_inputs(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, work
         z_in = (state_std * d) * _normal((B, H, d), seed_for(workload_id, "z", step), device).abs()
     return {"q": q.to(dtype).contiguous(), "k": k.to(dtype).contiguous(),
             "v": v.to(dtype).contiguous(), "state_in": s_in, "z_in": z_in}
+
+
+def softmax_inputs(B, H, n_frames, kv_frames, frame_len, d, dtype=torch.bfloat16, workload_id=6,
+                   step=0, device="cpu", dv=None):
+    """Inputs of frame-block-causal softmax attention: k, v ~ N(0,1) [B,H,kv_frames*N,d]
+    (the first kv_frames - n_frames frames stand for cached earlier frames) and
+    q ~ N(0,1) [B,H,n_frames*N,d]."""
+    dv = d if dv is None else dv
+    Tq, Tk = n_frames * frame_len, kv_frames * frame_len
+    q = _normal((B, H, Tq, d), seed_for(workload_id, "q", step), device)
+    k = _normal((B, H, Tk, d), seed_for(workload_id, "k", step), device)
+    v = _normal((B, H, Tk, dv), seed_for(workload_id, "v", step), device)
+    return {"q": q.to(dtype).contiguous(), "k": k.to(dtype).contiguous(), "v": v.to(dtype).contiguous()}

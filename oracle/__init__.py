@@ -1,4 +1,5 @@
-"""CPU oracle for the frame-wise gated delta rule and block-causal ReLU linear attention.
+"""CPU oracle for the frame-wise gated delta rule, block-causal ReLU linear attention and
+frame-block-causal softmax attention.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``; never by the product package.  It shares no code
@@ -12,4 +13,5 @@ from .oracle import (  # noqa: F401
     build,
     gdn_forward,
     linear_attn_block_causal,
+    softmax_attn_block_causal,
 )

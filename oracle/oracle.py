@@ -53,6 +53,9 @@ def _load():
             lib.oracle_linear_attn_block_causal.argtypes = [fp, fp, fp, fp, fp, dp, dp, dp,
                                                             i, i, i, i, i, i, ctypes.c_double, i]
             lib.oracle_linear_attn_block_causal.restype = i
+            lib.oracle_softmax_attn_block_causal.argtypes = [fp, fp, fp, dp, i, i, i, i, i, i, i,
+                                                             ctypes.c_double, i]
+            lib.oracle_softmax_attn_block_causal.restype = i
             _lib = lib
     return _lib
 
@@ -134,3 +137,28 @@ def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=N
     if rc != 0:
         raise RuntimeError("oracle_linear_attn_block_causal failed (%d)" % rc)
     return out, s_out, z_out
+
+
+def softmax_attn_block_causal(q, k, v, n_frames, kv_frames, frame_len, scale=0.0, n_threads=0):
+    """Frame-block-causal softmax attention (see ``oracle_gdn.c``).
+
+    q: [B, H, n_frames * frame_len, d_k]; k: [B, H, kv_frames * frame_len, d_k];
+    v: [B, H, kv_frames * frame_len, d_v].  The queries' frames are the last n_frames of
+    the kv_frames key frames.  scale <= 0 means 1 / sqrt(d_k).
+    Returns out [B, H, n_frames * frame_len, d_v] float64.
+    """
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Tq, dk = q.shape
+    dv = v.shape[-1]
+    if (Tq != n_frames * frame_len or k.shape != (B, H, kv_frames * frame_len, dk)
+            or v.shape[:3] != (B, H, kv_frames * frame_len) or kv_frames < n_frames):
+        raise ValueError("shape mismatch")
+    out = np.zeros((B, H, Tq, dv), dtype=np.float64)
+    rc = lib.oracle_softmax_attn_block_causal(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                              _ptr(v, ctypes.c_float), _ptr(out, ctypes.c_double),
+                                              B, H, n_frames, kv_frames, frame_len, dk, dv,
+                                              float(scale), int(n_threads))
+    if rc != 0:
+        raise RuntimeError("oracle_softmax_attn_block_causal failed (%d)" % rc)
+    return out

@@ -237,3 +237,75 @@ int oracle_linear_attn_block_causal(const float* q, const float* k, const float*
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Frame-block-causal softmax attention: the softmax layers of the hybrid mixer.
+ * [W] section "hybrid architecture for long rollouts", with "SANA-WM: one-minute
+ * 720p world model" (hn.hoangyell.com), "Hybrid Linear Attention" among its four
+ * technical decisions, and the Turkish summary of the same news topic
+ * (tr.news.hada.io, topic 29572), first bullet: the frame-wise Gated DeltaNet covers
+ * most of the sequence and is interleaved with periodic softmax attention over
+ * windows of frames.  The pages give neither the mask nor the window.  Reading taken:
+ * a query token sees, through an exact softmax, every key of its own frame and of
+ * earlier frames -- the same frame-level visibility as the linear layers' frame-end
+ * readout -- among the kv_frames frames the caller passes (the caller's choice of
+ * earlier frames is the window; the last n_frames of them are the queries' frames).
+ *
+ *   f_i   = (kv_frames - n_frames) + i / frame_len       (global frame of query i)
+ *   l_ij  = scale * (q_i . k_j)   for keys j < (f_i + 1) * frame_len
+ *   o_i   = sum_j exp(l_ij) v_j / sum_j exp(l_ij)
+ *
+ * written with the row maximum subtracted from every l_ij before exp (an exact
+ * identity that keeps exp in range).  scale <= 0 selects 1 / sqrt(dk).
+ * q, out [B, H, n_frames * frame_len, dk | dv]; k, v [B, H, kv_frames * frame_len, dk | dv].
+ * Returns 0, or -1 on bad sizes / allocation failure.
+ */
+int oracle_softmax_attn_block_causal(const float* q, const float* k, const float* v,
+                                     double* out, int B, int H, int n_frames, int kv_frames,
+                                     int frame_len, int dk, int dv, double scale, int n_threads)
+{
+    if (B < 0 || H < 0 || n_frames < 0 || kv_frames < n_frames || frame_len < 1 || dk <= 0 || dv <= 0)
+        return -1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)dk);
+    const long long Tq = (long long)n_frames * frame_len, Tk = (long long)kv_frames * frame_len;
+    const long long rows = (long long)B * H * Tq;
+    const int off = kv_frames - n_frames;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel reduction(| : failed)
+#endif
+    {
+        double* lg = (double*)malloc(sizeof(double) * (size_t)(Tk > 0 ? Tk : 1));
+        if (!lg) failed = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 64)
+#endif
+        for (long long r = 0; r < rows; ++r) {
+            if (!lg) continue;
+            const long long bh = r / Tq, i = r - bh * Tq;
+            const long long nvis = ((long long)off + i / frame_len + 1) * frame_len;
+            const float* qi = q + (size_t)r * dk;
+            const float* kh = k + (size_t)bh * Tk * dk;
+            const float* vh = v + (size_t)bh * Tk * dv;
+            double m = -HUGE_VAL;
+            for (long long j = 0; j < nvis; ++j) {
+                double s = 0.0;
+                for (int c = 0; c < dk; ++c) s += (double)qi[c] * (double)kh[j * dk + c];
+                lg[j] = scale * s;
+                if (lg[j] > m) m = lg[j];
+            }
+            double den = 0.0;
+            double* oi = out + (size_t)r * dv;
+            for (int c = 0; c < dv; ++c) oi[c] = 0.0;
+            for (long long j = 0; j < nvis; ++j) {
+                const double p = exp(lg[j] - m);
+                den += p;
+                for (int c = 0; c < dv; ++c) oi[c] += p * (double)vh[j * dv + c];
+            }
+            for (int c = 0; c < dv; ++c) oi[c] /= den;
+        }
+        free(lg);
+    }
+    return failed ? -1 : 0;
+}

@@ -317,3 +317,111 @@ def test_gate_logits_limits():
     out, _ = oracle.gdn_forward(q, k, v, big, big, T, 1, state_in=np.ones((1, 1, dv, d), np.float32), flags=flags)
     ref = _np64(v[0, 0]) * np.sum(kh[0, 0] * _np64(q[0, 0]), axis=-1, keepdims=True)
     np.testing.assert_allclose(out[0, 0], ref, rtol=0, atol=1e-12 + 1e-9 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- softmax attention layers
+def _sa_rand(B=1, H=2, F=3, KF=None, N=4, d=8, seed=61):
+    from linear_attention_video_gated_amd.inputs import softmax_inputs
+    KF = F if KF is None else KF
+    inp = softmax_inputs(B, H, F, KF, N, d, dtype=torch.float32, workload_id=seed)
+    return {n: inp[n].numpy().astype(np.float64) for n in ("q", "k", "v")}
+
+
+def _sdpa64(q, k, v, **kw):
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), **kw).numpy()
+
+
+def test_softmax_handworked_d2():
+    g = json.load(open(GOLD))["softmax"]
+    arr = lambda x: np.asarray(x, dtype=np.float32)[None, None]
+    out = oracle.softmax_attn_block_causal(arr(g["q"]), arr(g["k"]), arr(g["v"]), g["n_frames"],
+                                           g["kv_frames"], g["frame_len"], scale=g["scale"])
+    np.testing.assert_allclose(out[0, 0], np.asarray(g["out"]), rtol=1e-13, atol=1e-13)
+
+
+def test_softmax_one_token_frames_is_causal_attention():
+    """frame_len = 1: the frame mask is the token-causal mask of textbook attention."""
+    x = _sa_rand(F=13, N=1, d=8)
+    ref = _sdpa64(x["q"], x["k"], x["v"], is_causal=True)
+    out = oracle.softmax_attn_block_causal(x["q"], x["k"], x["v"], 13, 13, 1)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_last_frame_sees_everything():
+    """The queries of the newest frame see every key passed: plain unmasked attention,
+    with or without cached earlier frames."""
+    for F, KF in ((1, 1), (1, 4)):
+        x = _sa_rand(F=F, KF=KF, N=5, d=8, seed=62 + KF)
+        ref = _sdpa64(x["q"], x["k"], x["v"])
+        out = oracle.softmax_attn_block_causal(x["q"], x["k"], x["v"], F, KF, 5)
+        np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_equal_keys_average_the_visible_values():
+    """Equal keys give equal weights: each query gets the mean of the values of the keys it
+    sees, which counts the visible frames (its own included, cached ones included)."""
+    F, KF, N = 3, 5, 4
+    x = _sa_rand(F=F, KF=KF, N=N, d=6, seed=64)
+    k = np.broadcast_to(x["k"][:, :, :1], x["k"].shape).copy()
+    out = oracle.softmax_attn_block_causal(x["q"], k, x["v"], F, KF, N)
+    for i in range(F * N):
+        nvis = (KF - F + i // N + 1) * N
+        np.testing.assert_allclose(out[:, :, i], x["v"][:, :, :nvis].mean(axis=2), rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_frame_causality_and_block_invariance():
+    F, N = 4, 5
+    x = _sa_rand(F=F, N=N, d=8, seed=65)
+    base = oracle.softmax_attn_block_causal(x["q"], x["k"], x["v"], F, F, N)
+    rng = np.random.default_rng(3)
+    for f in range(F):
+        # keys and values of later frames do not reach frame f's queries ...
+        k2, v2 = x["k"].copy(), x["v"].copy()
+        k2[:, :, (f + 1) * N:] = rng.standard_normal(k2[:, :, (f + 1) * N:].shape)
+        v2[:, :, (f + 1) * N:] = rng.standard_normal(v2[:, :, (f + 1) * N:].shape)
+        o2 = oracle.softmax_attn_block_causal(x["q"], k2, v2, F, F, N)
+        np.testing.assert_array_equal(o2[:, :, :(f + 1) * N], base[:, :, :(f + 1) * N])
+        # ... but those of frame f itself do (the mask is inclusive of the own frame)
+        v3 = x["v"].copy()
+        v3[:, :, f * N + N - 1] += 1.0
+        o3 = oracle.softmax_attn_block_causal(x["q"], x["k"], v3, F, F, N)
+        assert np.abs(o3[:, :, f * N:(f + 1) * N] - base[:, :, f * N:(f + 1) * N]).min() > 1e-6
+    # keys (with their values) permuted inside a frame: same outputs (no order inside a frame)
+    perm = np.arange(F * N)
+    perm[N:2 * N] = perm[N:2 * N][::-1]
+    o4 = oracle.softmax_attn_block_causal(x["q"], x["k"][:, :, perm], x["v"][:, :, perm], F, F, N)
+    np.testing.assert_allclose(o4, base, rtol=1e-12, atol=1e-13)
+
+
+def test_softmax_cached_frames_equal_full_call_rows():
+    """Queries of the last frames against cached earlier frames = the same rows of one call
+    over all frames."""
+    KF, N = 5, 3
+    x = _sa_rand(F=KF, N=N, d=8, seed=66)
+    full = oracle.softmax_attn_block_causal(x["q"], x["k"], x["v"], KF, KF, N)
+    for F in (1, 2, 4):
+        part = oracle.softmax_attn_block_causal(x["q"][:, :, (KF - F) * N:], x["k"], x["v"], F, KF, N)
+        np.testing.assert_allclose(part, full[:, :, (KF - F) * N:], rtol=1e-13, atol=1e-14)
+
+
+def test_softmax_shift_scale_and_large_logits():
+    F, N = 3, 4
+    x = _sa_rand(F=F, N=N, d=8, seed=67)
+    x["k"] = np.round(x["k"] * 1024) / 1024  # on a grid where k + u below is exact in float32
+    base = oracle.softmax_attn_block_causal(x["q"], x["k"], x["v"], F, F, N)
+    # a vector added to every key shifts each query's logits by a constant: no change
+    u = np.linspace(-2, 3, 8).round(2) // 0.25 * 0.25
+    o1 = oracle.softmax_attn_block_causal(x["q"], x["k"] + u, x["v"], F, F, N)
+    np.testing.assert_allclose(o1, base, rtol=1e-10, atol=1e-11)
+    # the default scale is 1/sqrt(d_k)
+    o2 = oracle.softmax_attn_block_causal(x["q"], x["k"], x["v"], F, F, N, scale=1 / np.sqrt(8))
+    np.testing.assert_array_equal(o2, base)
+    # logits far beyond exp's range: each query takes the value of its best visible key
+    q = 1e4 * x["q"]
+    o3 = oracle.softmax_attn_block_causal(q, x["k"], x["v"], F, F, N)
+    for i in range(F * N):
+        nvis = (i // N + 1) * N
+        best = np.argmax(np.einsum("bhd,bhjd->bhj", q[:, :, i], x["k"][:, :, :nvis]), axis=-1)
+        want = np.take_along_axis(x["v"][:, :, :nvis], best[..., None, None], axis=2)[:, :, 0]
+        np.testing.assert_allclose(o3[:, :, i], want, rtol=1e-12, atol=1e-12)
