@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -163,6 +163,29 @@ int linear_attn_block_causal(const void* q, const void* k, const void* v,
                              const float* state_in, const float* z_in,
                              float* state_out, float* z_out, void* out,
                              const gdn_dims_t* dims, void* stream);
+
+/*
+ * Frame-block-causal softmax attention: the softmax layers that the hybrid mixer
+ * interleaves with the frame-wise Gated DeltaNet ("SANA-WM: one-minute 720p world
+ * model", hn.hoangyell.com, "Hybrid Linear Attention" among its four technical decisions;
+ * "SANA-WM ... 720p video" news summary, section "hybrid architecture for long rollouts").
+ * The pages fix neither the mask nor the window; this entry computes, exactly, attention
+ * in which query i of global frame f_i = (kv_frames - n_frames) + i / frame_len sees
+ * every key of frames <= f_i:
+ *     o_i = sum_j exp(s q_i.k_j) v_j / sum_j exp(s q_i.k_j),  j < (f_i + 1) frame_len,
+ *     s = 1 / sqrt(d_k).
+ *  q, out [B,H,n_frames*frame_len,d] dtype (out float32 with GDN_F_OUT_F32);
+ *  k, v   [B,H,kv_frames*frame_len,d] dtype, kv_frames >= n_frames: the last n_frames
+ *         frames are the queries' own, earlier ones cached frames (the window is the
+ *         caller's choice of which earlier frames to pass).
+ *  Allowed flags: GDN_F_OUT_F32 only.  No workspace is used (dims->workspace ignored).
+ *  phase_events, if phase_windows >= 1: events 0 and 1 are recorded just before and just
+ *  after the single launch.  bf16 inputs: logits and softmax in float32, probabilities
+ *  rounded to bf16 for the product with V, float32 accumulation.  out must not overlap
+ *  q, k or v (GDN_ERR_ALIAS).  Returns GDN_ERR_DIMS when kv_frames < n_frames.
+ */
+int softmax_attn_block_causal(const void* q, const void* k, const void* v, void* out,
+                              int32_t kv_frames, const gdn_dims_t* dims, void* stream);
 
 /* Bytes of workspace the entry (GDN_ENTRY_*) needs for these dims; 0 on invalid dims.
  * Bounded independently of n_frames. */

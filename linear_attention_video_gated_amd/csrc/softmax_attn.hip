@@ -1,0 +1,330 @@
+// softmax_attn.hip -- frame-block-causal softmax attention on gfx950: the softmax layers
+// that the hybrid mixer interleaves with the frame-wise gated delta rule ("SANA-WM:
+// one-minute 720p world model", hn.hoangyell.com, "Hybrid Linear Attention" among its four
+// technical decisions; the news summaries of the same topic, section on the hybrid
+// architecture for long rollouts).  The pages give neither mask nor window; the reading
+// here: a query of global frame f sees, through an exact softmax, every key of frames
+// <= f among the kv_frames frames passed (the last n_frames of them are the queries' own
+// frames, the earlier ones a cache -- which earlier frames to pass is the window):
+//   o_i = sum_j exp(s q_i.k_j) v_j / sum_j exp(s q_i.k_j),   j < (f_i + 1) N,  s = 1/sqrt(d)
+//
+// One launch.  A workgroup (4 waves) takes 128 consecutive queries of one (b, h), 32 per
+// wave, and streams the keys it needs -- those up to the end of its last query's frame --
+// in blocks of 64 through LDS (global -> LDS copies, two blocks in flight: the next
+// block's copies overlap this block's products).  Per block and wave, on the matrix cores:
+//   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d): the accumulator gives each lane
+//                 one query column, 16 of its keys, so the row maximum needs two lane
+//                 exchanges and the row sums none until the end;
+//   O^T += V^T P^T (d tiles x 2 query tiles, k = the 64 keys): the probabilities enter
+//                 as the B operand straight from the S^T registers (PAIR slot map), V^T
+//                 comes from transposed LDS reads.
+// Online softmax in base 2 (logits scaled by s log2 e), in float32; P is rounded to the
+// operand type (bf16 for bf16 inputs) before the product, the row sums are not.  Blocks
+// past every query of a wave are skipped (the mask's own structure, not the data), and
+// only blocks that straddle a query's frame end are masked element by element.
+// Workgroups are dispatched heaviest first: the last query tiles of every head, which
+// see the most keys, lead the grid.
+#include "gdn.h"
+#include "common.hpp"
+#include <math.h>
+#include <stdint.h>
+
+#define SA_API extern "C" __attribute__((visibility("default")))
+
+namespace gdn {
+namespace {
+
+struct SAArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    long long Tq, Tk;  // tokens per (b, h): queries / keys
+    int frame_len;
+    int off;           // kv_frames - n_frames: global frame of the first query frame
+    int ntiles;        // 128-query tiles per (b, h)
+    int BH;
+    float sl2e;        // softmax scale * log2(e)
+    int out_f32;
+};
+
+// LDS layout: K and V blocks of 64 keys, row-major with the row pitch rule of the other
+// kernels (bf16 rows span an odd number of 32-byte units: conflict-free transposed
+// reads), two blocks of each in flight.
+template <typename E, int ND> struct SAL {
+    static constexpr bool BF = sizeof(E) == 2;
+    static constexpr int RB = 16 * ND * (int)sizeof(E);
+    static constexpr int KPB = !BF ? RB : ((RB + 31) / 32 % 2 == 1) ? (RB + 31) / 32 * 32 : (RB + 31) / 32 * 32 + 32;
+    static constexpr int KG = KPB / 16, DG = RB / 16;  // 16-byte granules per row / with data
+    static constexpr int BLK_B = 64 * KPB;             // one K or V block
+    static constexpr int NI = BLK_B / 1024;            // 1 KB copy instructions per K or V block
+    static constexpr int LDS_B = 4 * BLK_B;            // [2] x (K, V)
+    static_assert(BLK_B % 1024 == 0, "blocks are whole 1 KB copies");
+    static_assert(LDS_B <= 160 * 1024, "LDS budget");
+};
+
+template <typename E, int ND>
+__global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
+    using O = Ops<E>;
+    using F8 = typename O::F8;
+    using L = SAL<E, ND>;
+    constexpr int D = 16 * ND, KB = (ND + 1) / 2;
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int rank = blockIdx.x / a.BH;
+    const int bh = blockIdx.x - rank * a.BH;
+    const int tile = a.ntiles - 1 - rank;
+    const long long N = a.frame_len;
+    const long long q0 = (long long)tile * 128;
+    const long long qlast = min(q0 + 127, a.Tq - 1);
+    // keys this workgroup needs: through the end of its last query's frame (<= Tk)
+    const long long kend_wg = ((long long)a.off + qlast / N + 1) * N;
+    const int nblk = (int)((kend_wg + 63) / 64);
+    const E* kp = (const E*)a.k + (long long)bh * a.Tk * D;
+    const E* vp = (const E*)a.v + (long long)bh * a.Tk * D;
+    const E* qp = (const E*)a.q + (long long)bh * a.Tq * D;
+
+    // block b's copies: instruction i moves 1 KB of K (i < NI) or V; rows past the keys
+    // copy the last key (finite values; their weights are masked to zero)
+    auto copy = [&](int b) {
+        unsigned char* dst = smem + (b & 1) * 2 * L::BLK_B;
+        for (int i = w; i < 2 * L::NI; i += 4) {
+            const int which = i >= L::NI, ii = which ? i - L::NI : i;
+            const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
+            const long long key = min(64LL * b + row, a.Tk - 1);
+            const E* src = (which ? vp : kp) + key * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
+            dma16(src, dst + which * L::BLK_B + ii * 1024);
+        }
+    };
+    copy(0);
+
+    // this wave's queries: q0 + 32w + 16qt + c (qt = 0, 1); those past Tq compute on the
+    // last query's values and are not stored
+    const long long qw0 = q0 + 32 * w;
+    const bool active = qw0 < a.Tq;
+    const long long qwl = min(qw0 + 31, a.Tq - 1);
+    const long long kmax_w = ((long long)a.off + qwl / N + 1) * N;                 // keys any query sees
+    const long long kmin_w = ((long long)a.off + min(qw0, a.Tq - 1) / N + 1) * N;  // keys every query sees
+    long long kend[2];
+    F8 qf[2][KB];  // Q^T operands, PAIR slot map over d
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const long long qi = min(qw0 + 16 * qt + c, a.Tq - 1);
+        kend[qt] = ((long long)a.off + qi / N + 1) * N;
+        const E* r = qp + qi * D;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const E* p = r + 32 * kb + 4 * g;
+            if (2 * kb + 1 < ND) {
+                qf[qt][kb] = O::ld44(p, p + 16);
+            } else {
+                qf[qt][kb] = O::ld44(p, p);
+#pragma unroll
+                for (int j = 4; j < 8; ++j) qf[qt][kb][j] = (E)0.f;
+            }
+        }
+    }
+    f32x4 acc[2][ND];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[qt][t] = zero4();
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+    for (int b = 0; b < nblk; ++b) {
+        wait_vmem_le(0);  // this wave's copies of block b (the Q loads before the loop too)
+        lds_barrier();    // every wave's copies visible; block b-1's buffers free
+        if (b + 1 < nblk) copy(b + 1);
+        if (!active || 64LL * b >= kmax_w) continue;  // no query of this wave sees block b
+        const unsigned char* kbuf = smem + (b & 1) * 2 * L::BLK_B;
+        const E* vbuf = (const E*)(kbuf + L::BLK_B);
+        // S^T tiles: s[qt][kt] lane (c, g) = q(16qt + c) . k(64b + 16kt + 4g + i)
+        f32x4 s[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s[qt][kt] = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const E* r = (const E*)(kbuf + (16 * kt + c) * L::KPB) + 32 * kb + 4 * g;
+                F8 kf;
+                if (2 * kb + 1 < ND) {
+                    kf = O::ld44(r, r + 16);
+                } else {
+                    kf = O::ld44(r, r);
+#pragma unroll
+                    for (int j = 4; j < 8; ++j) kf[j] = (E)0.f;
+                }
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) s[qt][kt] = O::mma32(kf, qf[qt][kb], s[qt][kt]);
+            }
+        }
+        const bool edge = 64LL * (b + 1) > kmin_w;  // some query of the wave misses some key
+        F8 pf[2][2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = s[qt][kt][i] * a.sl2e;
+                    if (edge && 64LL * b + 16 * kt + 4 * g + i >= kend[qt]) x = -INFINITY;
+                    s[qt][kt][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // block 0 holds key 0, which every query sees, so mn is finite from block 0 on
+            const float mn = fmaxf(m[qt], mx);
+            const float corr = hw_exp2(m[qt] - mn);
+            m[qt] = mn;
+            float ls = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = hw_exp2(s[qt][kt][i] - mn);
+                    s[qt][kt][i] = p;
+                    ls += p;
+                }
+            l[qt] = l[qt] * corr + ls;
+#pragma unroll
+            for (int t = 0; t < ND; ++t) acc[qt][t] *= corr;
+            pf[qt][0] = O::pack8(s[qt][0], s[qt][1]);
+            pf[qt][1] = O::pack8(s[qt][2], s[qt][3]);
+        }
+        // O^T[d tile t] += V^T P^T over the block's 64 keys, PAIR slot map over keys
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const F8 vf = __builtin_shufflevector(O::ldtr(vbuf, L::KPB, 32 * st, 16 * t, lane),
+                                                      O::ldtr(vbuf, L::KPB, 32 * st + 16, 16 * t, lane), 0, 1, 2, 3,
+                                                      4, 5, 6, 7);
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) acc[qt][t] = O::mma32(vf, pf[qt][st], acc[qt][t]);
+            }
+        }
+    }
+    if (!active) return;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        float lt = l[qt];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const float inv = 1.f / lt;
+        const long long qi = qw0 + 16 * qt + c;
+        if (qi >= a.Tq) continue;
+        const long long o = ((long long)bh * a.Tq + qi) * D + 4 * g;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+            if (a.out_f32) *(f32x4*)((float*)a.out + o + 16 * t) = acc[qt][t] * inv;
+            else O::st4((E*)a.out + o + 16 * t, acc[qt][t] * inv);
+        }
+    }
+}
+
+template <typename E, int ND>
+hipError_t launch_sa(const SAArgs& a, long long nwg, hipStream_t st, void* const* ev) {
+    hipError_t e;
+    static bool attr_done = false;  // per instantiation
+    if (!attr_done) {
+        if ((e = hipFuncSetAttribute((const void*)sa_fwd<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     SAL<E, ND>::LDS_B)) != hipSuccess)
+            return e;
+        attr_done = true;
+    }
+    if (ev && (e = hipEventRecord((hipEvent_t)ev[0], st)) != hipSuccess) return e;
+    constexpr int lds = SAL<E, ND>::LDS_B;
+    hipLaunchKernelGGL((sa_fwd<E, ND>), dim3((unsigned)nwg), dim3(256), lds, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return ev ? hipEventRecord((hipEvent_t)ev[1], st) : hipSuccess;
+}
+
+int nd_of_d(int d) {
+    switch (d) {
+        case 16: return 1;
+        case 32: return 2;
+        case 64: return 4;
+        case 112: return 7;
+        case 128: return 8;
+        default: return 0;
+    }
+}
+
+bool misaligned16(const void* p) { return p && ((uintptr_t)p & 15u) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+SA_API int softmax_attn_block_causal(const void* q, const void* k, const void* v, void* out, int32_t kv_frames,
+                                     const gdn_dims_t* d, void* stream) {
+    if (!d) return GDN_ERR_NULL;
+    if (d->dtype != GDN_BF16 && d->dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (d->B < 0 || d->H < 0 || d->n_frames < 0 || d->frame_len < 1 || kv_frames < d->n_frames)
+        return GDN_ERR_DIMS;
+    const int nd = nd_of_d(d->d_k);
+    if (d->d_k != d->d_v || nd == 0) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & ~(uint32_t)GDN_F_OUT_F32) return GDN_ERR_UNSUPPORTED;
+    const long long BH = (long long)d->B * d->H;
+    const long long Tq = (long long)d->n_frames * d->frame_len, Tk = (long long)kv_frames * d->frame_len;
+    if (BH == 0 || Tq == 0) return GDN_OK;
+    // element counts of k and v must fit comfortably in 63 bits; the grid in 31
+    if (Tk > ((long long)1 << 40) / BH / d->d_k) return GDN_ERR_DIMS;
+    const long long ntiles = (Tq + 127) / 128;
+    if (ntiles * BH >= ((long long)1 << 31)) return GDN_ERR_DIMS;
+    if (!q || !k || !v || !out) return GDN_ERR_NULL;
+    if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out)) return GDN_ERR_ALIGN;
+    const int es = d->dtype == GDN_BF16 ? 2 : 4;
+    const size_t qbytes = (size_t)(BH * Tq * d->d_k) * es, kbytes = (size_t)(BH * Tk * d->d_k) * es;
+    const size_t obytes = (size_t)(BH * Tq * d->d_v) * ((d->flags & GDN_F_OUT_F32) ? 4 : es);
+    if (overlaps(out, obytes, q, qbytes) || overlaps(out, obytes, k, kbytes) || overlaps(out, obytes, v, kbytes))
+        return GDN_ERR_ALIAS;
+    SAArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.frame_len = d->frame_len;
+    a.off = kv_frames - d->n_frames;
+    a.ntiles = (int)ntiles;
+    a.BH = (int)BH;
+    a.sl2e = (float)(1.4426950408889634 / sqrt((double)d->d_k));
+    a.out_f32 = (d->flags & GDN_F_OUT_F32) != 0;
+    void* const* ev = (d->phase_events && d->phase_windows >= 1) ? d->phase_events : nullptr;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipErrorInvalidValue;
+    const long long nwg = ntiles * BH;
+    if (d->dtype == GDN_BF16) {
+        switch (nd) {
+            case 1: e = launch_sa<bf16, 1>(a, nwg, st, ev); break;
+            case 2: e = launch_sa<bf16, 2>(a, nwg, st, ev); break;
+            case 4: e = launch_sa<bf16, 4>(a, nwg, st, ev); break;
+            case 7: e = launch_sa<bf16, 7>(a, nwg, st, ev); break;
+            case 8: e = launch_sa<bf16, 8>(a, nwg, st, ev); break;
+        }
+    } else {
+        switch (nd) {
+            case 1: e = launch_sa<float, 1>(a, nwg, st, ev); break;
+            case 2: e = launch_sa<float, 2>(a, nwg, st, ev); break;
+            case 4: e = launch_sa<float, 4>(a, nwg, st, ev); break;
+            case 7: e = launch_sa<float, 7>(a, nwg, st, ev); break;
+            case 8: e = launch_sa<float, 8>(a, nwg, st, ev); break;
+        }
+    }
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}

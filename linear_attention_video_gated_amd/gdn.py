@@ -19,7 +19,7 @@ GDN_BF16, GDN_F32 = 0, 1
 NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS = 1, 2, 4, 8, 16
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
 EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
-           "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
+           "softmax_attn_block_causal", "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -61,6 +61,8 @@ def lib():
         L.gdn_frame_forward_readonly.restype = ctypes.c_int
         L.linear_attn_block_causal.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
         L.linear_attn_block_causal.restype = ctypes.c_int
+        L.softmax_attn_block_causal.argtypes = [vp, vp, vp, vp, ctypes.c_int32, dp, vp]
+        L.softmax_attn_block_causal.restype = ctypes.c_int
         L.gdn_workspace_bytes.argtypes = [dp, ctypes.c_int]
         L.gdn_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_window_count.argtypes = [dp, ctypes.c_int]
@@ -247,3 +249,24 @@ def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=N
                                           _ptr(state_out), _ptr(z_out), _ptr(out), ctypes.byref(dims),
                                           _stream(q.device, stream)))
     return out, state_out, z_out
+
+
+def softmax_attn_block_causal(q, k, v, n_frames, kv_frames, frame_len, out=None, stream=None, out_dtype=None,
+                              events=None):
+    """softmax_attn_block_causal: q [B,H,n_frames*frame_len,d] against k, v
+    [B,H,kv_frames*frame_len,d] (the last n_frames frames are the queries' own).
+    Returns out shaped like q (float32 with out_dtype=torch.float32 or a float32 out)."""
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, H, Tq, d] and k, v [B, H, Tk, d]")
+    B, H, Tq, d = q.shape
+    if Tq != n_frames * frame_len or k.shape[2] != kv_frames * frame_len:
+        raise ValueError("Tq=%d, Tk=%d do not match n_frames=%d, kv_frames=%d, frame_len=%d"
+                         % (Tq, k.shape[2], n_frames, kv_frames, frame_len))
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    out, flags = _out(q, out, out_dtype, 0)
+    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(q.dtype), flags, events=events)
+    _check(lib().softmax_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(kv_frames),
+                                           ctypes.byref(dims), _stream(q.device, stream)))
+    return out

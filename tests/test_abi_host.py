@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 3
+    assert gdn.lib().gdn_abi_version() == 4
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
@@ -158,3 +158,28 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gdn, "LIB_PATH", "/nonexistent/libgdn_mi355x.so")
     with pytest.raises(gdn.GdnLibraryMissing):
         gdn.lib()
+
+
+def sa(dm, kv_frames=None, q=FAKE, k=FAKE + 2 ** 28, v=FAKE + 2 ** 29, out=FAKE + 2 ** 32):
+    kv = dm.n_frames if kv_frames is None else kv_frames
+    return gdn.lib().softmax_attn_block_causal(q, k, v, out, kv, ctypes.byref(dm), None)
+
+
+def test_softmax_attention_argument_checks():
+    L = gdn.lib()
+    assert L.softmax_attn_block_causal(FAKE, FAKE, FAKE, FAKE, 3, None, None) == -1
+    assert sa(dims(flags=0), kv_frames=2) == -2           # fewer key frames than query frames
+    assert sa(dims(flags=gdn.NORMALIZE_K)) == -7          # only OUT_F32 applies here
+    assert sa(dims(flags=gdn.RELU_QK)) == -7
+    assert sa(dims(flags=0, d=48)) == -7
+    assert sa(dims(flags=0, dtype=7)) == -3
+    dm = dims(flags=0)
+    dm.frame_len = 0
+    assert sa(dm) == -2
+    assert sa(dims(flags=0), q=None) == -1
+    assert sa(dims(flags=0), v=FAKE + 2 ** 29 + 8) == -4
+    assert sa(dims(flags=0), out=FAKE + 64) == -5          # out inside q
+    assert sa(dims(flags=gdn.OUT_F32), kv_frames=5, out=FAKE + 2 ** 29 + 4096) == -5  # inside v
+    # nothing to compute: no pointer is looked at
+    assert sa(dims(flags=0, B=0), q=None, k=None, v=None, out=None) == 0
+    assert sa(dims(flags=0, F=0), kv_frames=4, q=None, k=None, v=None, out=None) == 0
