@@ -33,11 +33,12 @@ _CSRC = "linear_attention_video_gated_amd/csrc/"
 KERNEL_SOURCES = {
     "gdn": [_CSRC + f for f in ("gdn_frame.hip", "gdn_api.hip", "gdn_kernels.hpp", "common.hpp")],
     "block_causal": [_CSRC + f for f in ("block_causal.hip", "common.hpp")],
+    "softmax": [_CSRC + f for f in ("softmax_attn.hip", "common.hpp")],
 }
 
 
 def kernel_family(kind):
-    return "block_causal" if kind == "block_causal" else "gdn"
+    return kind if kind in ("block_causal", "softmax") else "gdn"
 
 # Per-kernel algorithmic bytes per token-head (d, element size es):
 #   gdn_frame_affine  reads k, v and the two gates:  2*d*es + 8
@@ -49,6 +50,16 @@ def kernel_family(kind):
 GDN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_frame_readout")
 TOKEN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_token_readout")
 BC_KERNELS = ("bc_partial", "bc_scan", "bc_readout")
+SA_KERNELS = ("sa_fwd",)
+METRIC_SA = "frame-block-causal softmax attention fwd tokens/s (720p 5s, H=20 d=112) + % of bf16 MFMA peak"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks of MI355X
+
+
+def softmax_flops(wl):
+    """Algorithmic flops of one frame-block-causal softmax attention call: 2 d for q.k and
+    2 d for p v per (query, visible key) pair; frame f's N queries see (f + 1) N keys."""
+    pairs = wl.frame_len * wl.frame_len * wl.n_frames * (wl.n_frames + 1) // 2
+    return 4 * wl.d * wl.B * wl.H * pairs
 
 
 def kernel_bytes_per_token_head(kind, d, es):
@@ -62,7 +73,7 @@ def kernel_bytes_per_token_head(kind, d, es):
 
 def path_bytes_per_token_head(kind, d, es):
     """Algorithmic bytes per token-head of the whole path: q, k, v, o (and the gates)."""
-    return 4 * d * es + (0 if kind == "block_causal" else 8)
+    return 4 * d * es + (0 if kind in ("block_causal", "softmax") else 8)
 
 
 def kernel_source_hash(kind):
@@ -127,8 +138,11 @@ def setup(wl, device, gates="config"):
     """Seeded inputs of the workload.  The streaming workload gets fresh q, k, v, alpha,
     beta for every call of a step (its denoising steps and the commit), one state_in."""
     import torch
-    from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs
+    from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs, softmax_inputs
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if wl.kind == "softmax":
+        return softmax_inputs(wl.B, wl.H, wl.n_frames, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
+                              workload_id=wl.wid, device=device)
     if wl.kind == "block_causal":
         return block_causal_inputs(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
                                    workload_id=wl.wid, device=device)
@@ -195,6 +209,9 @@ def make_step(wl, inp, events=None):
     import torch
     q, k, v = inp["q"], inp["k"], inp["v"]
     out = torch.empty_like(q)
+    if wl.kind == "softmax":
+        return lambda ev=None: gdn.softmax_attn_block_causal(q, k, v, wl.n_frames, wl.n_frames, wl.frame_len,
+                                                             out=out, events=ev)
     if wl.kind == "block_causal":
         st = torch.empty(wl.B, wl.H, wl.d, wl.d, device=q.device)
         z = torch.empty(wl.B, wl.H, wl.d, device=q.device)
@@ -255,7 +272,9 @@ def cpu_baseline(wl, inp, budget_heads=16, frames=None):
     take = lambda x: x[:1, :heads, :T].detach().float().cpu().numpy() if x is not None else None
     q, k, v = take(inp["q"]), take(inp["k"]), take(inp["v"])
     t0 = time.perf_counter()
-    if wl.kind == "block_causal":
+    if wl.kind == "softmax":
+        oracle.softmax_attn_block_causal(q, k, v, frames, frames, wl.frame_len, n_threads=cores)
+    elif wl.kind == "block_causal":
         oracle.linear_attn_block_causal(q, k, v, frames, wl.frame_len, n_threads=cores)
     else:
         a, b = take(inp["alpha"]), take(inp["beta"])
@@ -310,15 +329,18 @@ def main():
     dt = _t.bfloat16 if wl.dtype == "bf16" else _t.float32
     entry = {"block_causal": gdn.ENTRY_BLOCK_CAUSAL, "stream": gdn.ENTRY_READONLY,
              "token": gdn.ENTRY_TOKEN}.get(wl.kind, gdn.ENTRY_FORWARD)
-    nwin = gdn.window_count(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
-                            flags=gdn.RELU_QK if wl.kind == "block_causal" else gdn.NORMALIZE_K, entry=entry)
+    if wl.kind == "softmax":  # one launch per call
+        nk, nwin = 1, 1
+    else:
+        nwin = gdn.window_count(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
+                                flags=gdn.RELU_QK if wl.kind == "block_causal" else gdn.NORMALIZE_K, entry=entry)
     ev = [hip.create(6 * nwin) for _ in range(args.steps)]
     scrub = scrubber(wl, dev)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     ms_step = time_steps(step, args.steps, scrub, ev)
     t_wall = time.perf_counter() - t_wall0
-    names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS}.get(wl.kind, GDN_KERNELS)
+    names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS, "softmax": SA_KERNELS}.get(wl.kind, GDN_KERNELS)
     kms = [0.0] * nk  # per call, summed over the call's windows
     for e in ev:
         for wi in range(nwin):
@@ -332,21 +354,30 @@ def main():
     value = wl.B * wl.T / (ms_step * 1e-3)
     es = 2 if wl.dtype == "bf16" else 4
     th = wl.B * wl.H * wl.T
-    per = kernel_bytes_per_token_head(wl.kind, wl.d, es)
     j = max(range(nk), key=lambda i: kms[i])
     kname = names[j]
-    # one launch per window: algorithmic bytes and duration per launch (window sizes are
-    # equal but for the last, so this is the call's total bytes over its total duration)
-    kbytes = per[kname] * th / nwin
     kms_launch = kms[j] / nwin
-    achieved = kbytes / (kms_launch * 1e-3) / 1e9
     counters = read_counters(args.workload, wl.kind)
     traffic = counters["bytes"] if counters and counters["kernel"] == kname else None
-    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin,
-                "algorithmic_bytes": round(kbytes),
-                "all_kernels_ms_per_call": {n: round(x, 4) for n, x in zip(names, kms)}}
+    if wl.kind == "softmax":
+        # a dense contraction (QK^T and PV on the matrix cores): the MFMA roofline binds
+        flops = softmax_flops(wl)
+        achieved = flops / (kms_launch * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[wl.dtype]
+        roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_flops": flops}
+    else:
+        per = kernel_bytes_per_token_head(wl.kind, wl.d, es)
+        # one launch per window: algorithmic bytes and duration per launch (window sizes are
+        # equal but for the last, so this is the call's total bytes over its total duration)
+        kbytes = per[kname] * th / nwin
+        achieved = kbytes / (kms_launch * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin,
+                    "algorithmic_bytes": round(kbytes),
+                    "all_kernels_ms_per_call": {n: round(x, 4) for n, x in zip(names, kms)}}
     path_per = path_bytes_per_token_head(wl.kind, wl.d, es)
     path_bytes = path_per * th * calls
     path_gbps = path_bytes / (ms_step * 1e-3) / 1e9
@@ -354,7 +385,7 @@ def main():
             "unit": "GB/s", "frac_of_8TBps": round(path_gbps / HBM_PEAK_GBPS, 4)}
 
     extra = {}
-    if wl.kind != "block_causal":
+    if wl.kind in ("gdn", "stream", "token"):
         # the alpha ~ 1 stress variant (slow decay: the maps and states keep full range);
         # the kernels do the same work whatever the gate values, so this should match
         extra["alpha_near_one"] = near_one_timing(wl, dev, ms_step, scrub)
@@ -363,10 +394,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp)
+        # the softmax oracle costs ~N^2 F^2 d per head: a few heads of the same call
+        cpu = cpu_baseline(wl, inp, budget_heads=4 if wl.kind == "softmax" else 16)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_SA if wl.kind == "softmax" else METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes of 720p/480p latent frames)",

@@ -12,7 +12,8 @@
 // wave, and streams the keys it needs -- those up to the end of its last query's frame --
 // in blocks of 64 through LDS (global -> LDS copies, two blocks in flight: the next
 // block's copies overlap this block's products).  Per block and wave, on the matrix cores:
-//   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d): the accumulator gives each lane
+//   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d; K rows read as 16-byte pieces): the
+//                 accumulator gives each lane
 //                 one query column, 16 of its keys, so the row maximum needs two lane
 //                 exchanges and the row sums none until the end;
 //   O^T += V^T P^T (d tiles x 2 query tiles, k = the 64 keys): the probabilities enter
@@ -48,7 +49,8 @@ struct SAArgs {
     int out_f32;
 };
 
-// LDS layout: K and V blocks of 64 keys, row-major with the row pitch rule of the other
+// LDS layout (float32 blocks are large enough that one workgroup fills a CU, hence the
+// launch bound of one for them): K and V blocks of 64 keys, row-major with the row pitch rule of the other
 // kernels (bf16 rows span an odd number of 32-byte units: conflict-free transposed
 // reads), two blocks of each in flight.
 template <typename E, int ND> struct SAL {
@@ -64,7 +66,7 @@ template <typename E, int ND> struct SAL {
 };
 
 template <typename E, int ND>
-__global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
+__global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a) {
     using O = Ops<E>;
     using F8 = typename O::F8;
     using L = SAL<E, ND>;
@@ -85,16 +87,31 @@ __global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
     const E* vp = (const E*)a.v + (long long)bh * a.Tk * D;
     const E* qp = (const E*)a.q + (long long)bh * a.Tq * D;
 
-    // block b's copies: instruction i moves 1 KB of K (i < NI) or V; rows past the keys
-    // copy the last key (finite values; their weights are masked to zero)
+    // block b's copies: instruction i = w + 4u moves 1 KB of K (i < NI) or V; lane l's
+    // 16 bytes are granule ii * 64 + l of the block (row, piece), the same for every
+    // block, so each lane keeps its element offsets; rows past the keys copy the last key
+    // (finite values; their weights are masked to zero)
+    constexpr int NU = (2 * L::NI + 3) / 4;
+    int roff[NU], prow[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int i = w + 4 * u, ii = i >= L::NI ? i - L::NI : i;
+        const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
+        prow[u] = row;
+        roff[u] = row * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
+    }
     auto copy = [&](int b) {
         unsigned char* dst = smem + (b & 1) * 2 * L::BLK_B;
-        for (int i = w; i < 2 * L::NI; i += 4) {
+        const bool tail = 64LL * (b + 1) > a.Tk;  // the last block of the keys may be ragged
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int i = w + 4 * u;
+            if (i >= 2 * L::NI) break;
             const int which = i >= L::NI, ii = which ? i - L::NI : i;
-            const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
-            const long long key = min(64LL * b + row, a.Tk - 1);
-            const E* src = (which ? vp : kp) + key * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
-            dma16(src, dst + which * L::BLK_B + ii * 1024);
+            const E* base = (which ? vp : kp) + 64LL * b * D;
+            int off = roff[u];
+            if (tail) off += (int)(min(64LL * b + prow[u], a.Tk - 1) - 64LL * b - prow[u]) * D;
+            dma16(base + off, dst + which * L::BLK_B + ii * 1024);
         }
     };
     copy(0);
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
     const long long kmax_w = ((long long)a.off + qwl / N + 1) * N;                 // keys any query sees
     const long long kmin_w = ((long long)a.off + min(qw0, a.Tq - 1) / N + 1) * N;  // keys every query sees
     long long kend[2];
-    F8 qf[2][KB];  // Q^T operands, PAIR slot map over d
+    F8 qf[2][KB];  // Q^T operands, IDENT slot map over d: lane (c, g) holds d 32kb + 8g ..
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
         const long long qi = min(qw0 + 16 * qt + c, a.Tq - 1);
@@ -115,14 +132,8 @@ __global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
         const E* r = qp + qi * D;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const E* p = r + 32 * kb + 4 * g;
-            if (2 * kb + 1 < ND) {
-                qf[qt][kb] = O::ld44(p, p + 16);
-            } else {
-                qf[qt][kb] = O::ld44(p, p);
-#pragma unroll
-                for (int j = 4; j < 8; ++j) qf[qt][kb][j] = (E)0.f;
-            }
+            const int col = 32 * kb + 8 * g;
+            qf[qt][kb] = col < D ? O::ld8(r + col) : O::zero8();
         }
     }
     f32x4 acc[2][ND];
@@ -149,37 +160,37 @@ __global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const E* r = (const E*)(kbuf + (16 * kt + c) * L::KPB) + 32 * kb + 4 * g;
-                F8 kf;
-                if (2 * kb + 1 < ND) {
-                    kf = O::ld44(r, r + 16);
-                } else {
-                    kf = O::ld44(r, r);
-#pragma unroll
-                    for (int j = 4; j < 8; ++j) kf[j] = (E)0.f;
-                }
+                // IDENT slot map: key row 16kt + c, d 32kb + 8g .. +7 (zero past d)
+                const int col = 32 * kb + 8 * g;
+                const F8 kf = col < D ? O::ld8((const E*)(kbuf + (16 * kt + c) * L::KPB) + col) : O::zero8();
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) s[qt][kt] = O::mma32(kf, qf[qt][kb], s[qt][kt]);
             }
         }
-        const bool edge = 64LL * (b + 1) > kmin_w;  // some query of the wave misses some key
+        if (64LL * (b + 1) > kmin_w) {  // some query of the wave misses some key of the block
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                const int rel = (int)max(-1LL, min(64LL, kend[qt] - 64LL * b));  // keys it sees here
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * kt + 4 * g + i >= rel) s[qt][kt][i] = -INFINITY;
+            }
+        }
         F8 pf[2][2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
+            // the maximum of the raw scores; the scale (s log2 e > 0) commutes with it
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = s[qt][kt][i] * a.sl2e;
-                    if (edge && 64LL * b + 16 * kt + 4 * g + i >= kend[qt]) x = -INFINITY;
-                    s[qt][kt][i] = x;
-                    mx = fmaxf(mx, x);
-                }
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qt][kt][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             // block 0 holds key 0, which every query sees, so mn is finite from block 0 on
-            const float mn = fmaxf(m[qt], mx);
+            const float mn = fmaxf(m[qt], mx * a.sl2e);
             const float corr = hw_exp2(m[qt] - mn);
             m[qt] = mn;
             float ls = 0.f;
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void sa_fwd(SAArgs a) {
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = hw_exp2(s[qt][kt][i] - mn);
+                    const float p = hw_exp2(__builtin_fmaf(s[qt][kt][i], a.sl2e, -mn));
                     s[qt][kt][i] = p;
                     ls += p;
                 }

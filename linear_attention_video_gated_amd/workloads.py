@@ -10,6 +10,7 @@ class Workload:
     name: str
     wid: int            # seed key
     kind: str           # "gdn" | "block_causal" | "stream" | "token" (per-token readout)
+                        # | "softmax" (frame-block-causal softmax attention)
     B: int
     H: int
     n_frames: int
@@ -33,5 +34,6 @@ WORKLOADS = {
         Workload("gdn_720p_60s", 3, "gdn", 1, 20, 240, 880, 112, "bf16"),
         Workload("stream_denoise_b16", 4, "stream", 16, 20, 1, 880, 112, "bf16", state_std=0.1, steps=50),
         Workload("gdn_720p_60s_token", 5, "token", 1, 20, 240, 880, 112, "bf16"),
+        Workload("softmax_720p_5s", 6, "softmax", 1, 20, 21, 880, 112, "bf16"),
     ]
 }
