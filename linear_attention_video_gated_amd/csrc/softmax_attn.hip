@@ -8,10 +8,10 @@
 // frames, the earlier ones a cache -- which earlier frames to pass is the window):
 //   o_i = sum_j exp(s q_i.k_j) v_j / sum_j exp(s q_i.k_j),   j < (f_i + 1) N,  s = 1/sqrt(d)
 //
-// One launch.  A workgroup (4 waves) takes 128 consecutive queries of one (b, h), 32 per
-// wave, and streams the keys it needs -- those up to the end of its last query's frame --
-// in blocks of 64 through LDS (global -> LDS copies, two blocks in flight: the next
-// block's copies overlap this block's products).  Per block and wave, on the matrix cores:
+// One launch.  A workgroup (8 waves for bf16, 4 for float32) takes 32 consecutive queries
+// of one (b, h) per wave and streams the keys it needs -- those up to the end of its last
+// query's frame -- in blocks of 64 through LDS (global -> LDS copies; the next block's
+// copies in flight while this one is used).  Per block and wave, on the matrix cores:
 //   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d; K rows read as 16-byte pieces): the
 //                 accumulator gives each lane
 //                 one query column, 16 of its keys, so the row maximum needs two lane
@@ -19,8 +19,9 @@
 //   O^T += V^T P^T (d tiles x 2 query tiles, k = the 64 keys): the probabilities enter
 //                 as the B operand straight from the S^T registers (PAIR slot map), V^T
 //                 comes from transposed LDS reads.
-// Online softmax in base 2 (logits scaled by s log2 e), in float32; P is rounded to the
-// operand type (bf16 for bf16 inputs) before the product, the row sums are not.  Blocks
+// Online softmax in base 2 (logits scaled by s log2 e), in float32, with a reference point
+// that moves only when a score exceeds it by more than 2^8 (weights <= 256); P is rounded
+// to the operand type (bf16 for bf16 inputs) before the product, the row sums are not.  Blocks
 // past every query of a wave are skipped (the mask's own structure, not the data), and
 // only blocks that straddle a query's frame end are masked element by element.
 // Workgroups are dispatched heaviest first: the last query tiles of every head, which
@@ -43,7 +44,7 @@ struct SAArgs {
     long long Tq, Tk;  // tokens per (b, h): queries / keys
     int frame_len;
     int off;           // kv_frames - n_frames: global frame of the first query frame
-    int ntiles;        // 128-query tiles per (b, h)
+    int ntiles;        // query tiles (one workgroup each) per (b, h)
     int BH;
     float sl2e;        // softmax scale * log2(e)
     int out_f32;
@@ -60,13 +61,45 @@ template <typename E, int ND> struct SAL {
     static constexpr int KG = KPB / 16, DG = RB / 16;  // 16-byte granules per row / with data
     static constexpr int BLK_B = 64 * KPB;             // one K or V block
     static constexpr int NI = BLK_B / 1024;            // 1 KB copy instructions per K or V block
-    static constexpr int LDS_B = 4 * BLK_B;            // [2] x (K, V)
+    // bf16: 8 waves (256 queries share each key block's copy); float32: 4 waves (register
+    // budget).  Two block buffers: the next block's copies overlap this block's products
+    // (a third buffer, two blocks in flight, measured slower at 8 waves)
+    static constexpr int NWV = BF ? 8 : 4;
+    static constexpr int NT = 64 * NWV;
+    static constexpr int QT = 32 * NWV;                // queries per workgroup
+    static constexpr int NBUF = 2;
+    static constexpr int NU = (2 * NI + NWV - 1) / NWV;  // copy instructions per wave and block (at most)
+    static constexpr int LDS_B = NBUF * 2 * BLK_B;     // [NBUF] x (K, V)
     static_assert(BLK_B % 1024 == 0, "blocks are whole 1 KB copies");
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
 };
 
+// op over the lanes l, l^16, l^32 and l^48 -- the four row groups g of one accumulator
+// column -- with the gfx950 lane swaps (v_permlane32_swap: lanes 32..63 of the first
+// register trade places with lanes 0..31 of the second; v_permlane16_swap: the odd rows of
+// 16 lanes of the first with the even rows of the second).  Given two copies of x, each
+// lane ends up holding its own value and its partner's.  Written as one instruction with
+// two in/out registers (wait states before and after): the builtins' two results get
+// folded into one by the compiler.
+__device__ __forceinline__ float across_g_max(float x) {
+    float y = x;
+    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    x = fmaxf(x, y);
+    y = x;
+    __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    return fmaxf(x, y);
+}
+__device__ __forceinline__ float across_g_sum(float x) {
+    float y = x;
+    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    x = x + y;
+    y = x;
+    __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    return x + y;
+}
+
 template <typename E, int ND>
-__global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a) {
+__global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
     using O = Ops<E>;
     using F8 = typename O::F8;
     using L = SAL<E, ND>;
@@ -78,8 +111,8 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
     const int bh = blockIdx.x - rank * a.BH;
     const int tile = a.ntiles - 1 - rank;
     const long long N = a.frame_len;
-    const long long q0 = (long long)tile * 128;
-    const long long qlast = min(q0 + 127, a.Tq - 1);
+    const long long q0 = (long long)tile * L::QT;
+    const long long qlast = min(q0 + L::QT - 1, a.Tq - 1);
     // keys this workgroup needs: through the end of its last query's frame (<= Tk)
     const long long kend_wg = ((long long)a.off + qlast / N + 1) * N;
     const int nblk = (int)((kend_wg + 63) / 64);
@@ -87,25 +120,26 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
     const E* vp = (const E*)a.v + (long long)bh * a.Tk * D;
     const E* qp = (const E*)a.q + (long long)bh * a.Tq * D;
 
-    // block b's copies: instruction i = w + 4u moves 1 KB of K (i < NI) or V; lane l's
+    // block b's copies: instruction i = w + NWV u moves 1 KB of K (i < NI) or V; lane l's
     // 16 bytes are granule ii * 64 + l of the block (row, piece), the same for every
     // block, so each lane keeps its element offsets; rows past the keys copy the last key
     // (finite values; their weights are masked to zero)
-    constexpr int NU = (2 * L::NI + 3) / 4;
+    constexpr int NU = L::NU;
+    const int ncp = (2 * L::NI - w + L::NWV - 1) / L::NWV;  // this wave's copies per block
     int roff[NU], prow[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int i = w + 4 * u, ii = i >= L::NI ? i - L::NI : i;
+        const int i = w + L::NWV * u, ii = i >= L::NI ? i - L::NI : i;
         const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
         prow[u] = row;
         roff[u] = row * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
     }
     auto copy = [&](int b) {
-        unsigned char* dst = smem + (b & 1) * 2 * L::BLK_B;
+        unsigned char* dst = smem + (b % L::NBUF) * 2 * L::BLK_B;
         const bool tail = 64LL * (b + 1) > a.Tk;  // the last block of the keys may be ragged
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int i = w + 4 * u;
+            const int i = w + L::NWV * u;
             if (i >= 2 * L::NI) break;
             const int which = i >= L::NI, ii = which ? i - L::NI : i;
             const E* base = (which ? vp : kp) + 64LL * b * D;
@@ -114,7 +148,6 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
             dma16(base + off, dst + which * L::BLK_B + ii * 1024);
         }
     };
-    copy(0);
 
     // this wave's queries: q0 + 32w + 16qt + c (qt = 0, 1); those past Tq compute on the
     // last query's values and are not stored
@@ -136,6 +169,9 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
             qf[qt][kb] = col < D ? O::ld8(r + col) : O::zero8();
         }
     }
+    // the first blocks' copies go out after the Q loads: the wait before block 0 then
+    // covers both
+    for (int b = 0; b < L::NBUF - 1 && b < nblk; ++b) copy(b);
     f32x4 acc[2][ND];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
@@ -144,11 +180,13 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
     for (int b = 0; b < nblk; ++b) {
-        wait_vmem_le(0);  // this wave's copies of block b (the Q loads before the loop too)
-        lds_barrier();    // every wave's copies visible; block b-1's buffers free
-        if (b + 1 < nblk) copy(b + 1);
+        // this wave's copies of block b done (and the Q loads); those of the next block
+        // may still be in flight
+        wait_vmem_le(ncp * min(L::NBUF - 2, nblk - 1 - b));
+        lds_barrier();  // every wave's copies visible; block b-1's buffers free
+        if (b + L::NBUF - 1 < nblk) copy(b + L::NBUF - 1);
         if (!active || 64LL * b >= kmax_w) continue;  // no query of this wave sees block b
-        const unsigned char* kbuf = smem + (b & 1) * 2 * L::BLK_B;
+        const unsigned char* kbuf = smem + (b % L::NBUF) * 2 * L::BLK_B;
         const E* vbuf = (const E*)(kbuf + L::BLK_B);
         // S^T tiles: s[qt][kt] lane (c, g) = q(16qt + c) . k(64b + 16kt + 4g + i)
         f32x4 s[2][4];
@@ -160,9 +198,10 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                // IDENT slot map: key row 16kt + c, d 32kb + 8g .. +7 (zero past d)
-                const int col = 32 * kb + 8 * g;
-                const F8 kf = col < D ? O::ld8((const E*)(kbuf + (16 * kt + c) * L::KPB) + col) : O::zero8();
+                // IDENT slot map: key row 16kt + c, d 32kb + 8g .. +7.  Past d the piece
+                // holds the next row's (or, after row 63, the V block's) finite values, which
+                // meet zero slots of Q
+                const F8 kf = O::ld8((const E*)(kbuf + (16 * kt + c) * L::KPB) + 32 * kb + 8 * g);
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) s[qt][kt] = O::mma32(kf, qf[qt][kb], s[qt][kt]);
             }
@@ -187,12 +226,22 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qt][kt][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // block 0 holds key 0, which every query sees, so mn is finite from block 0 on
-            const float mn = fmaxf(m[qt], mx * a.sl2e);
-            const float corr = hw_exp2(m[qt] - mn);
-            m[qt] = mn;
+            mx = across_g_max(mx);
+            // The reference point m of the exponentials moves only when some query of the
+            // wave sees a score more than 2^8 above it (always in block 0, whose key 0 every
+            // query sees, so m is finite from then on): the weights stay <= 256 and the
+            // rescaling of the accumulators is skipped for most blocks; the quotient is the
+            // same softmax whatever the reference point.
+            const float mc = mx * a.sl2e;
+            if (__builtin_amdgcn_ballot_w64(mc > m[qt] + 8.f) != 0) {
+                const float mn = fmaxf(m[qt], mc);
+                const float corr = hw_exp2(m[qt] - mn);
+                m[qt] = mn;
+                l[qt] *= corr;
+#pragma unroll
+                for (int t = 0; t < ND; ++t) acc[qt][t] *= corr;
+            }
+            const float mn = m[qt];
             float ls = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
@@ -202,9 +251,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
                     s[qt][kt][i] = p;
                     ls += p;
                 }
-            l[qt] = l[qt] * corr + ls;
-#pragma unroll
-            for (int t = 0; t < ND; ++t) acc[qt][t] *= corr;
+            l[qt] += ls;
             pf[qt][0] = O::pack8(s[qt][0], s[qt][1]);
             pf[qt][1] = O::pack8(s[qt][2], s[qt][3]);
         }
@@ -224,9 +271,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
     if (!active) return;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        float lt = l[qt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = across_g_sum(l[qt]);
         const float inv = 1.f / lt;
         const long long qi = qw0 + 16 * qt + c;
         if (qi >= a.Tq) continue;
@@ -240,7 +285,7 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) void sa_fwd(SAArgs a
 }
 
 template <typename E, int ND>
-hipError_t launch_sa(const SAArgs& a, long long nwg, hipStream_t st, void* const* ev) {
+hipError_t launch_sa(const SAArgs& a, hipStream_t st, void* const* ev) {
     hipError_t e;
     static bool attr_done = false;  // per instantiation
     if (!attr_done) {
@@ -251,7 +296,11 @@ hipError_t launch_sa(const SAArgs& a, long long nwg, hipStream_t st, void* const
     }
     if (ev && (e = hipEventRecord((hipEvent_t)ev[0], st)) != hipSuccess) return e;
     constexpr int lds = SAL<E, ND>::LDS_B;
-    hipLaunchKernelGGL((sa_fwd<E, ND>), dim3((unsigned)nwg), dim3(256), lds, st, a);
+    SAArgs r = a;
+    r.ntiles = (int)((a.Tq + SAL<E, ND>::QT - 1) / SAL<E, ND>::QT);
+    const long long nwg = (long long)r.ntiles * a.BH;
+    constexpr int nt = SAL<E, ND>::NT;
+    hipLaunchKernelGGL((sa_fwd<E, ND>), dim3((unsigned)nwg), dim3(nt), lds, st, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return ev ? hipEventRecord((hipEvent_t)ev[1], st) : hipSuccess;
 }
@@ -294,8 +343,7 @@ SA_API int softmax_attn_block_causal(const void* q, const void* k, const void* v
     if (BH == 0 || Tq == 0) return GDN_OK;
     // element counts of k and v must fit comfortably in 63 bits; the grid in 31
     if (Tk > ((long long)1 << 40) / BH / d->d_k) return GDN_ERR_DIMS;
-    const long long ntiles = (Tq + 127) / 128;
-    if (ntiles * BH >= ((long long)1 << 31)) return GDN_ERR_DIMS;
+    if ((Tq + 127) / 128 * BH >= ((long long)1 << 31)) return GDN_ERR_DIMS;  // grid (>= 128 queries a workgroup)
     if (!q || !k || !v || !out) return GDN_ERR_NULL;
     if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out)) return GDN_ERR_ALIGN;
     const int es = d->dtype == GDN_BF16 ? 2 : 4;
@@ -312,29 +360,28 @@ SA_API int softmax_attn_block_causal(const void* q, const void* k, const void* v
     a.Tk = Tk;
     a.frame_len = d->frame_len;
     a.off = kv_frames - d->n_frames;
-    a.ntiles = (int)ntiles;
+    a.ntiles = 0;  // set per instantiation (queries per workgroup)
     a.BH = (int)BH;
     a.sl2e = (float)(1.4426950408889634 / sqrt((double)d->d_k));
     a.out_f32 = (d->flags & GDN_F_OUT_F32) != 0;
     void* const* ev = (d->phase_events && d->phase_windows >= 1) ? d->phase_events : nullptr;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipErrorInvalidValue;
-    const long long nwg = ntiles * BH;
     if (d->dtype == GDN_BF16) {
         switch (nd) {
-            case 1: e = launch_sa<bf16, 1>(a, nwg, st, ev); break;
-            case 2: e = launch_sa<bf16, 2>(a, nwg, st, ev); break;
-            case 4: e = launch_sa<bf16, 4>(a, nwg, st, ev); break;
-            case 7: e = launch_sa<bf16, 7>(a, nwg, st, ev); break;
-            case 8: e = launch_sa<bf16, 8>(a, nwg, st, ev); break;
+            case 1: e = launch_sa<bf16, 1>(a, st, ev); break;
+            case 2: e = launch_sa<bf16, 2>(a, st, ev); break;
+            case 4: e = launch_sa<bf16, 4>(a, st, ev); break;
+            case 7: e = launch_sa<bf16, 7>(a, st, ev); break;
+            case 8: e = launch_sa<bf16, 8>(a, st, ev); break;
         }
     } else {
         switch (nd) {
-            case 1: e = launch_sa<float, 1>(a, nwg, st, ev); break;
-            case 2: e = launch_sa<float, 2>(a, nwg, st, ev); break;
-            case 4: e = launch_sa<float, 4>(a, nwg, st, ev); break;
-            case 7: e = launch_sa<float, 7>(a, nwg, st, ev); break;
-            case 8: e = launch_sa<float, 8>(a, nwg, st, ev); break;
+            case 1: e = launch_sa<float, 1>(a, st, ev); break;
+            case 2: e = launch_sa<float, 2>(a, st, ev); break;
+            case 4: e = launch_sa<float, 4>(a, st, ev); break;
+            case 7: e = launch_sa<float, 7>(a, st, ev); break;
+            case 8: e = launch_sa<float, 8>(a, st, ev); break;
         }
     }
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
