@@ -183,3 +183,11 @@ def test_softmax_attention_argument_checks():
     # nothing to compute: no pointer is looked at
     assert sa(dims(flags=0, B=0), q=None, k=None, v=None, out=None) == 0
     assert sa(dims(flags=0, F=0), kv_frames=4, q=None, k=None, v=None, out=None) == 0
+
+
+def test_softmax_attention_size_limits():
+    # key tensors past the element-count bound, and a grid past 2^31 workgroups
+    dm = dims(flags=0, B=1, H=1, F=1, N=1 << 30, d=128)
+    assert sa(dm, kv_frames=1 << 10) == -2
+    dm = dims(flags=0, B=65535, H=65535, F=1, N=128, d=16)
+    assert sa(dm) == -2

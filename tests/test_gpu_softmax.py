@@ -135,3 +135,30 @@ def test_softmax_empty_calls():
     out = gdn.softmax_attn_block_causal(q, k, k.clone(), 0, 3, 16)
     torch.cuda.synchronize()
     assert out.shape == q.shape
+
+
+def test_softmax_many_heads_tiny_frames():
+    """A 1-D grid of (query tile, head) pairs with many heads: 1000 heads of 3 frames x 5
+    tokens (one partial tile each); sampled heads against the oracle."""
+    B, H, F, N = 2, 500, 3, 5
+    say("case softmax many heads B=%d H=%d" % (B, H))
+    inp = softmax_inputs(B, H, F, F, N, 32, dtype=torch.bfloat16, workload_id=750)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    out = gdn.softmax_attn_block_causal(q, k, v, F, F, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (0, 499), (1, 250), (1, 499)):
+        ref = oracle.softmax_attn_block_causal(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
+                                               inp["v"][b:b + 1, h:h + 1], F, F, N)
+        check("b%d h%d" % (b, h), out[b:b + 1, h:h + 1], ref, TOL[torch.bfloat16])
+
+
+def test_softmax_long_cache_one_frame():
+    """One new frame of 100 tokens against 39 cached ones: a long key stream whose end is
+    not a multiple of the 64-key block, in both dtypes."""
+    for dtype in (torch.bfloat16, torch.float32):
+        run_case(1, 2, 1, 40, 100, 112, dtype, seed=760)
+
+
+def test_softmax_batch_and_ragged_tiles():
+    """B = 3 with 5 frames of 77 tokens: query tiles straddle frames and end mid-tile."""
+    run_case(3, 2, 5, 5, 77, 64, torch.bfloat16, seed=770)
