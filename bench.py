@@ -300,6 +300,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="gdn_720p_60s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gates", default="config", choices=("config", "near_one"),
+                    help="gate distribution of the timed run (near_one: the alpha ~ 1 stress variant)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 2 GiB device copy (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -314,7 +316,7 @@ def main():
     gdn.lib()
     wl = WORKLOADS[args.workload]
     dev = "cuda:0"
-    inp = setup(wl, dev)
+    inp = setup(wl, dev, gates=args.gates)
     step = make_step(wl, inp)
     hip = HipEvents()
 
@@ -385,7 +387,7 @@ def main():
             "unit": "GB/s", "frac_of_8TBps": round(path_gbps / HBM_PEAK_GBPS, 4)}
 
     extra = {}
-    if wl.kind in ("gdn", "stream", "token"):
+    if wl.kind in ("gdn", "stream", "token") and args.gates == "config":
         # the alpha ~ 1 stress variant (slow decay: the maps and states keep full range);
         # the kernels do the same work whatever the gate values, so this should match
         extra["alpha_near_one"] = near_one_timing(wl, dev, ms_step, scrub)
@@ -408,6 +410,7 @@ def main():
         "roofline": roofline, "path": path, "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 3), "kernel_source_sha": kernel_source_hash(wl.kind),
         "cache": "1 GiB read before each timed step" if scrub else "working set above the caches",
+        "gates": args.gates,
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
