@@ -35,5 +35,7 @@ WORKLOADS = {
         Workload("stream_denoise_b16", 4, "stream", 16, 20, 1, 880, 112, "bf16", state_std=0.1, steps=50),
         Workload("gdn_720p_60s_token", 5, "token", 1, 20, 240, 880, 112, "bf16"),
         Workload("softmax_720p_5s", 6, "softmax", 1, 20, 21, 880, 112, "bf16"),
+        # one GPU's share of the 60 s rollout split into 8 frame ranges (30 frames each)
+        Workload("gdn_720p_60s_share8", 7, "gdn", 1, 20, 30, 880, 112, "bf16"),
     ]
 }
