@@ -12,10 +12,10 @@
 // of one (b, h) per wave and streams the keys it needs -- those up to the end of its last
 // query's frame -- in blocks of 64 through LDS (global -> LDS copies; the next block's
 // copies in flight while this one is used).  Per block and wave, on the matrix cores:
-//   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d; K rows read as 16-byte pieces): the
-//                 accumulator gives each lane
-//                 one query column, 16 of its keys, so the row maximum needs two lane
-//                 exchanges and the row sums none until the end;
+//   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d; K rows read as 16-byte pieces):
+//                 the accumulator gives each lane one query column, 16 of its keys, so
+//                 the row maximum needs two lane exchanges and the row sums none until
+//                 the end;
 //   O^T += V^T P^T (d tiles x 2 query tiles, k = the 64 keys): the probabilities enter
 //                 as the B operand straight from the S^T registers (PAIR slot map), V^T
 //                 comes from transposed LDS reads.
@@ -50,10 +50,11 @@ struct SAArgs {
     int out_f32;
 };
 
-// LDS layout (float32 blocks are large enough that one workgroup fills a CU, hence the
-// launch bound of one for them): K and V blocks of 64 keys, row-major with the row pitch rule of the other
+// LDS layout: K and V blocks of 64 keys, row-major with the row pitch rule of the other
 // kernels (bf16 rows span an odd number of 32-byte units: conflict-free transposed
-// reads), two blocks of each in flight.
+// reads), two buffers of each (the block in use, the next block's copies).  One
+// workgroup per CU (launch bound one): bf16's eight waves take the register file at two
+// waves per SIMD, float32's blocks most of the LDS.
 template <typename E, int ND> struct SAL {
     static constexpr bool BF = sizeof(E) == 2;
     static constexpr int RB = 16 * ND * (int)sizeof(E);
