@@ -25,6 +25,10 @@
  *      S_f = S_in + sum_{g<=f} phi(K_g)^T V_g   (d_k x d_v),   z_f = z_in + sum phi(k)
  *      o_t = phi(q_t)^T S_f / (phi(q_t) . z_f + 1e-6)
  *
+ *  Frame-block-causal softmax attention (the softmax layers interleaved with the
+ *  Gated DeltaNet in the hybrid mixer; see softmax_attn_block_causal below): exact
+ *  softmax over the keys of the query's own and earlier frames.
+ *
  * Conventions shared by every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller; `dims` is a HOST pointer.
  *  - Layouts are contiguous row-major: q, k, out [B, H, T, d]; v [B, H, T, d_v];
