@@ -14,14 +14,14 @@
 // copies in flight while this one is used).  Per block and wave, on the matrix cores:
 //   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d; K rows read as 16-byte pieces):
 //                 the accumulator gives each lane one query column, 16 of its keys, so
-//                 the row maximum needs two lane exchanges and the row sums none until
-//                 the end;
+//                 the row maximum needs two lane exchanges;
 //   O^T += V^T P^T (d tiles x 2 query tiles, k = the 64 keys): the probabilities enter
 //                 as the B operand straight from the S^T registers (PAIR slot map), V^T
 //                 comes from transposed LDS reads.
 // Online softmax in base 2 (logits scaled by s log2 e), in float32, with a reference point
 // that moves only when a score exceeds it by more than 2^8 (weights <= 256); P is rounded
-// to the operand type (bf16 for bf16 inputs) before the product, the row sums are not.  Blocks
+// to the operand type (bf16 for bf16 inputs) before the product, and the row sums are
+// taken on the matrix cores from the same rounded weights.  Blocks
 // past every query of a wave are skipped (the mask's own structure, not the data), and
 // only blocks that straddle a query's frame end are masked element by element.
 // Workgroups are dispatched heaviest first: the last query tiles of every head, which
@@ -89,14 +89,6 @@ __device__ __forceinline__ float across_g_max(float x) {
     y = x;
     __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
     return fmaxf(x, y);
-}
-__device__ __forceinline__ float across_g_sum(float x) {
-    float y = x;
-    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-    x = x + y;
-    y = x;
-    __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-    return x + y;
 }
 
 template <typename E, int ND>
@@ -178,7 +170,13 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int t = 0; t < ND; ++t) acc[qt][t] = zero4();
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY};
+    // row sums on the matrix cores: a ones operand times the same (rounded) probabilities
+    // that enter the PV product; every row of lsum[qt] holds query c's sum
+    f32x4 lsum[2] = {zero4(), zero4()};
+    F8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (E)1.f;
 
     for (int b = 0; b < nblk; ++b) {
         // this wave's copies of block b done (and the Q loads); those of the next block
@@ -238,21 +236,15 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
                 const float mn = fmaxf(m[qt], mc);
                 const float corr = hw_exp2(m[qt] - mn);
                 m[qt] = mn;
-                l[qt] *= corr;
+                lsum[qt] *= corr;
 #pragma unroll
                 for (int t = 0; t < ND; ++t) acc[qt][t] *= corr;
             }
             const float mn = m[qt];
-            float ls = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = hw_exp2(__builtin_fmaf(s[qt][kt][i], a.sl2e, -mn));
-                    s[qt][kt][i] = p;
-                    ls += p;
-                }
-            l[qt] += ls;
+                for (int i = 0; i < 4; ++i) s[qt][kt][i] = hw_exp2(__builtin_fmaf(s[qt][kt][i], a.sl2e, -mn));
             pf[qt][0] = O::pack8(s[qt][0], s[qt][1]);
             pf[qt][1] = O::pack8(s[qt][2], s[qt][3]);
         }
@@ -268,12 +260,15 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
                 for (int qt = 0; qt < 2; ++qt) acc[qt][t] = O::mma32(vf, pf[qt][st], acc[qt][t]);
             }
         }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) lsum[qt] = O::mma32(ones, pf[qt][st], lsum[qt]);
     }
     if (!active) return;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        const float lt = across_g_sum(l[qt]);
-        const float inv = 1.f / lt;
+        const float inv = 1.f / lsum[qt][0];
         const long long qi = qw0 + 16 * qt + c;
         if (qi >= a.Tq) continue;
         const long long o = ((long long)bh * a.Tq + qi) * D + 4 * g;
