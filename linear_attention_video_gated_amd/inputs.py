@@ -22,7 +22,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "alpha": 3, "beta": 4, "state": 5, "z": 6}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "alpha": 3, "beta": 4, "state": 5, "z": 6, "x": 7, "w": 8, "bias": 9,
+              "carry": 10}
 
 
 def seed_for(workload_id: int, tensor: str, step: int = 0) -> int:
@@ -97,3 +98,16 @@ def softmax_inputs(B, H, n_frames, kv_frames, frame_len, d, dtype=torch.bfloat16
     k = _normal((B, H, Tk, d), seed_for(workload_id, "k", step), device)
     v = _normal((B, H, Tk, dv), seed_for(workload_id, "v", step), device)
     return {"q": q.to(dtype).contiguous(), "k": k.to(dtype).contiguous(), "v": v.to(dtype).contiguous()}
+
+
+def tconv_inputs(B, n_frames, frame_len, channels, dtype=torch.bfloat16, workload_id=8, step=0, device="cpu",
+                 carry=True):
+    """Inputs of the causal temporal convolution: x ~ N(0,1) [B, F, P, C] and the carried
+    last frame of the previous block ~ N(0,1) [B, P, C] (None without a carry), both in
+    dtype; random-init parameters w ~ N(0, 1/3) [3, C] and bias ~ N(0, 0.1^2) [C], float32."""
+    x = _normal((B, n_frames, frame_len, channels), seed_for(workload_id, "x", step), device)
+    w = _normal((3, channels), seed_for(workload_id, "w", step), device) / 3 ** 0.5
+    bias = 0.1 * _normal((channels,), seed_for(workload_id, "bias", step), device)
+    c = _normal((B, frame_len, channels), seed_for(workload_id, "carry", step), device) if carry else None
+    return {"x": x.to(dtype).contiguous(), "w": w.contiguous(), "bias": bias.contiguous(),
+            "carry_in": None if c is None else c.to(dtype).contiguous()}

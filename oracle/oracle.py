@@ -56,6 +56,8 @@ def _load():
             lib.oracle_softmax_attn_block_causal.argtypes = [fp, fp, fp, dp, i, i, i, i, i, i, i,
                                                              ctypes.c_double, i]
             lib.oracle_softmax_attn_block_causal.restype = i
+            lib.oracle_temporal_conv_block.argtypes = [fp, fp, fp, fp, dp, dp, i, i, i, i]
+            lib.oracle_temporal_conv_block.restype = i
             _lib = lib
     return _lib
 
@@ -162,3 +164,29 @@ def softmax_attn_block_causal(q, k, v, n_frames, kv_frames, frame_len, scale=0.0
     if rc != 0:
         raise RuntimeError("oracle_softmax_attn_block_causal failed (%d)" % rc)
     return out
+
+
+def temporal_conv_block(x, w, bias=None, carry_in=None):
+    """Causal temporal convolution of one block with its carry (see ``oracle_gdn.c``).
+
+    x: [B, F, P, C]; w: [3, C]; bias: [C] or None; carry_in: [B, P, C] or None.
+    Returns (y [B, F, P, C], carry_out [B, P, C]) float64.
+    """
+    lib = _load()
+    x, w = _f32(x), _f32(w)
+    B, F, P, C = x.shape
+    if w.shape != (3, C):
+        raise ValueError("w must be [3, C]")
+    bias, carry_in = _f32(bias), _f32(carry_in)
+    if bias is not None and bias.shape != (C,):
+        raise ValueError("bias must be [C]")
+    if carry_in is not None and carry_in.shape != (B, P, C):
+        raise ValueError("carry_in must be [B, P, C]")
+    y = np.zeros((B, F, P, C), dtype=np.float64)
+    carry = np.zeros((B, P, C), dtype=np.float64)
+    rc = lib.oracle_temporal_conv_block(_ptr(x, ctypes.c_float), _ptr(carry_in, ctypes.c_float),
+                                        _ptr(w, ctypes.c_float), _ptr(bias, ctypes.c_float),
+                                        _ptr(y, ctypes.c_double), _ptr(carry, ctypes.c_double), B, F, P, C)
+    if rc != 0:
+        raise RuntimeError("oracle_temporal_conv_block failed (%d)" % rc)
+    return y, carry

@@ -309,3 +309,45 @@ int oracle_softmax_attn_block_causal(const float* q, const float* k, const float
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Causal temporal convolution with a block carry: the temporal convolution of the
+ * causal FFN ("SANA-Video ... Block Linear Diffusion Transformer" talk, the segment on
+ * a causal FFN with temporal convolution, two-block example).  During training a zero
+ * token is padded between consecutive blocks, so a block never sees the next one, and
+ * the last token of block i-1 is cached as block i's first token, so a block does see
+ * the one before it.  The pages give neither the kernel size nor the weights.  Reading
+ * taken: a depthwise convolution along the frame axis with three taps centred on the
+ * frame (the zero token and the cached token are each one frame wide), weights w[3][C]
+ * and bias[C] given by the caller.  For a block of F frames, per (b, position p,
+ * channel c):
+ *   prev(f) = f > 0 ? x[f-1] : carry_in (zero when there is none)
+ *   next(f) = f < F-1 ? x[f+1] : 0       (the zero token after the block)
+ *   y[f]    = w[0][c] prev(f) + w[1][c] x[f] + w[2][c] next(f) + bias[c]
+ *   carry_out = x[F-1]                    (the next block's cached token)
+ * x, y [B, F, P, C]; carry_in, carry_out [B, P, C]; bias may be NULL.
+ * Returns 0, or -1 on bad sizes.
+ */
+int oracle_temporal_conv_block(const float* x, const float* carry_in, const float* w,
+                               const float* bias, double* y, double* carry_out,
+                               int B, int F, int P, int C)
+{
+    if (B < 0 || F < 0 || P < 0 || C < 0) return -1;
+    const size_t frame = (size_t)P * C;
+    for (int b = 0; b < B; ++b) {
+        const float* xb = x + (size_t)b * F * frame;
+        double* yb = y + (size_t)b * F * frame;
+        for (size_t e = 0; e < frame; ++e) {
+            const int c = (int)(e % (size_t)C);
+            for (int f = 0; f < F; ++f) {
+                const double prev = f > 0 ? (double)xb[(size_t)(f - 1) * frame + e]
+                                          : (carry_in ? (double)carry_in[(size_t)b * frame + e] : 0.0);
+                const double next = f < F - 1 ? (double)xb[(size_t)(f + 1) * frame + e] : 0.0;
+                yb[(size_t)f * frame + e] = (double)w[c] * prev + (double)w[C + c] * (double)xb[(size_t)f * frame + e]
+                                          + (double)w[2 * C + c] * next + (bias ? (double)bias[c] : 0.0);
+            }
+            if (carry_out && F > 0) carry_out[(size_t)b * frame + e] = (double)xb[(size_t)(F - 1) * frame + e];
+        }
+    }
+    return 0;
+}

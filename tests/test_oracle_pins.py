@@ -425,3 +425,61 @@ def test_softmax_shift_scale_and_large_logits():
         best = np.argmax(np.einsum("bhd,bhjd->bhj", q[:, :, i], x["k"][:, :, :nvis]), axis=-1)
         want = np.take_along_axis(x["v"][:, :, :nvis], best[..., None, None], axis=2)[:, :, 0]
         np.testing.assert_allclose(o3[:, :, i], want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- causal temporal convolution
+def _tc_rand(B=2, F=4, P=3, C=5, seed=81, carry=True):
+    from linear_attention_video_gated_amd.inputs import tconv_inputs
+    inp = tconv_inputs(B, F, P, C, dtype=torch.float32, workload_id=seed, carry=carry)
+    return {k: (None if v is None else v.numpy().astype(np.float64)) for k, v in inp.items()}
+
+
+def test_tconv_special_taps():
+    x = _tc_rand()
+    C = x["x"].shape[-1]
+    eye = lambda j: np.stack([np.full(C, 1.0 if i == j else 0.0) for i in range(3)])
+    # centre tap: identity; the carry out is the block's last frame
+    y, c = oracle.temporal_conv_block(x["x"], eye(1), carry_in=x["carry_in"])
+    np.testing.assert_array_equal(y, x["x"])
+    np.testing.assert_array_equal(c, x["x"][:, -1])
+    # left tap: the previous frame, the carried one for frame 0
+    y, _ = oracle.temporal_conv_block(x["x"], eye(0), carry_in=x["carry_in"])
+    np.testing.assert_array_equal(y[:, 1:], x["x"][:, :-1])
+    np.testing.assert_array_equal(y[:, 0], x["carry_in"])
+    y, _ = oracle.temporal_conv_block(x["x"], eye(0))  # no carry: zero before the first block
+    np.testing.assert_array_equal(y[:, 0], 0 * x["x"][:, 0])
+    # right tap: the next frame, the zero token after the last one
+    y, _ = oracle.temporal_conv_block(x["x"], eye(2), carry_in=x["carry_in"])
+    np.testing.assert_array_equal(y[:, :-1], x["x"][:, 1:])
+    np.testing.assert_array_equal(y[:, -1], 0 * x["x"][:, -1])
+    # bias only
+    y, _ = oracle.temporal_conv_block(x["x"], 0 * eye(0), bias=x["bias"], carry_in=x["carry_in"])
+    np.testing.assert_allclose(y, np.broadcast_to(x["bias"], y.shape), rtol=0, atol=1e-7)
+
+
+def test_tconv_blocks_equal_the_training_sequence():
+    """The talk's training form: blocks concatenated with a zero token after each block and
+    the previous block's last token before each later block, one 'same'-padded convolution
+    over the whole sequence (scipy's correlate1d, zeros outside), the inserted tokens then
+    removed -- equals block-by-block calls that carry the last frame."""
+    from scipy.ndimage import correlate1d
+    blocks = [_tc_rand(B=1, F=F, P=2, C=3, seed=90 + i, carry=False)["x"] for i, F in enumerate((3, 1, 4))]
+    prm = _tc_rand(B=1, F=1, P=2, C=3, seed=99)
+    w, bias = prm["w"], prm["bias"]
+    seq, keep = [], []
+    for i, blk in enumerate(blocks):
+        if i > 0:
+            seq.append(blocks[i - 1][:, -1:])  # cached last token of the previous block
+            keep.append(False)
+        seq.append(blk)
+        keep += [True] * blk.shape[1]
+        seq.append(np.zeros_like(blk[:, :1]))  # zero token after the block
+        keep.append(False)
+    seq = np.concatenate(seq, axis=1)
+    ref = np.stack([correlate1d(seq[..., c], w[:, c], axis=1, mode="constant", cval=0.0) for c in range(3)], -1)
+    ref = ref[:, np.array(keep)] + bias
+    outs, carry = [], None
+    for blk in blocks:
+        y, carry = oracle.temporal_conv_block(blk, w, bias=bias, carry_in=carry)
+        outs.append(y)
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), ref, rtol=1e-6, atol=1e-6)
