@@ -34,11 +34,12 @@ KERNEL_SOURCES = {
     "gdn": [_CSRC + f for f in ("gdn_frame.hip", "gdn_api.hip", "gdn_kernels.hpp", "common.hpp")],
     "block_causal": [_CSRC + f for f in ("block_causal.hip", "common.hpp")],
     "softmax": [_CSRC + f for f in ("softmax_attn.hip", "common.hpp")],
+    "tconv": [_CSRC + f for f in ("temporal_conv.hip", "common.hpp")],
 }
 
 
 def kernel_family(kind):
-    return kind if kind in ("block_causal", "softmax") else "gdn"
+    return kind if kind in ("block_causal", "softmax", "tconv") else "gdn"
 
 # Per-kernel algorithmic bytes per token-head (d, element size es):
 #   gdn_frame_affine  reads k, v and the two gates:  2*d*es + 8
@@ -51,6 +52,8 @@ GDN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_frame_readout")
 TOKEN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_token_readout")
 BC_KERNELS = ("bc_partial", "bc_scan", "bc_readout")
 SA_KERNELS = ("sa_fwd",)
+TC_KERNELS = ("tconv_block",)
+METRIC_TC = "causal temporal convolution with block carry tokens/s (720p 5s, C=2240) + % of HBM roofline"
 METRIC_SA = "frame-block-causal softmax attention fwd tokens/s (720p 5s, H=20 d=112) + % of bf16 MFMA peak"
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks of MI355X
 
@@ -73,6 +76,8 @@ def kernel_bytes_per_token_head(kind, d, es):
 
 def path_bytes_per_token_head(kind, d, es):
     """Algorithmic bytes per token-head of the whole path: q, k, v, o (and the gates)."""
+    if kind == "tconv":  # x read and y written, per token of the H * d channels
+        return 2 * d * es
     return 4 * d * es + (0 if kind in ("block_causal", "softmax") else 8)
 
 
@@ -140,6 +145,10 @@ def setup(wl, device, gates="config"):
     import torch
     from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs, softmax_inputs
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if wl.kind == "tconv":
+        from linear_attention_video_gated_amd.inputs import tconv_inputs
+        return tconv_inputs(wl.B, wl.n_frames, wl.frame_len, wl.H * wl.d, dtype=dt, workload_id=wl.wid,
+                            device=device)
     if wl.kind == "softmax":
         return softmax_inputs(wl.B, wl.H, wl.n_frames, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
                               workload_id=wl.wid, device=device)
@@ -207,6 +216,12 @@ def make_step(wl, inp, events=None):
     """One pass of the hot path: a closure that enqueues it on the current stream."""
     from linear_attention_video_gated_amd import gdn
     import torch
+    if wl.kind == "tconv":
+        x = inp["x"]
+        y = torch.empty_like(x)
+        co = torch.empty_like(inp["carry_in"])
+        return lambda ev=None: gdn.temporal_conv_block(x, inp["w"], inp["bias"], carry_in=inp["carry_in"],
+                                                       carry_out=co, out=y, events=ev)
     q, k, v = inp["q"], inp["k"], inp["v"]
     out = torch.empty_like(q)
     if wl.kind == "softmax":
@@ -269,6 +284,15 @@ def cpu_baseline(wl, inp, budget_heads=16, frames=None):
     heads = min(wl.H, budget_heads)
     frames = wl.n_frames if frames is None else min(frames, wl.n_frames)
     T = frames * wl.frame_len
+    if wl.kind == "tconv":  # the whole block: one pass over x
+        x = inp["x"].float().cpu().numpy()
+        c = inp["carry_in"].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.temporal_conv_block(x, inp["w"].cpu().numpy(), bias=inp["bias"].cpu().numpy(), carry_in=c)
+        dt = time.perf_counter() - t0
+        return {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "the whole block (%d frames x %d positions x %d channels, %.1f s, float64, one thread)"
+                          % (wl.n_frames, wl.frame_len, wl.H * wl.d, dt)}
     take = lambda x: x[:1, :heads, :T].detach().float().cpu().numpy() if x is not None else None
     q, k, v = take(inp["q"]), take(inp["k"]), take(inp["v"])
     t0 = time.perf_counter()
@@ -331,7 +355,7 @@ def main():
     dt = _t.bfloat16 if wl.dtype == "bf16" else _t.float32
     entry = {"block_causal": gdn.ENTRY_BLOCK_CAUSAL, "stream": gdn.ENTRY_READONLY,
              "token": gdn.ENTRY_TOKEN}.get(wl.kind, gdn.ENTRY_FORWARD)
-    if wl.kind == "softmax":  # one launch per call
+    if wl.kind in ("softmax", "tconv"):  # one launch per call
         nk, nwin = 1, 1
     else:
         nwin = gdn.window_count(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
@@ -342,7 +366,8 @@ def main():
     t_wall0 = time.perf_counter()
     ms_step = time_steps(step, args.steps, scrub, ev)
     t_wall = time.perf_counter() - t_wall0
-    names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS, "softmax": SA_KERNELS}.get(wl.kind, GDN_KERNELS)
+    names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS, "softmax": SA_KERNELS,
+             "tconv": TC_KERNELS}.get(wl.kind, GDN_KERNELS)
     kms = [0.0] * nk  # per call, summed over the call's windows
     for e in ev:
         for wi in range(nwin):
@@ -369,6 +394,13 @@ def main():
         roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                     "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_flops": flops}
+    elif wl.kind == "tconv":
+        # x read, y written, carry read and written: algorithmic bytes of the block
+        kbytes = (2 * wl.n_frames + 2) * wl.B * wl.frame_len * wl.H * wl.d * es
+        achieved = kbytes / (kms_launch * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_bytes": kbytes}
     else:
         per = kernel_bytes_per_token_head(wl.kind, wl.d, es)
         # one launch per window: algorithmic bytes and duration per launch (window sizes are
@@ -400,7 +432,7 @@ def main():
         cpu = cpu_baseline(wl, inp, budget_heads=4 if wl.kind == "softmax" else 16)
 
     line = {
-        "metric": METRIC_SA if wl.kind == "softmax" else METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": {"softmax": METRIC_SA, "tconv": METRIC_TC}.get(wl.kind, METRIC), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes of 720p/480p latent frames)",

@@ -29,6 +29,9 @@
  *  Gated DeltaNet in the hybrid mixer; see softmax_attn_block_causal below): exact
  *  softmax over the keys of the query's own and earlier frames.
  *
+ *  Causal temporal convolution with a block carry (the causal FFN's temporal
+ *  convolution; see temporal_conv_block below).
+ *
  * Conventions shared by every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller; `dims` is a HOST pointer.
  *  - Layouts are contiguous row-major: q, k, out [B, H, T, d]; v [B, H, T, d_v];
@@ -69,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -190,6 +193,30 @@ int linear_attn_block_causal(const void* q, const void* k, const void* v,
  */
 int softmax_attn_block_causal(const void* q, const void* k, const void* v, void* out,
                               int32_t kv_frames, const gdn_dims_t* dims, void* stream);
+
+/*
+ * Causal temporal convolution of one block of frames, with the carry between blocks: the
+ * temporal convolution of the causal FFN ("SANA-Video ... Block Linear Diffusion
+ * Transformer" talk, segment on a causal FFN with temporal convolution: a zero token
+ * follows each block in training, so a block never sees the next one, and the previous
+ * block's last token is cached as its first, so it sees the one before).  The pages fix
+ * neither kernel size nor weights; this entry computes a depthwise, three-tap convolution
+ * along frames, per (b, position p, channel c), for the block's frames f = 0..F-1:
+ *     y[f] = w[0][c] prev(f) + w[1][c] x[f] + w[2][c] next(f) + bias[c]
+ *     prev(0) = carry_in (0 when NULL),  next(F-1) = 0,  carry_out = x[F-1]
+ *  x, y      [B, F, P, C] dtype (y float32 with GDN_F_OUT_F32), F = n_frames, P = frame_len
+ *  carry_in  [B, P, C] dtype or NULL;  carry_out [B, P, C] dtype or NULL, may equal
+ *            carry_in (with F = 0 it receives carry_in, or zeros)
+ *  weight    [3, C] float32 (taps for the previous, the same and the next frame);
+ *            bias [C] float32 or NULL
+ *  C must be a multiple of 8 (bf16) or 4 (float32).  events (may be NULL): two hipEvent_t
+ *  recorded just before and after the single launch.  Allowed flags: GDN_F_OUT_F32.
+ *  y must not overlap x or the carries (GDN_ERR_ALIAS).
+ */
+int temporal_conv_block(const void* x, const void* carry_in, const float* weight,
+                        const float* bias, void* y, void* carry_out, int32_t B,
+                        int32_t n_frames, int32_t frame_len, int32_t channels,
+                        int32_t dtype, uint32_t flags, void* const* events, void* stream);
 
 /* Bytes of workspace the entry (GDN_ENTRY_*) needs for these dims; 0 on invalid dims.
  * Bounded independently of n_frames. */

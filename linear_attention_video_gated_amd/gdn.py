@@ -19,7 +19,7 @@ GDN_BF16, GDN_F32 = 0, 1
 NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS = 1, 2, 4, 8, 16
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
 EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
-           "softmax_attn_block_causal", "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
+           "softmax_attn_block_causal", "temporal_conv_block", "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -63,6 +63,9 @@ def lib():
         L.linear_attn_block_causal.restype = ctypes.c_int
         L.softmax_attn_block_causal.argtypes = [vp, vp, vp, vp, ctypes.c_int32, dp, vp]
         L.softmax_attn_block_causal.restype = ctypes.c_int
+        i32 = ctypes.c_int32
+        L.temporal_conv_block.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_uint32, vp, vp]
+        L.temporal_conv_block.restype = ctypes.c_int
         L.gdn_workspace_bytes.argtypes = [dp, ctypes.c_int]
         L.gdn_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_window_count.argtypes = [dp, ctypes.c_int]
@@ -270,3 +273,30 @@ def softmax_attn_block_causal(q, k, v, n_frames, kv_frames, frame_len, out=None,
     _check(lib().softmax_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(kv_frames),
                                            ctypes.byref(dims), _stream(q.device, stream)))
     return out
+
+
+def temporal_conv_block(x, weight, bias=None, carry_in=None, carry_out=None, out=None, stream=None,
+                        out_dtype=None, events=None, return_carry=True):
+    """temporal_conv_block: x [B, F, P, C] (bf16 or float32), weight [3, C] and bias [C]
+    float32, carry_in [B, P, C] in x's dtype or None.  Returns (y, carry_out)."""
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, F, P, C] device tensor")
+    B, F, P, C = x.shape
+    if carry_in is not None and (tuple(carry_in.shape) != (B, P, C) or carry_in.dtype != x.dtype
+                                 or not carry_in.is_contiguous()):
+        raise ValueError("carry_in must be a contiguous [B, P, C] tensor of x's dtype")
+    weight = _f32(weight, (3, C), "weight")
+    bias = _f32(bias, (C,), "bias")
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if tuple(out.shape) != tuple(x.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like x")
+    flags = OUT_F32 if out.dtype == torch.float32 and x.dtype != torch.float32 else 0
+    if out.dtype not in (x.dtype, torch.float32):
+        raise ValueError("out must have x's dtype or float32")
+    if carry_out is None and return_carry:
+        carry_out = torch.empty((B, P, C), dtype=x.dtype, device=x.device)
+    ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
+    _check(lib().temporal_conv_block(_ptr(x), _ptr(carry_in), _ptr(weight), _ptr(bias), _ptr(out), _ptr(carry_out),
+                                     B, F, P, C, _dtype_code(x.dtype), flags, ev, _stream(x.device, stream)))
+    return out, carry_out

@@ -11,6 +11,7 @@ class Workload:
     wid: int            # seed key
     kind: str           # "gdn" | "block_causal" | "stream" | "token" (per-token readout)
                         # | "softmax" (frame-block-causal softmax attention)
+                        # | "tconv" (causal temporal convolution, channels H * d)
     B: int
     H: int
     n_frames: int
@@ -37,5 +38,7 @@ WORKLOADS = {
         Workload("softmax_720p_5s", 6, "softmax", 1, 20, 21, 880, 112, "bf16"),
         # one GPU's share of the 60 s rollout split into 8 frame ranges (30 frames each)
         Workload("gdn_720p_60s_share8", 7, "gdn", 1, 20, 30, 880, 112, "bf16"),
+        # causal temporal convolution over one block: channels = H * d = 2240
+        Workload("tconv_720p_5s", 8, "tconv", 1, 20, 21, 880, 112, "bf16"),
     ]
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 4
+    assert gdn.lib().gdn_abi_version() == 5
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
@@ -191,3 +191,23 @@ def test_softmax_attention_size_limits():
     assert sa(dm, kv_frames=1 << 10) == -2
     dm = dims(flags=0, B=65535, H=65535, F=1, N=128, d=16)
     assert sa(dm) == -2
+
+
+def test_temporal_conv_argument_checks():
+    """Every call here is rejected (or has nothing to do) before any launch."""
+    L = gdn.lib()
+    tc = lambda B=1, F=3, P=4, C=16, dtype=gdn.GDN_BF16, flags=0, x=FAKE, cin=None, w=FAKE + 2 ** 30, b=None, \
+        y=FAKE + 2 ** 31, cout=None: L.temporal_conv_block(x, cin, w, b, y, cout, B, F, P, C, dtype, flags, None, None)
+    assert tc(dtype=5) == -3
+    assert tc(F=-1) == -2
+    assert tc(flags=gdn.NORMALIZE_K) == -7
+    assert tc(C=12) == -7                      # bf16 channels come in groups of 8
+    assert tc(C=12, dtype=gdn.GDN_F32, w=None) == -1  # float32: groups of 4 (then the NULL weight)
+    assert tc(w=None) == -1
+    assert tc(x=None) == -1
+    assert tc(x=FAKE + 8) == -4
+    assert tc(y=FAKE + 64) == -5                # y inside x
+    assert tc(B=0) == 0 and tc(P=0, x=None, y=None) == 0
+    # an empty block needs no x or y (it only passes the carry on): past the NULL check,
+    # stopped by the misaligned carry_out
+    assert tc(F=0, x=None, y=None, cout=FAKE + 2 ** 32 + 8) == -4
