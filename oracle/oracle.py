@@ -58,6 +58,8 @@ def _load():
             lib.oracle_softmax_attn_block_causal.restype = i
             lib.oracle_temporal_conv_block.argtypes = [fp, fp, fp, fp, dp, dp, i, i, i, i]
             lib.oracle_temporal_conv_block.restype = i
+            lib.oracle_rope3d.argtypes = [fp, dp, i, i, i, i, i, i, i, i, i, ctypes.c_double]
+            lib.oracle_rope3d.restype = i
             _lib = lib
     return _lib
 
@@ -190,3 +192,19 @@ def temporal_conv_block(x, w, bias=None, carry_in=None):
     if rc != 0:
         raise RuntimeError("oracle_temporal_conv_block failed (%d)" % rc)
     return y, carry
+
+
+def rope3d(x, n_frames, grid_h, grid_w, d_t, d_h, frame_offset=0, base=10000.0):
+    """3D rotary position embedding (see ``oracle_gdn.c``): x [B, H, T, d],
+    T = n_frames * grid_h * grid_w.  Returns the rotated tensor, float64."""
+    lib = _load()
+    x = _f32(x)
+    B, H, T, d = x.shape
+    if T != n_frames * grid_h * grid_w:
+        raise ValueError("T must be n_frames * grid_h * grid_w")
+    y = np.zeros(x.shape, dtype=np.float64)
+    rc = lib.oracle_rope3d(_ptr(x, ctypes.c_float), _ptr(y, ctypes.c_double), B, H, n_frames, grid_h, grid_w, d,
+                           d_t, d_h, frame_offset, float(base))
+    if rc != 0:
+        raise RuntimeError("oracle_rope3d failed (%d)" % rc)
+    return y

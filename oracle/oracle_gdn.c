@@ -351,3 +351,42 @@ int oracle_temporal_conv_block(const float* x, const float* carry_in, const floa
     }
     return 0;
 }
+
+/*
+ * 3D rotary position embedding on q or k: "SANA-Video ... Block Linear Diffusion
+ * Transformer" talk, the segment on temporal modelling (a 3D RoPE for the linear
+ * attention).  The pages give no frequency layout, split of the head dimension or base.
+ * Reading taken: the axial form -- the head dimension is cut into three contiguous
+ * parts of d_t, d_h and d_w = d - d_t - d_h dimensions (all even, given by the caller),
+ * rotated by the token's frame index, latent row and latent column respectively; inside
+ * a part of size n, the pair (2i, 2i+1) turns by the angle pos * base^(-2i/n):
+ *   (x_{2i}, x_{2i+1}) <- (x_{2i} cos a - x_{2i+1} sin a,  x_{2i} sin a + x_{2i+1} cos a).
+ * Token t of a [B, H, T, d] tensor, T = n_frames * grid_h * grid_w, sits at frame
+ * frame_offset + t / (grid_h grid_w), row (t mod grid_h grid_w) / grid_w, column t mod
+ * grid_w.  Returns 0, or -1 on bad sizes.
+ */
+int oracle_rope3d(const float* x, double* y, int B, int H, int n_frames, int grid_h, int grid_w,
+                  int d, int d_t, int d_h, int frame_offset, double base)
+{
+    const int d_w = d - d_t - d_h;
+    if (B < 0 || H < 0 || n_frames < 0 || grid_h < 1 || grid_w < 1 || d_t < 0 || d_h < 0 || d_w < 0 ||
+        (d_t | d_h | d_w) & 1 || base <= 0.0)
+        return -1;
+    const long long per_frame = (long long)grid_h * grid_w, T = (long long)n_frames * per_frame;
+    for (long long r = 0; r < (long long)B * H * T; ++r) {
+        const long long t = r % T;
+        const long long pos[3] = {frame_offset + t / per_frame, (t % per_frame) / grid_w, t % grid_w};
+        const int start[3] = {0, d_t, d_t + d_h}, size[3] = {d_t, d_h, d_w};
+        const float* xr = x + r * d;
+        double* yr = y + r * d;
+        for (int ax = 0; ax < 3; ++ax) {
+            for (int i = 0; 2 * i < size[ax]; ++i) {
+                const double ang = (double)pos[ax] * pow(base, -2.0 * i / size[ax]);
+                const double x0 = xr[start[ax] + 2 * i], x1 = xr[start[ax] + 2 * i + 1];
+                yr[start[ax] + 2 * i] = x0 * cos(ang) - x1 * sin(ang);
+                yr[start[ax] + 2 * i + 1] = x0 * sin(ang) + x1 * cos(ang);
+            }
+        }
+    }
+    return 0;
+}

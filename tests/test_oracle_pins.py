@@ -483,3 +483,41 @@ def test_tconv_blocks_equal_the_training_sequence():
         y, carry = oracle.temporal_conv_block(blk, w, bias=bias, carry_in=carry)
         outs.append(y)
     np.testing.assert_allclose(np.concatenate(outs, axis=1), ref, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- 3D rotary position embedding
+def _rope_x(B=1, H=2, F=3, gh=2, gw=3, d=16, seed=95):
+    g = np.random.default_rng(seed)
+    return g.standard_normal((B, H, F * gh * gw, d)).astype(np.float32).astype(np.float64)
+
+
+def test_rope3d_rotations():
+    F, gh, gw, d, dt, dh = 3, 2, 3, 16, 4, 6
+    x = _rope_x(F=F, gh=gh, gw=gw, d=d)
+    y = oracle.rope3d(x, F, gh, gw, dt, dh)
+    # a rotation of every pair: norms of each pair kept
+    pn = lambda z: z[..., 0::2] ** 2 + z[..., 1::2] ** 2
+    np.testing.assert_allclose(pn(y), pn(x), rtol=1e-12, atol=1e-12)
+    # token 0 of frame 0 sits at the origin: unchanged
+    np.testing.assert_allclose(y[:, :, 0], x[:, :, 0], rtol=0, atol=1e-15)
+    # pair 0 of each part turns by the position itself (frequency base^0 = 1): token 5 is
+    # frame 0, row 1, column 2
+    t, pos = 5, {0: 0, dt: 1, dt + dh: 2}
+    for s0, p0 in pos.items():
+        c, s = np.cos(p0), np.sin(p0)
+        x0, x1 = x[:, :, t, s0], x[:, :, t, s0 + 1]
+        np.testing.assert_allclose(y[:, :, t, s0], x0 * c - x1 * s, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y[:, :, t, s0 + 1], x0 * s + x1 * c, rtol=1e-12, atol=1e-12)
+
+
+def test_rope3d_relative_positions():
+    """Scores between rotated q and k depend on the two tokens' position difference only:
+    moving every frame by the same offset changes no score."""
+    F, gh, gw, d, dt, dh = 4, 2, 2, 12, 4, 4
+    q, k = _rope_x(F=F, gh=gh, gw=gw, d=d, seed=96), _rope_x(F=F, gh=gh, gw=gw, d=d, seed=97)
+    s0 = np.einsum("bhtd,bhsd->bhts", oracle.rope3d(q, F, gh, gw, dt, dh), oracle.rope3d(k, F, gh, gw, dt, dh))
+    s7 = np.einsum("bhtd,bhsd->bhts", oracle.rope3d(q, F, gh, gw, dt, dh, frame_offset=7),
+                   oracle.rope3d(k, F, gh, gw, dt, dh, frame_offset=7))
+    np.testing.assert_allclose(s7, s0, rtol=1e-10, atol=1e-10)
+    # and the offset does change the rotated vectors themselves
+    assert np.abs(oracle.rope3d(q, F, gh, gw, dt, dh, frame_offset=7) - oracle.rope3d(q, F, gh, gw, dt, dh)).max() > 1e-3
