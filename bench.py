@@ -35,11 +35,12 @@ KERNEL_SOURCES = {
     "block_causal": [_CSRC + f for f in ("block_causal.hip", "common.hpp")],
     "softmax": [_CSRC + f for f in ("softmax_attn.hip", "common.hpp")],
     "tconv": [_CSRC + f for f in ("temporal_conv.hip", "common.hpp")],
+    "rope": [_CSRC + f for f in ("rope3d.hip", "common.hpp")],
 }
 
 
 def kernel_family(kind):
-    return kind if kind in ("block_causal", "softmax", "tconv") else "gdn"
+    return kind if kind in ("block_causal", "softmax", "tconv", "rope") else "gdn"
 
 # Per-kernel algorithmic bytes per token-head (d, element size es):
 #   gdn_frame_affine  reads k, v and the two gates:  2*d*es + 8
@@ -53,6 +54,9 @@ TOKEN_KERNELS = ("gdn_frame_affine", "gdn_frame_chain", "gdn_token_readout")
 BC_KERNELS = ("bc_partial", "bc_scan", "bc_readout")
 SA_KERNELS = ("sa_fwd",)
 TC_KERNELS = ("tconv_block",)
+RP_KERNELS = ("rope3d_apply_kernel",)
+METRIC_RP = "3D rotary position embedding tokens/s (720p 5s q, H=20 d=112, in place) + % of HBM roofline"
+RP_GRID, RP_SPLIT = (22, 40), (36, 38)  # latent rows x columns of a 720p frame; d_t, d_h of d = 112
 METRIC_TC = "causal temporal convolution with block carry tokens/s (720p 5s, C=2240) + % of HBM roofline"
 METRIC_SA = "frame-block-causal softmax attention fwd tokens/s (720p 5s, H=20 d=112) + % of bf16 MFMA peak"
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks of MI355X
@@ -76,7 +80,7 @@ def kernel_bytes_per_token_head(kind, d, es):
 
 def path_bytes_per_token_head(kind, d, es):
     """Algorithmic bytes per token-head of the whole path: q, k, v, o (and the gates)."""
-    if kind == "tconv":  # x read and y written, per token of the H * d channels
+    if kind in ("tconv", "rope"):  # read once and written once, per token-head (tconv: per channel group)
         return 2 * d * es
     return 4 * d * es + (0 if kind in ("block_causal", "softmax") else 8)
 
@@ -145,6 +149,9 @@ def setup(wl, device, gates="config"):
     import torch
     from linear_attention_video_gated_amd.inputs import block_causal_inputs, gdn_inputs, softmax_inputs
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if wl.kind == "rope":
+        return {"x": softmax_inputs(wl.B, wl.H, wl.n_frames, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
+                                    workload_id=wl.wid, device=device)["q"]}
     if wl.kind == "tconv":
         from linear_attention_video_gated_amd.inputs import tconv_inputs
         return tconv_inputs(wl.B, wl.n_frames, wl.frame_len, wl.H * wl.d, dtype=dt, workload_id=wl.wid,
@@ -216,6 +223,9 @@ def make_step(wl, inp, events=None):
     """One pass of the hot path: a closure that enqueues it on the current stream."""
     from linear_attention_video_gated_amd import gdn
     import torch
+    if wl.kind == "rope":  # rotates the same tensor again every call (a rotation keeps it bounded)
+        return lambda ev=None: gdn.rope3d_apply(inp["x"], wl.n_frames, RP_GRID[0], RP_GRID[1], RP_SPLIT[0],
+                                                RP_SPLIT[1], events=ev)
     if wl.kind == "tconv":
         x = inp["x"]
         y = torch.empty_like(x)
@@ -284,6 +294,13 @@ def cpu_baseline(wl, inp, budget_heads=16, frames=None):
     heads = min(wl.H, budget_heads)
     frames = wl.n_frames if frames is None else min(frames, wl.n_frames)
     T = frames * wl.frame_len
+    if wl.kind == "rope":  # 4 of the heads
+        x = inp["x"][:1, :4].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.rope3d(x, wl.n_frames, RP_GRID[0], RP_GRID[1], RP_SPLIT[0], RP_SPLIT[1])
+        dt = time.perf_counter() - t0
+        return {"value": wl.T * 4 / wl.H / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": "B=1, 4 of %d heads, all %d tokens (%.1f s, float64, one thread)" % (wl.H, wl.T, dt)}
     if wl.kind == "tconv":  # the whole block: one pass over x
         x = inp["x"].float().cpu().numpy()
         c = inp["carry_in"].float().cpu().numpy()
@@ -355,7 +372,7 @@ def main():
     dt = _t.bfloat16 if wl.dtype == "bf16" else _t.float32
     entry = {"block_causal": gdn.ENTRY_BLOCK_CAUSAL, "stream": gdn.ENTRY_READONLY,
              "token": gdn.ENTRY_TOKEN}.get(wl.kind, gdn.ENTRY_FORWARD)
-    if wl.kind in ("softmax", "tconv"):  # one launch per call
+    if wl.kind in ("softmax", "tconv", "rope"):  # one launch per call
         nk, nwin = 1, 1
     else:
         nwin = gdn.window_count(wl.B, wl.H, wl.n_frames, wl.frame_len, wl.d, dtype=dt,
@@ -367,7 +384,7 @@ def main():
     ms_step = time_steps(step, args.steps, scrub, ev)
     t_wall = time.perf_counter() - t_wall0
     names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS, "softmax": SA_KERNELS,
-             "tconv": TC_KERNELS}.get(wl.kind, GDN_KERNELS)
+             "tconv": TC_KERNELS, "rope": RP_KERNELS}.get(wl.kind, GDN_KERNELS)
     kms = [0.0] * nk  # per call, summed over the call's windows
     for e in ev:
         for wi in range(nwin):
@@ -394,9 +411,9 @@ def main():
         roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                     "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_flops": flops}
-    elif wl.kind == "tconv":
-        # x read, y written, carry read and written: algorithmic bytes of the block
-        kbytes = (2 * wl.n_frames + 2) * wl.B * wl.frame_len * wl.H * wl.d * es
+    elif wl.kind in ("tconv", "rope"):
+        # tconv: x read, y written, carry read and written; rope: x read and written
+        kbytes = ((2 * wl.n_frames + 2) if wl.kind == "tconv" else 2 * wl.n_frames) * wl.B * wl.frame_len * wl.H * wl.d * es
         achieved = kbytes / (kms_launch * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -432,7 +449,8 @@ def main():
         cpu = cpu_baseline(wl, inp, budget_heads=4 if wl.kind == "softmax" else 16)
 
     line = {
-        "metric": {"softmax": METRIC_SA, "tconv": METRIC_TC}.get(wl.kind, METRIC), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": {"softmax": METRIC_SA, "tconv": METRIC_TC, "rope": METRIC_RP}.get(wl.kind, METRIC),
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes of 720p/480p latent frames)",

@@ -30,7 +30,8 @@
  *  softmax over the keys of the query's own and earlier frames.
  *
  *  Causal temporal convolution with a block carry (the causal FFN's temporal
- *  convolution; see temporal_conv_block below).
+ *  convolution; see temporal_conv_block below) and the 3D rotary position embedding of
+ *  q and k (rope3d_apply).
  *
  * Conventions shared by every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller; `dims` is a HOST pointer.
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
     GDN_OK = 0,
@@ -217,6 +218,24 @@ int temporal_conv_block(const void* x, const void* carry_in, const float* weight
                         const float* bias, void* y, void* carry_out, int32_t B,
                         int32_t n_frames, int32_t frame_len, int32_t channels,
                         int32_t dtype, uint32_t flags, void* const* events, void* stream);
+
+/*
+ * 3D rotary position embedding of q or k, in place ("SANA-Video ... Block Linear Diffusion
+ * Transformer" talk, segment on temporal modelling: a 3D RoPE for the linear attention).
+ * The pages fix neither the frequency layout nor the split of d nor the base; this entry
+ * computes the axial form with those from the caller: d is cut into contiguous parts of
+ * d_t, d_h and d_w = d - d_t - d_h dimensions (all even), rotated by the token's frame,
+ * latent row and latent column; in a part of n dimensions the pair (2i, 2i+1) turns by
+ * pos * base^(-2i/n).
+ *  x [B, H, T, d] dtype, T = n_frames * grid_h * grid_w; token t sits at frame
+ *    frame_offset + t / (grid_h grid_w), row (t mod grid_h grid_w) / grid_w, column
+ *    t mod grid_w.  d must be a multiple of 8 (bf16) or 4 (float32), at most 256;
+ *    frame_offset + n_frames <= 2^24.  A stand-alone pass (not fused into the attention kernels).
+ *  events (may be NULL): two hipEvent_t recorded around the single launch.
+ */
+int rope3d_apply(void* x, int32_t B, int32_t H, int32_t n_frames, int32_t grid_h,
+                 int32_t grid_w, int32_t d, int32_t d_t, int32_t d_h, int32_t frame_offset,
+                 float base, int32_t dtype, void* const* events, void* stream);
 
 /* Bytes of workspace the entry (GDN_ENTRY_*) needs for these dims; 0 on invalid dims.
  * Bounded independently of n_frames. */

@@ -1,0 +1,125 @@
+// rope3d.hip -- 3D rotary position embedding of q or k on gfx950, in place
+// ("SANA-Video: Efficient Video Generation with Block Linear Diffusion Transformer" talk,
+// the segment on temporal modelling: a 3D RoPE for the linear attention).  The pages give
+// no frequency layout, split of the head dimension or base; the reading here is the axial
+// form with those three left to the caller: the head dimension is cut into contiguous
+// parts of d_t, d_h and d_w = d - d_t - d_h dimensions (even), rotated by the token's
+// frame, latent row and latent column; in a part of n dimensions the pair (2i, 2i+1)
+// turns by pos * base^(-2i/n).  Token t of [B, H, T, d] (T = n_frames grid_h grid_w)
+// sits at frame frame_offset + t / (grid_h grid_w), row (t mod grid_h grid_w) / grid_w,
+// column t mod grid_w.
+//
+// A stand-alone pass (one read and one write of the tensor): each thread rotates the
+// pairs of one 16-byte group of a token row; consecutive threads take consecutive groups
+// (coalesced).  Frequencies come from the host in double as float hi + lo pairs; the
+// angle is the float32 product plus its exact remainder, so late frames keep full
+// precision; rotation in float32 (sincosf); a bf16 result is rounded to nearest even.
+#include "gdn.h"
+#include "common.hpp"
+#include <math.h>
+#include <stdint.h>
+
+#define RP_API extern "C" __attribute__((visibility("default")))
+
+namespace gdn {
+namespace {
+
+constexpr int kMaxPairs = 128;  // d <= 256
+
+struct RPArgs {
+    void* x;
+    long long ngrp;   // 16-byte groups in the tensor
+    long long T;      // tokens per (b, h)
+    int gpr;          // groups per token row: d / EPV
+    int grid_h, grid_w, frame_offset;
+    int start[3], size[3];
+    float fhi[kMaxPairs], flo[kMaxPairs];  // frequency of pair j/2 as hi + lo (from double)
+};
+
+template <typename E>
+__global__ __launch_bounds__(256) void rope3d_apply_kernel(RPArgs a) {
+    constexpr int EPV = 16 / (int)sizeof(E);
+    typedef E V __attribute__((ext_vector_type(EPV)));
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= a.ngrp) return;
+    const long long row = gid / a.gpr;
+    const int j0 = (int)(gid - row * a.gpr) * EPV;  // first dimension of this group
+    const long long t = row % a.T;
+    const long long per_frame = (long long)a.grid_h * a.grid_w;
+    const long long tf = t / per_frame, ti = t - tf * per_frame;
+    const float pos[3] = {(float)(a.frame_offset + tf), (float)(ti / a.grid_w), (float)(ti % a.grid_w)};
+    V v = ((V*)a.x)[gid];
+#pragma unroll
+    for (int p = 0; p < EPV / 2; ++p) {
+        const int j = j0 + 2 * p;
+        const int ax = j < a.start[1] ? 0 : (j < a.start[2] ? 1 : 2);
+        // angle = pos * (fhi + flo): the rounded product, plus its exact remainder (fma)
+        // and the lo part; sine and cosine corrected to first order in that small rest
+        const float fh = a.fhi[j >> 1], ang = pos[ax] * fh;
+        const float rest = __builtin_fmaf(pos[ax], fh, -ang) + pos[ax] * a.flo[j >> 1];
+        float s, c;
+        sincosf(ang, &s, &c);
+        const float s1 = __builtin_fmaf(c, rest, s), c1 = __builtin_fmaf(-s, rest, c);
+        s = s1;
+        c = c1;
+        const float x0 = (float)v[2 * p], x1 = (float)v[2 * p + 1];
+        v[2 * p] = (E)(x0 * c - x1 * s);
+        v[2 * p + 1] = (E)(x0 * s + x1 * c);
+    }
+    ((V*)a.x)[gid] = v;
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+RP_API int rope3d_apply(void* x, int32_t B, int32_t H, int32_t n_frames, int32_t grid_h, int32_t grid_w,
+                        int32_t d, int32_t d_t, int32_t d_h, int32_t frame_offset, float base, int32_t dtype,
+                        void* const* events, void* stream) {
+    if (dtype != GDN_BF16 && dtype != GDN_F32) return GDN_ERR_DTYPE;
+    const int d_w = d - d_t - d_h;
+    if (B < 0 || H < 0 || n_frames < 0 || grid_h < 1 || grid_w < 1 || d < 0 || d_t < 0 || d_h < 0 || d_w < 0 ||
+        frame_offset < 0 || !(base > 0.f))
+        return GDN_ERR_DIMS;
+    if ((d_t | d_h | d_w) & 1) return GDN_ERR_UNSUPPORTED;  // rotations act on pairs
+    const int es = dtype == GDN_BF16 ? 2 : 4, epv = 16 / es;
+    if (d % epv != 0 || d > 2 * kMaxPairs) return GDN_ERR_UNSUPPORTED;  // whole 16-byte groups per row
+    const long long T = (long long)n_frames * grid_h * grid_w;
+    if (T > 0 && (long long)frame_offset + n_frames > (1LL << 24)) return GDN_ERR_DIMS;  // exact float positions
+    if (T > 0 && ((long long)1 << 40) / T / (d > 0 ? d : 1) < (long long)B * H) return GDN_ERR_DIMS;
+    const long long ngrp = (long long)B * H * T * d / epv;
+    if (ngrp == 0) return GDN_OK;
+    if ((ngrp + 255) / 256 >= ((long long)1 << 31)) return GDN_ERR_DIMS;
+    if (!x) return GDN_ERR_NULL;
+    if ((uintptr_t)x & 15u) return GDN_ERR_ALIGN;
+    RPArgs a;
+    a.x = x;
+    a.ngrp = ngrp;
+    a.T = T;
+    a.gpr = d / epv;
+    a.grid_h = grid_h;
+    a.grid_w = grid_w;
+    a.frame_offset = frame_offset;
+    a.start[0] = 0;
+    a.start[1] = d_t;
+    a.start[2] = d_t + d_h;
+    a.size[0] = d_t;
+    a.size[1] = d_h;
+    a.size[2] = d_w;
+    for (int ax = 0; ax < 3; ++ax)
+        for (int i = 0; 2 * i < a.size[ax]; ++i) {  // frequencies in double, split hi + lo
+            const double f = pow((double)base, -2.0 * i / a.size[ax]);
+            const int pr = (a.start[ax] >> 1) + i;
+            a.fhi[pr] = (float)f;
+            a.flo[pr] = (float)(f - (double)a.fhi[pr]);
+        }
+    hipStream_t st = (hipStream_t)stream;
+    if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess) return GDN_ERR_HIP;
+    const unsigned grid = (unsigned)((ngrp + 255) / 256);
+    if (dtype == GDN_BF16) hipLaunchKernelGGL(rope3d_apply_kernel<bf16>, dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(rope3d_apply_kernel<float>, dim3(grid), dim3(256), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+    if (events && hipEventRecord((hipEvent_t)events[1], st) != hipSuccess) return GDN_ERR_HIP;
+    return GDN_OK;
+}

@@ -19,7 +19,7 @@ GDN_BF16, GDN_F32 = 0, 1
 NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS = 1, 2, 4, 8, 16
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
 EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
-           "softmax_attn_block_causal", "temporal_conv_block", "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
+           "softmax_attn_block_causal", "temporal_conv_block", "rope3d_apply", "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -66,6 +66,8 @@ def lib():
         i32 = ctypes.c_int32
         L.temporal_conv_block.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_uint32, vp, vp]
         L.temporal_conv_block.restype = ctypes.c_int
+        L.rope3d_apply.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp]
+        L.rope3d_apply.restype = ctypes.c_int
         L.gdn_workspace_bytes.argtypes = [dp, ctypes.c_int]
         L.gdn_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_window_count.argtypes = [dp, ctypes.c_int]
@@ -300,3 +302,16 @@ def temporal_conv_block(x, weight, bias=None, carry_in=None, carry_out=None, out
     _check(lib().temporal_conv_block(_ptr(x), _ptr(carry_in), _ptr(weight), _ptr(bias), _ptr(out), _ptr(carry_out),
                                      B, F, P, C, _dtype_code(x.dtype), flags, ev, _stream(x.device, stream)))
     return out, carry_out
+
+
+def rope3d_apply(x, n_frames, grid_h, grid_w, d_t, d_h, frame_offset=0, base=10000.0, stream=None, events=None):
+    """rope3d_apply: rotates x [B, H, T, d] (bf16 or float32) in place and returns it."""
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, T, d] device tensor")
+    B, H, T, d = x.shape
+    if T != n_frames * grid_h * grid_w:
+        raise ValueError("T=%d != n_frames * grid_h * grid_w" % T)
+    ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
+    _check(lib().rope3d_apply(_ptr(x), B, H, n_frames, grid_h, grid_w, d, d_t, d_h, frame_offset, float(base),
+                              _dtype_code(x.dtype), ev, _stream(x.device, stream)))
+    return x

@@ -12,6 +12,7 @@ class Workload:
     kind: str           # "gdn" | "block_causal" | "stream" | "token" (per-token readout)
                         # | "softmax" (frame-block-causal softmax attention)
                         # | "tconv" (causal temporal convolution, channels H * d)
+                        # | "rope" (3D rotary position embedding of q, in place)
     B: int
     H: int
     n_frames: int
@@ -40,5 +41,7 @@ WORKLOADS = {
         Workload("gdn_720p_60s_share8", 7, "gdn", 1, 20, 30, 880, 112, "bf16"),
         # causal temporal convolution over one block: channels = H * d = 2240
         Workload("tconv_720p_5s", 8, "tconv", 1, 20, 21, 880, 112, "bf16"),
+        # 3D RoPE of q on the 22 x 40 latent grid, d = 112 cut (36, 38, 38)
+        Workload("rope_720p_5s", 9, "rope", 1, 20, 21, 880, 112, "bf16"),
     ]
 }

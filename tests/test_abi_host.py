@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 5
+    assert gdn.lib().gdn_abi_version() == 6
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
@@ -211,3 +211,20 @@ def test_temporal_conv_argument_checks():
     # an empty block needs no x or y (it only passes the carry on): past the NULL check,
     # stopped by the misaligned carry_out
     assert tc(F=0, x=None, y=None, cout=FAKE + 2 ** 32 + 8) == -4
+
+
+def test_rope3d_argument_checks():
+    """Every call here is rejected (or has nothing to do) before any launch."""
+    L = gdn.lib()
+    rp = lambda x=FAKE, B=1, H=2, F=3, gh=2, gw=4, d=16, dt=4, dh=6, off=0, base=10000.0, dtype=gdn.GDN_BF16: \
+        L.rope3d_apply(x, B, H, F, gh, gw, d, dt, dh, off, base, dtype, None, None)
+    assert rp(dtype=9) == -3
+    assert rp(dt=3, dh=7) == -7              # odd parts
+    assert rp(d=12) == -7                    # bf16 rows are whole 16-byte groups
+    assert rp(dt=10, dh=10) == -2            # d_w < 0
+    assert rp(base=0.0) == -2
+    assert rp(gh=0) == -2
+    assert rp(off=1 << 24) == -2
+    assert rp(x=None) == -1
+    assert rp(x=FAKE + 8) == -4
+    assert rp(B=0, x=None) == 0 and rp(F=0, x=None) == 0
