@@ -11,9 +11,10 @@
 //
 // A stand-alone pass (one read and one write of the tensor): each thread rotates the
 // pairs of one 16-byte group of a token row; consecutive threads take consecutive groups
-// (coalesced).  Frequencies come from the host in double as float hi + lo pairs; the
-// angle is the float32 product plus its exact remainder, so late frames keep full
-// precision; rotation in float32 (sincosf); a bf16 result is rounded to nearest even.
+// (coalesced).  Frequencies / 2 pi come from the host in double as float hi + lo pairs;
+// the angle in revolutions is reduced exactly to its fraction (late frames keep full
+// precision) and fed to the hardware sine and cosine; rotation in float32; a bf16 result
+// is rounded to nearest even.
 #include "gdn.h"
 #include "common.hpp"
 #include <math.h>
@@ -33,7 +34,7 @@ struct RPArgs {
     int gpr;          // groups per token row: d / EPV
     int grid_h, grid_w, frame_offset;
     int start[3], size[3];
-    float fhi[kMaxPairs], flo[kMaxPairs];  // frequency of pair j/2 as hi + lo (from double)
+    float ghi[kMaxPairs], glo[kMaxPairs];  // frequency / 2 pi of pair j/2 as hi + lo (from double)
 };
 
 template <typename E>
@@ -53,15 +54,13 @@ __global__ __launch_bounds__(256) void rope3d_apply_kernel(RPArgs a) {
     for (int p = 0; p < EPV / 2; ++p) {
         const int j = j0 + 2 * p;
         const int ax = j < a.start[1] ? 0 : (j < a.start[2] ? 1 : 2);
-        // angle = pos * (fhi + flo): the rounded product, plus its exact remainder (fma)
-        // and the lo part; sine and cosine corrected to first order in that small rest
-        const float fh = a.fhi[j >> 1], ang = pos[ax] * fh;
-        const float rest = __builtin_fmaf(pos[ax], fh, -ang) + pos[ax] * a.flo[j >> 1];
-        float s, c;
-        sincosf(ang, &s, &c);
-        const float s1 = __builtin_fmaf(c, rest, s), c1 = __builtin_fmaf(-s, rest, c);
-        s = s1;
-        c = c1;
+        // the angle in revolutions, pos * (ghi + glo): the rounded product's fraction (an
+        // exact subtraction) plus the product's exact remainder (fma) and the lo part;
+        // then the hardware sine and cosine of 2 pi times that fraction (v_sin_f32 and
+        // v_cos_f32 take revolutions)
+        const float gh = a.ghi[j >> 1], rh = pos[ax] * gh;
+        const float fr = (rh - __builtin_floorf(rh)) + (__builtin_fmaf(pos[ax], gh, -rh) + pos[ax] * a.glo[j >> 1]);
+        const float s = __builtin_amdgcn_sinf(fr), c = __builtin_amdgcn_cosf(fr);
         const float x0 = (float)v[2 * p], x1 = (float)v[2 * p + 1];
         v[2 * p] = (E)(x0 * c - x1 * s);
         v[2 * p + 1] = (E)(x0 * s + x1 * c);
@@ -109,10 +108,10 @@ RP_API int rope3d_apply(void* x, int32_t B, int32_t H, int32_t n_frames, int32_t
     a.size[2] = d_w;
     for (int ax = 0; ax < 3; ++ax)
         for (int i = 0; 2 * i < a.size[ax]; ++i) {  // frequencies in double, split hi + lo
-            const double f = pow((double)base, -2.0 * i / a.size[ax]);
+            const double f = pow((double)base, -2.0 * i / a.size[ax]) / (2.0 * 3.141592653589793);
             const int pr = (a.start[ax] >> 1) + i;
-            a.fhi[pr] = (float)f;
-            a.flo[pr] = (float)(f - (double)a.fhi[pr]);
+            a.ghi[pr] = (float)f;
+            a.glo[pr] = (float)(f - (double)a.ghi[pr]);
         }
     hipStream_t st = (hipStream_t)stream;
     if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess) return GDN_ERR_HIP;
