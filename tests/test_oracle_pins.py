@@ -521,3 +521,25 @@ def test_rope3d_relative_positions():
     np.testing.assert_allclose(s7, s0, rtol=1e-10, atol=1e-10)
     # and the offset does change the rotated vectors themselves
     assert np.abs(oracle.rope3d(q, F, gh, gw, dt, dh, frame_offset=7) - oracle.rope3d(q, F, gh, gw, dt, dh)).max() > 1e-3
+
+
+def test_rope3d_frequency_ladder_handworked():
+    """Pairs i >= 1 of each part: angles worked by hand (tests/golden/rope3d_handworked.json)
+    from pos * base^(-2i/n).  Every pair of the chosen token gets (1, 0) or (0, 1), so the
+    rotated pair is (cos a, sin a) or (-sin a, cos a)."""
+    import json
+    import math
+    spec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rope3d_handworked.json")))
+    for case in spec["cases"]:
+        d, F, gh, gw = case["d"], case["n_frames"], case["grid_h"], case["grid_w"]
+        x = _rope_x(F=F, gh=gh, gw=gw, d=d, seed=98)
+        t = case["token"]
+        x[:, :, t, :] = 0.0
+        x[:, :, t, 0::4] = 1.0   # even pairs: (1, 0)
+        x[:, :, t, 3::4] = 1.0   # odd pairs: (0, 1)
+        y = oracle.rope3d(x, F, gh, gw, case["d_t"], case["d_h"], frame_offset=case["frame_offset"],
+                          base=case["base"])
+        for p, a in enumerate(case["pair_angles"]):
+            want = (math.cos(a), math.sin(a)) if p % 2 == 0 else (-math.sin(a), math.cos(a))
+            np.testing.assert_allclose(y[:, :, t, 2 * p], want[0], rtol=0, atol=1e-12, err_msg=case["name"])
+            np.testing.assert_allclose(y[:, :, t, 2 * p + 1], want[1], rtol=0, atol=1e-12, err_msg=case["name"])
