@@ -50,11 +50,15 @@
  *    with n_frames == 0 copies state_in, or zeros, to state_out).
  *  - workspace: caller-owned device scratch of at least gdn_workspace_bytes(dims,
  *    entry) bytes.  Its size grows with B*H but never with n_frames: frames are
- *    processed in windows of at most 8192 (b, h, frame) units (the environment
- *    variable GDN_WINDOW_UNITS, read at each call, overrides that bound).  Contents
- *    need no initialisation and are garbage afterwards.
- *  - stream: a hipStream_t (NULL = the default stream).  Every launch is enqueued on
- *    it, asynchronously; the library never allocates, frees or synchronises.
+ *    processed in windows of at most 8192 (b, h, frame) units (dims->window_units
+ *    overrides that bound).  Contents need no initialisation and are garbage afterwards.
+ *    Two calls in flight at once need two workspaces.
+ *  - stream: a hipStream_t (NULL = the default stream) of the current device.  Every
+ *    launch is enqueued on it, asynchronously; the library never allocates, frees or
+ *    synchronises.  The first call on each device sets the kernels' shared-memory
+ *    attributes there (once per device, safe from several host threads).  Calls with
+ *    distinct workspaces and outputs may run concurrently from several threads and
+ *    streams.
  *  - Errors: every check runs on the host before anything is enqueued and returns a
  *    negative gdn_status_t; nothing is launched then.  A failed launch returns
  *    GDN_ERR_HIP.  Device faults surface at the caller's next synchronisation.
@@ -73,7 +77,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
     GDN_OK = 0,
@@ -116,6 +120,12 @@ typedef struct gdn_dims {
                                      window's i-th launch (i = 0, 1, 2), on the stream that
                                      launch goes to; for per-kernel timing only           */
     int32_t phase_windows;        /* windows covered by phase_events (see gdn_window_count) */
+    /* Plan overrides, for tests and tuning; 0 = the library's choice.  They change how the
+     * work is cut (and the workspace size), not the result beyond rounding. */
+    int32_t window_units;         /* (b, h, frame) units per window (default 8192)        */
+    int32_t group_frames;         /* gated delta rule: frames per group of the frame-map
+                                     kernel (default: chosen from B*H, n_frames, frame_len
+                                     and the device's compute units)                     */
 } gdn_dims_t;
 
 /*

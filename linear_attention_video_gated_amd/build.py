@@ -2,7 +2,8 @@
 
     python -m linear_attention_video_gated_amd.build
 
-Each ``csrc/*.hip`` compiles to an object under ``_build/`` (in parallel), then one link.
+Each ``csrc/*.hip`` compiles with hipcc and each ``csrc/*.cpp`` (host-only C++) with g++ to
+an object under ``_build/`` (in parallel), then one link.
 The library exports only the C ABI of ``include/gdn.h``.
 """
 from __future__ import annotations
@@ -29,13 +30,22 @@ CFLAGS = [
 ]
 
 
+# host-only C++ (no device code): the call planning, also built on its own with sanitizers
+# by the CPU tests
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I" + INCLUDE, "-I" + CSRC]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+    obj = os.path.join(BUILD, os.path.basename(src).rsplit(".", 1)[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = [CXX] + CXXFLAGS + ["-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

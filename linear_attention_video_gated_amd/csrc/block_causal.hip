@@ -282,15 +282,15 @@ hipError_t launch_bc_window(const BC1Args& a1, const BC2Args& a2, const BC3Args&
                             void* const* ev) {
     hipError_t e = record(ev, 0, st);
     if (e != hipSuccess) return e;
-    static bool attr_done = false;  // per instantiation
-    if (!attr_done) {
-        if ((e = hipFuncSetAttribute((const void*)bc_partial<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     BCP<E, ND>::LDS_B)) != hipSuccess ||
-            (e = hipFuncSetAttribute((const void*)bc_readout<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     2 * BCP<E, ND>::TILE_B)) != hipSuccess)
-            return e;
-        attr_done = true;
-    }
+    static PerDeviceOnce attr;  // per instantiation
+    e = attr.run([] {
+        hipError_t r = hipFuncSetAttribute((const void*)bc_partial<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           BCP<E, ND>::LDS_B);
+        if (r != hipSuccess) return r;
+        return hipFuncSetAttribute((const void*)bc_readout<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   2 * BCP<E, ND>::TILE_B);
+    });
+    if (e != hipSuccess) return e;
     constexpr int lds1 = BCP<E, ND>::LDS_B;
     hipLaunchKernelGGL((bc_partial<E, ND>), dim3(a1.nf, BH), dim3(256), lds1, st, a1);
     if ((e = hipGetLastError()) != hipSuccess || (e = record(ev, 1, st)) != hipSuccess ||
@@ -319,12 +319,5 @@ hipError_t launch_bc_window(const BC1Args& a1, const BC2Args& a2, const BC3Args&
 BC_INST(bf16, 1) BC_INST(bf16, 2) BC_INST(bf16, 4) BC_INST(bf16, 7) BC_INST(bf16, 8)
 BC_INST(float, 1) BC_INST(float, 2) BC_INST(float, 4) BC_INST(float, 7) BC_INST(float, 8)
 
-size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack) {
-    const int kb = (nd + 1) / 2;
-    const int nsplit = esize == 2 ? 2 : 1;  // bf16 operands are stored as hi + lo
-    *part = (size_t)nd * (nd + 1) * 256 * 4;
-    *pack = (size_t)nsplit * (nd + 1) * kb * 64 * 8 * esize;
-    return *part + *pack;
-}
 
 }  // namespace gdn

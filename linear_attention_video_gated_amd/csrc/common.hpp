@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace gdn {
 
 typedef __bf16 bf16;
@@ -256,6 +258,35 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
     return x;
 }
 
+// The same inclusive prefix carried as an unevaluated sum hi + lo (hi = the rounded
+// prefix, lo = the rounding error of every addition, each addition an error-free
+// two-sum).  A difference of two prefixes, (hi_t - hi_i) + (lo_t - lo_i), is then accurate
+// to about 2^-24 of the difference itself, however large the two prefixes are (a run of
+// near-zero gates before both tokens cancels exactly).
+__device__ __forceinline__ float wave_incl_scan2(float x, float& lo_out) {
+#pragma clang fp contract(off)  // the two-sums must round each operation as written
+    float hi = x, lo = 0.f;
+#define GDN_DPP2(CTRL, ROWMASK)                                                                                 \
+    {                                                                                                           \
+        const float bh = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hi), \
+                                                                               CTRL, ROWMASK, 0xf, false));    \
+        const float bl = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, lo), \
+                                                                               CTRL, ROWMASK, 0xf, false));    \
+        const float s = hi + bh, bb = s - hi, e = (hi - (s - bb)) + (bh - bb);                                  \
+        hi = s;                                                                                                 \
+        lo = lo + (bl + e);                                                                                     \
+    }
+    GDN_DPP2(0x111, 0xf)
+    GDN_DPP2(0x112, 0xf)
+    GDN_DPP2(0x114, 0xf)
+    GDN_DPP2(0x118, 0xf)
+    GDN_DPP2(0x142, 0xa)
+    GDN_DPP2(0x143, 0xc)
+#undef GDN_DPP2
+    lo_out = lo;
+    return hi;
+}
+
 // Split precision: bf16 operands that must carry ~16 significant bits are sent to the
 // matrix cores as hi + lo pairs (hi = RNE(x), lo = RNE(x - hi)); a product a*b is then
 // a_hi*b_hi + a_lo*b_hi + a_hi*b_lo (the lo*lo term is below fp32 accumulation noise).
@@ -270,6 +301,23 @@ template <typename E, int ND_> struct Geo {
     static constexpr int DP = 32 * KB;          // padded d
     static constexpr int EPV = Ops<E>::EPV;     // elements per 16-byte vector
     static constexpr int FRAG = 64 * 8;         // elements in one K32 operand fragment
+};
+
+// Per-device one-time set-up (kernel attributes): the first call on each device runs f
+// there, once, whatever the number of host threads; later calls return its status.
+struct PerDeviceOnce {
+    static constexpr int kMaxDevices = 64;
+    std::once_flag flag[kMaxDevices];
+    hipError_t status[kMaxDevices] = {};
+    template <typename F>
+    hipError_t run(F&& f) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        std::call_once(flag[dev], [&] { status[dev] = f(); });
+        return status[dev];
+    }
 };
 
 }  // namespace gdn

@@ -1,7 +1,7 @@
 // gdn_api.hip -- the C ABI declared in include/gdn.h: argument checks (host only, before
-// anything is enqueued), workspace sizing and layout, and dispatch over (dtype, d) to the
-// kernel launchers.  Frames are processed in windows of at most kMaxUnits (b, h, frame)
-// units so the workspace never grows with the number of frames.
+// anything is enqueued; the plan and workspace layout are in gdn_plan.cpp) and dispatch
+// over (dtype, d) to the kernel launchers.  Frames are processed in windows of at most
+// kMaxUnits (b, h, frame) units so the workspace never grows with the number of frames.
 //
 // All launches go to the caller's stream, window after window.  (Running the chain and
 // the readout of one window on other streams beside the next window's frame maps was
@@ -19,125 +19,23 @@
 namespace gdn {
 namespace {
 
-constexpr long long kMaxUnits = 8192;  // default (b, h, frame) units per window
-
-long long env_ll(const char* name) {
-    const char* e = getenv(name);
-    return e ? atoll(e) : 0;
+// Compute units of the current device (the group plan depends on it), queried once per
+// device; 256 (MI355X) when the query fails.
+int device_cus() {
+    static PerDeviceOnce once;
+    static int cus[PerDeviceOnce::kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PerDeviceOnce::kMaxDevices) return 256;
+    once.run([&] {
+        int n = 0;
+        const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        cus[dev] = (e == hipSuccess && n > 0) ? n : 256;
+        return hipSuccess;
+    });
+    return cus[dev] > 0 ? cus[dev] : 256;
 }
 
-long long window_units() {
-    const long long v = env_ll("GDN_WINDOW_UNITS");
-    return v > 0 ? v : kMaxUnits;
-}
-
-// Frames per group of the gated-delta-rule path.  The frame-map kernel runs one
-// workgroup per (b, h, group) and one workgroup per CU (its LDS footprint), so its time
-// goes as (rounds of workgroups over the 256 CUs of an MI355X) x (frames per group);
-// the serial chain takes one step per group.  G minimises the sum of the two, with
-// about 0.051 us per token of a frame in the frame-map kernel and 3 us per chain step
-// (measured at d = 112).  GDN_GROUP_FRAMES overrides.  Windows hold whole groups.
-int group_frames(long long BH, int n_frames, int frame_len) {
-    const long long forced = env_ll("GDN_GROUP_FRAMES");
-    if (forced > 0) return (int)(forced < n_frames ? forced : n_frames);
-    constexpr long long kCUs = 256;
-    const double per_frame = 0.051 * frame_len, per_step = 3.0;
-    int best = 1;
-    double best_cost = 1e300;
-    for (int G = 1; G <= n_frames && G <= 64; ++G) {
-        const long long groups = (n_frames + G - 1) / G;
-        const long long rounds = (BH * groups + kCUs - 1) / kCUs;
-        const double cost = rounds * G * per_frame + groups * per_step;
-        if (cost < best_cost * (1 - 1e-9)) {
-            best_cost = cost;
-            best = G;
-        }
-    }
-    return best;
-}
-constexpr size_t kAlign = 256;
-
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-int nd_of(int d) {
-    switch (d) {
-        case 16: return 1;
-        case 32: return 2;
-        case 64: return 4;
-        case 112: return 7;
-        case 128: return 8;
-        default: return 0;
-    }
-}
-
-int esize_of(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
-
-// Plan of one call: window size and workspace offsets.
-struct Plan {
-    long long BH = 0, T = 0;
-    int nd = 0, es = 0, nfw = 0, nwin = 0, G = 1;
-    // block-causal: off_a per-frame sums, off_c prefix operands; gated delta rule: the
-    // regions of GdnRegions
-    size_t off_a = 0, off_b = 0, off_x = 0, off_ga = 0, off_gb = 0, off_c = 0, off_carry = 0, total = 0;
-};
-
-int check_dims(const gdn_dims_t* d, int entry, Plan* p) {
-    if (!d) return GDN_ERR_NULL;
-    if (d->dtype != GDN_BF16 && d->dtype != GDN_F32) return GDN_ERR_DTYPE;
-    if (d->B < 0 || d->H < 0 || d->n_frames < 0 || d->frame_len < 1) return GDN_ERR_DIMS;
-    if (d->d_k != d->d_v || nd_of(d->d_k) == 0) return GDN_ERR_UNSUPPORTED;
-    const uint32_t allowed = (entry == GDN_ENTRY_BLOCK_CAUSAL)
-                                 ? (uint32_t)(GDN_F_RELU_QK | GDN_F_OUT_F32)
-                                 : (uint32_t)(GDN_F_NORMALIZE_K | GDN_F_ADDITIVE | GDN_F_OUT_F32 |
-                                              GDN_F_GATE_LOGITS);
-    if (d->flags & ~allowed) return GDN_ERR_UNSUPPORTED;
-    p->BH = (long long)d->B * d->H;
-    p->T = (long long)d->n_frames * d->frame_len;
-    if (p->BH > 65535) return GDN_ERR_DIMS;  // grid y extent
-    p->nd = nd_of(d->d_k);
-    p->es = esize_of(d->dtype);
-    // element count of q must fit comfortably in 63 bits
-    if (p->T > ((long long)1 << 40) / (p->BH ? p->BH : 1) / d->d_k) return GDN_ERR_DIMS;
-    if (p->BH == 0 || d->n_frames == 0) return GDN_OK;
-    const bool bc = entry == GDN_ENTRY_BLOCK_CAUSAL;
-    if (!bc) p->G = group_frames(p->BH, d->n_frames, d->frame_len);
-    const long long G = p->G;
-    long long nfw = window_units() / p->BH / G * G;  // whole groups per window
-    if (nfw < G) nfw = G;
-    if (nfw > d->n_frames) nfw = d->n_frames;
-    p->nfw = (int)nfw;
-    p->nwin = (int)((d->n_frames + nfw - 1) / nfw);
-    const size_t units = (size_t)p->BH * (size_t)nfw;
-    size_t carry = 0;
-    GdnRegions r{0, 0, 0, 0, 0, 0};
-    size_t groups = 0;
-    if (bc) {
-        bc_unit_bytes(p->nd, p->es, &r.afr, &r.sgrp);
-        carry = (size_t)p->BH * p->nd * (p->nd + 1) * 256 * 4;
-        groups = units;
-    } else {
-        r = gdn_region_bytes(p->nd, p->es);
-        carry = (size_t)p->BH * d->d_k * d->d_v * 4;
-        groups = (size_t)p->BH * ((p->nfw + p->G - 1) / p->G);
-    }
-    p->off_a = 0;
-    p->off_b = align_up(units * r.afr);
-    p->off_x = p->off_b + align_up(units * r.bfr);
-    p->off_ga = p->off_x + align_up(units * r.xexp);
-    p->off_gb = p->off_ga + align_up(groups * r.agr);
-    p->off_c = p->off_gb + align_up(groups * r.bgr);
-    p->off_carry = p->off_c + align_up(groups * r.sgrp);
-    p->total = p->off_carry + (p->nwin > 1 ? align_up(carry) : 0);
-    return GDN_OK;
-}
-
-bool misaligned(const void* ptr) { return ptr && ((uintptr_t)ptr & 15u) != 0; }
-
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-    if (!a || !b || na == 0 || nb == 0) return false;
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return a0 < b0 + nb && b0 < a0 + na;
-}
+int plan_call(const gdn_dims_t* d, int entry, Plan* p) { return check_dims(d, entry, p, device_cus()); }
 
 __global__ void fill_or_copy(const float* src, float* dst, long long n) {
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
@@ -254,7 +152,7 @@ int gdn_common(const void* q, const void* k, const void* v, const float* alpha, 
                const float* state_in, float* state_out, void* out, const gdn_dims_t* d, void* stream,
                int entry) {
     Plan p;
-    int rc = check_dims(d, entry, &p);
+    int rc = plan_call(d, entry, &p);
     if (rc != GDN_OK) return rc;
     const long long nstate = p.BH * d->d_k * d->d_v;
     const size_t sbytes = (size_t)nstate * 4;
@@ -316,7 +214,7 @@ GDN_API int linear_attn_block_causal(const void* q, const void* k, const void* v
                                      const gdn_dims_t* dims, void* stream) {
     const gdn_dims_t* d = dims;
     Plan p;
-    int rc = check_dims(d, GDN_ENTRY_BLOCK_CAUSAL, &p);
+    int rc = plan_call(d, GDN_ENTRY_BLOCK_CAUSAL, &p);
     if (rc != GDN_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const long long ns = p.BH * d->d_k * d->d_v, nz = p.BH * d->d_k;
@@ -353,7 +251,7 @@ GDN_API size_t gdn_workspace_bytes(const gdn_dims_t* dims, int entry) {
         entry != GDN_ENTRY_TOKEN)
         return 0;
     Plan p;
-    if (check_dims(dims, entry, &p) != GDN_OK) return 0;
+    if (plan_call(dims, entry, &p) != GDN_OK) return 0;
     return p.total;
 }
 
@@ -362,7 +260,7 @@ GDN_API int gdn_window_count(const gdn_dims_t* dims, int entry) {
         entry != GDN_ENTRY_TOKEN)
         return GDN_ERR_UNSUPPORTED;
     Plan p;
-    const int rc = check_dims(dims, entry, &p);
+    const int rc = plan_call(dims, entry, &p);
     return rc != GDN_OK ? rc : p.nwin;
 }
 

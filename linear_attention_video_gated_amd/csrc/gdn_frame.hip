@@ -86,15 +86,20 @@ template <typename E, int ND, bool TOK = false> struct P1 {
     static constexpr int KV_B = al(64 * KPB);
     static constexpr int RAW_B = al(2 * 64 * 4);
     // per-token scalars: [0,64) b e^G n, [64,128) b, [128,192) e^{G_C - G} n, [192] gamma_C;
-    // TOK adds [208,272) G (log2, inclusive), [272,336) n, [336,400) e^G
-    static constexpr int SC_N = TOK ? 400 : 208;
+    // TOK adds [208,272) G (log2, inclusive), [272,336) n, [336,400) e^G and, for fp32
+    // inputs, [400,464) the low part of G (G = hi + lo, see wave_incl_scan2)
+    static constexpr int SC_N = TOK ? (BF ? 400 : 464) : 208;
     static constexpr int SC_B = al(SC_N * 4);
     static constexpr int FR_B = al(FR_E * (int)sizeof(E));
     static constexpr int W_B = al(G::D * WPB);
     // TOK: the 10 lower-triangle 16x16 tiles of the decay-masked (K Q^T), hi (+ lo) fragments
     static constexpr int AQ_B = TOK ? al(10 * SplitCount<E>::N * 64 * 4 * (int)sizeof(E)) : 0;
     static constexpr int LD_B = al(4 * 16 * LD_P * 4);
-    static constexpr int TK_B = al(7 * 64 * 4);
+    // prep wave's per-token scalars: [0,64) G, [64,128) n, [128,192) b n, [192,256) the
+    // within-block decay, [256,448) the cross-block decays; fp32 inputs add [448,512) the
+    // low part of G
+    static constexpr int TKN = BF ? 7 : 8;
+    static constexpr int TK_B = al(TKN * 64 * 4);
     // Buffer counts.  OV (overlapped): the chain waves run the state update of chunk q
     // together with the substitution of chunk q+1, the prep wave prepares chunk q+2 and
     // copies of chunk q+3 are in flight -- K for chunks q..q+3, V and gates for q+1..q+3,
@@ -271,7 +276,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     auto has_off = [](auto R) { return R.value != 0; };
     // ---- prep, first part: Gram matrix on the matrix cores and the key norms
     auto prep1 = [&](int p, f32x4 (&gr)[10], auto R) {
-        float* const sTK = sTK0 + (R.value == 1 ? 7 * 64 : 0);
+        float* const sTK = sTK0 + (R.value == 1 ? L::TKN * 64 : 0);
         const int Cc = chunk_len(p);
         const int t = lane;
         const bool valid = t < Cc;
@@ -321,7 +326,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // ---- prep, second part: gate prefix and per-token scalars, L from the Gram tiles, its
     //      off-diagonal blocks as operand fragments, its diagonal blocks to LDS
     auto prep2 = [&](int p, f32x4 (&gr)[10], auto R) {
-        float* const sTK = sTK0 + (R.value == 1 ? 7 * 64 : 0);
+        float* const sTK = sTK0 + (R.value == 1 ? L::TKN * 64 : 0);
         E* fr = FR(p);
         const int Cc = chunk_len(p);
         float* sc = SC(p);
@@ -349,38 +354,54 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             gl = valid ? l2a : 0.f;
             be = valid ? bb : 0.f;
         }
-        const float Gs = wave_incl_scan(gl);  // inclusive prefix over the chunk (log2 units)
+        // inclusive prefix over the chunk (log2 units).  Only differences of it and values
+        // near the chunk's start are used; for fp32 inputs it is carried as hi + lo so
+        // that a difference stays accurate after a run of near-zero gates (whose prefix
+        // can reach thousands, where fp32 keeps ~1e-4 absolute); bf16 inputs keep hi only
+        // (the bf16 rounding of the operands dominates there)
+        float Gl = 0.f;
+        const float Gs = L::BF ? wave_incl_scan(gl) : wave_incl_scan2(gl, Gl);
         // (the lane-read builtins are integer-typed: move the bits, not the value)
         auto lane_of = [](float x, int l) {
             return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
         };
-        const float GC = lane_of(Gs, 63);
+        // G_x - G_y from (hi, lo) pairs
+        auto gdif = [](float xh, float xl, float yh, float yl) { return L::BF ? xh - yh : (xh - yh) + (xl - yl); };
+        const float GC = lane_of(Gs, 63), GCl = L::BF ? 0.f : lane_of(Gl, 63);
         if (has_diag(R)) {
-            sc[t] = additive ? 0.f : be * hw_exp2(Gs) * nrm;
+            sc[t] = additive ? 0.f : be * hw_exp2(Gs + Gl) * nrm;
             sc[64 + t] = be;
-            sc[128 + t] = hw_exp2(GC - Gs) * nrm;
-            if (t == 0) sc[192] = hw_exp2(GC);
+            sc[128 + t] = hw_exp2(gdif(GC, GCl, Gs, Gl)) * nrm;
+            if (t == 0) sc[192] = hw_exp2(GC + GCl);
             if constexpr (TOK) {
                 sc[208 + t] = Gs;
                 sc[272 + t] = nrm;
-                sc[336 + t] = hw_exp2(Gs);
+                sc[336 + t] = hw_exp2(Gs + Gl);
+                if constexpr (!L::BF) sc[400 + t] = Gl;
             }
         }
         // decay factors of L split at the end of 16-token block J (both factors <= 1):
         // e^{G_i - G_j} = e^{G_i - G_end(J)} e^{G_end(J) - G_j} for i in a later block
         const int Jt = t >> 4;
-        const float Gend = lane_of(Gs, 15) * (Jt == 0) + lane_of(Gs, 31) * (Jt == 1) +
-                           lane_of(Gs, 47) * (Jt == 2) + lane_of(Gs, 63) * (Jt == 3);
+        auto blk_end = [&](float x) {
+            return lane_of(x, 15) * (Jt == 0) + lane_of(x, 31) * (Jt == 1) + lane_of(x, 47) * (Jt == 2) +
+                   lane_of(x, 63) * (Jt == 3);
+        };
+        const float Gend = blk_end(Gs), Gendl = L::BF ? 0.f : blk_end(Gl);
         sTK[t] = Gs;
+        if constexpr (!L::BF) sTK[448 + t] = Gl;
         sTK[128 + t] = be * nrm;
-        sTK[192 + t] = nrm * hw_exp2(Gend - Gs);
+        sTK[192 + t] = nrm * hw_exp2(gdif(Gend, Gendl, Gs, Gl));
 #pragma unroll
         for (int J = 0; J < 3; ++J)
-            sTK[256 + 64 * J + t] = J < Jt ? be * nrm * hw_exp2(Gs - lane_of(Gs, 16 * J + 15)) : 0.f;
+            sTK[256 + 64 * J + t] =
+                J < Jt ? be * nrm *
+                             hw_exp2(gdif(Gs, Gl, lane_of(Gs, 16 * J + 15), L::BF ? 0.f : lane_of(Gl, 16 * J + 15)))
+                       : 0.f;
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // sTK written by other lanes
         // every per-token factor first (reads only), then the scaling, then the writes
-        f32x4 cf[3], gj[4], nj[4];
-        float rf[6], si[4], gi_[4];
+        f32x4 cf[3], gj[4], nj[4], gjl[4];
+        float rf[6], si[4], gi_[4], gil[4];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J < 3) cf[J] = *(const f32x4*)(sTK + 192 + 16 * J + 4 * g);
@@ -388,6 +409,8 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             nj[J] = *(const f32x4*)(sTK + 64 + 16 * J + 4 * g);
             si[J] = sTK[128 + 16 * J + c];
             gi_[J] = sTK[16 * J + c];
+            gjl[J] = L::BF ? zero4() : *(const f32x4*)(sTK + 448 + 16 * J + 4 * g);
+            gil[J] = L::BF ? 0.f : sTK[448 + 16 * J + c];
         }
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
@@ -411,7 +434,9 @@ __device__ __forceinline__ void affine_body(P1Args a) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int j = 16 * J + 4 * g + ii;
-                    acc[ii] = (i > j) ? si[I] * nj[J][ii] * hw_exp2(gi_[I] - gj[J][ii]) * acc[ii] : 0.f;
+                    acc[ii] = (i > j) ? si[I] * nj[J][ii] * hw_exp2(gdif(gi_[I], gil[I], gj[J][ii], gjl[J][ii])) *
+                                            acc[ii]
+                                      : 0.f;
                 }
             }
         }
@@ -564,14 +589,19 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             const float gt = sc[208 + 16 * T + c];
             const f32x4 gi4 = *(const f32x4*)(sc + 208 + 16 * J + 4 * g);
             const f32x4 ni4 = *(const f32x4*)(sc + 272 + 16 * J + 4 * g);
+            // fp32 inputs: G = hi + lo (differences stay accurate after near-zero gates)
+            const float gtl = L::BF ? 0.f : sc[400 + 16 * T + c];
+            const f32x4 gi4l = L::BF ? zero4() : *(const f32x4*)(sc + 400 + 16 * J + 4 * g);
+            auto gdif = [](float xh, float xl, float yh, float yl) { return L::BF ? xh - yh : (xh - yh) + (xl - yl); };
             if (T == J) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a4[i] = (4 * g + i <= c) ? a4[i] * ni4[i] * hw_exp2(gt - gi4[i]) : 0.f;
+                for (int i = 0; i < 4; ++i)
+                    a4[i] = (4 * g + i <= c) ? a4[i] * ni4[i] * hw_exp2(gdif(gt, gtl, gi4[i], gi4l[i])) : 0.f;
             } else {
-                const float ge = sc[208 + 16 * J + 15];
-                const float rowf = hw_exp2(gt - ge);
+                const float ge = sc[208 + 16 * J + 15], gel = L::BF ? 0.f : sc[400 + 16 * J + 15];
+                const float rowf = hw_exp2(gdif(gt, gtl, ge, gel));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a4[i] *= rowf * ni4[i] * hw_exp2(ge - gi4[i]);
+                for (int i = 0; i < 4; ++i) a4[i] *= rowf * ni4[i] * hw_exp2(gdif(ge, gel, gi4[i], gi4l[i]));
             }
             F4 hi, lo;
             O::split4(a4, hi, lo);
@@ -1395,8 +1425,8 @@ template <typename E, int ND>
 hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev) {
     using L = P1<E, ND>;
     using LT = P1<E, ND, true>;
-    static bool attr_done = false;  // per instantiation
-    if (!attr_done) {
+    static PerDeviceOnce attr;  // per instantiation
+    hipError_t e = attr.run([] {
         const void* aff[8] = {(const void*)gdn_frame_affine<E, ND, 0>, (const void*)gdn_frame_affine<E, ND, 1>,
                               (const void*)gdn_frame_affine<E, ND, 2>, (const void*)gdn_frame_affine<E, ND, 3>,
                               (const void*)gdn_frame_affine<E, ND, 4>, (const void*)gdn_frame_affine<E, ND, 5>,
@@ -1413,13 +1443,12 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
         e = hipFuncSetAttribute((const void*)gdn_frame_chain<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 P2<E, ND>::LDS_B);
         if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void*)gdn_frame_readout<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                P3<E, ND>::LDS_B);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+        return hipFuncSetAttribute((const void*)gdn_frame_readout<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   P3<E, ND>::LDS_B);
+    });
+    if (e != hipSuccess) return e;
     const int slot = phase == 3 ? 2 : phase;  // the per-token readout is a window's third launch
-    hipError_t e = record(ev, 2 * slot, st);
+    e = record(ev, 2 * slot, st);
     if (e != hipSuccess) return e;
     if (phase == 3) {
         const P1Args& p1 = *(const P1Args*)args;
@@ -1470,18 +1499,5 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
 GDN_INST(bf16, 1) GDN_INST(bf16, 2) GDN_INST(bf16, 4) GDN_INST(bf16, 7) GDN_INST(bf16, 8)
 GDN_INST(float, 1) GDN_INST(float, 2) GDN_INST(float, 4) GDN_INST(float, 7) GDN_INST(float, 8)
 
-GdnRegions gdn_region_bytes(int nd, int esize) {
-    const size_t frag = (size_t)nd * ((nd + 1) / 2) * 64 * 8;  // elements of one set of A fragments
-    const size_t tiles = (size_t)nd * nd * 256;                // elements of the B tiles
-    const bool bf = esize == 2;
-    GdnRegions r;
-    r.afr = frag * (bf ? 2 : 4);         // fp16 (bf16 inputs) or fp32
-    r.bfr = tiles * (bf ? 2 : 4);
-    r.xexp = bf ? 16 * sizeof(int) : 0;
-    r.agr = frag * esize * (bf ? 2 : 1);  // bf16 operands are stored as hi + lo
-    r.bgr = tiles * 4;
-    r.sgrp = (size_t)16 * nd * 16 * nd * 4;  // a d x d fp32 state
-    return r;
-}
 
 }  // namespace gdn

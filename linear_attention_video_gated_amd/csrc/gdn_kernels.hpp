@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "gdn_plan.hpp"
+
 namespace gdn {
 
 struct P1Args {
@@ -133,11 +135,5 @@ inline hipError_t record(void* const* ev, int i, hipStream_t st) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
 }
 
-// bytes of the workspace regions: per unit (afr, bfr, xexp), per group (agr, bgr, sgrp)
-struct GdnRegions {
-    size_t afr, bfr, xexp, agr, bgr, sgrp;
-};
-GdnRegions gdn_region_bytes(int nd, int esize);
-size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack);
 
 }  // namespace gdn

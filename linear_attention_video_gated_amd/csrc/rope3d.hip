@@ -39,6 +39,10 @@ struct RPArgs {
 
 template <typename E>
 __global__ __launch_bounds__(256) void rope3d_apply_kernel(RPArgs a) {
+    // no contraction in this kernel: the angle reduction below needs rh rounded, and
+    // fusing rh's product into the fraction's subtraction would count the product's
+    // remainder twice
+#pragma clang fp contract(off)
     constexpr int EPV = 16 / (int)sizeof(E);
     typedef E V __attribute__((ext_vector_type(EPV)));
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;

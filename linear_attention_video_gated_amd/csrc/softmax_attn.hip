@@ -282,14 +282,12 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
 
 template <typename E, int ND>
 hipError_t launch_sa(const SAArgs& a, hipStream_t st, void* const* ev) {
-    hipError_t e;
-    static bool attr_done = false;  // per instantiation
-    if (!attr_done) {
-        if ((e = hipFuncSetAttribute((const void*)sa_fwd<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     SAL<E, ND>::LDS_B)) != hipSuccess)
-            return e;
-        attr_done = true;
-    }
+    static PerDeviceOnce attr;  // per instantiation
+    hipError_t e = attr.run([] {
+        return hipFuncSetAttribute((const void*)sa_fwd<E, ND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   SAL<E, ND>::LDS_B);
+    });
+    if (e != hipSuccess) return e;
     if (ev && (e = hipEventRecord((hipEvent_t)ev[0], st)) != hipSuccess) return e;
     constexpr int lds = SAL<E, ND>::LDS_B;
     SAArgs r = a;

@@ -37,7 +37,8 @@ class Dims(ctypes.Structure):
                 ("frame_len", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p),
-                ("phase_windows", ctypes.c_int32)]
+                ("phase_windows", ctypes.c_int32), ("window_units", ctypes.c_int32),
+                ("group_frames", ctypes.c_int32)]
 
 
 _lib = None
@@ -101,47 +102,61 @@ def _dtype_code(dt):
     raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dt)
 
 
-def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0, events=None):
+def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0, events=None, plan=None):
     """events: None or a ctypes array of 6 * n hipEvent_t handles, recorded around the
-    three launches of each of the call's first n windows (per-kernel timing)."""
+    three launches of each of the call's first n windows (per-kernel timing).
+    plan: None or a dict with "window_units" and/or "group_frames" (the dims' plan
+    overrides, for tests and tuning)."""
+    plan = plan or {}
     return Dims(B, H, n_frames, frame_len, d, d, dtype_code, flags,
                 None if workspace is None else workspace.data_ptr(), nbytes,
                 None if events is None else ctypes.cast(events, ctypes.c_void_p).value,
-                0 if events is None else len(events) // 6)
+                0 if events is None else len(events) // 6,
+                int(plan.get("window_units", 0)), int(plan.get("group_frames", 0)))
 
 
-def window_count(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K, entry=ENTRY_FORWARD):
+def window_count(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K, entry=ENTRY_FORWARD,
+                 plan=None):
     """gdn_window_count: the number of windows (three launches each) such a call makes."""
-    n = lib().gdn_window_count(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, _dtype_code(dtype), flags)),
-                               entry)
+    n = lib().gdn_window_count(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, _dtype_code(dtype), flags,
+                                                      plan=plan)), entry)
     _check(min(n, 0))
     return n
 
 
 def workspace_bytes(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K,
-                    entry=ENTRY_FORWARD):
-    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(dtype), flags)
+                    entry=ENTRY_FORWARD, plan=None):
+    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(dtype), flags, plan=plan)
     return lib().gdn_workspace_bytes(ctypes.byref(dims), entry)
 
 
+# One scratch buffer per (device, stream): calls on different streams may run at the
+# same time and must not share one.  Each buffer is allocated while its stream is
+# current, so torch's caching allocator reuses its memory only in that stream's order
+# (also when a larger call replaces it).
 _ws_cache = {}
 
 
-def _workspace(device, nbytes):
-    """A cached uint8 device buffer of at least nbytes (grown on demand, per device)."""
+def _workspace(device, nbytes, stream):
+    """A cached uint8 device buffer of at least nbytes for calls on `stream`."""
     if nbytes == 0:
         return None
-    key = torch.device(device)
+    key = (torch.device(device), stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache.pop(key, None)
+        with torch.cuda.stream(stream):
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
 
-def _stream(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+def _stream_of(device, stream):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _handle(stream):
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _shapes(q, k, v, n_frames, frame_len):
@@ -179,80 +194,91 @@ def _f32(t, shape, name):
 
 def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
                   out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
-                  events=None, _entry=ENTRY_FORWARD):
+                  events=None, plan=None, _entry=ENTRY_FORWARD):
     """gdn_frame_forward.  Returns (out [B,H,T,d], state_out [B,H,d,d] float32 or None).
-    out_dtype=torch.float32 (or a float32 ``out``) returns the unrounded float32 result."""
+    out_dtype=torch.float32 (or a float32 ``out``) returns the unrounded float32 result.
+    stream: a torch stream of q's device (default: its current stream); the outputs this
+    function allocates and its scratch buffer belong to that stream.  plan: the dims' plan
+    overrides (see make_dims)."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     alpha = _f32(alpha, (B, H, T), "alpha")
     beta = _f32(beta, (B, H, T), "beta")
     state_in = _f32(state_in, (B, H, d, d), "state_in")
-    out, flags = _out(q, out, out_dtype, flags)
-    if state_out is None and return_state:
-        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    state_out = _f32(state_out, (B, H, d, d), "state_out")
-    code = _dtype_code(q.dtype)
-    need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
-                                     _entry)
-    ws = _workspace(q.device, need)
-    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
-    fn = lib().gdn_token_forward if _entry == ENTRY_TOKEN else lib().gdn_frame_forward
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
-              ctypes.byref(dims), _stream(q.device, stream)))
+    st = _stream_of(q.device, stream)
+    with torch.cuda.device(q.device), torch.cuda.stream(st):
+        out, flags = _out(q, out, out_dtype, flags)
+        if state_out is None and return_state:
+            state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+        state_out = _f32(state_out, (B, H, d, d), "state_out")
+        code = _dtype_code(q.dtype)
+        need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags,
+                                                                plan=plan)), _entry)
+        ws = _workspace(q.device, need, st)
+        dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events,
+                         plan)
+        fn = lib().gdn_token_forward if _entry == ENTRY_TOKEN else lib().gdn_frame_forward
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+                  ctypes.byref(dims), _handle(st)))
     return out, state_out
 
 
 def token_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
                   out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
-                  events=None):
+                  events=None, plan=None):
     """gdn_token_forward: every token reads the state after itself (o_t = S_t q_t).
     Same arguments and returns as frame_forward."""
     return frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=state_in, state_out=state_out,
                          out=out, flags=flags, return_state=return_state, stream=stream, out_dtype=out_dtype,
-                         events=events, _entry=ENTRY_TOKEN)
+                         events=events, plan=plan, _entry=ENTRY_TOKEN)
 
 
 def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, out=None,
-                           flags=NORMALIZE_K, stream=None, out_dtype=None, events=None):
+                           flags=NORMALIZE_K, stream=None, out_dtype=None, events=None, plan=None):
     """gdn_frame_forward_readonly.  Returns out; state_in is never written."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     alpha = _f32(alpha, (B, H, T), "alpha")
     beta = _f32(beta, (B, H, T), "beta")
     state_in = _f32(state_in, (B, H, d, d), "state_in")
-    out, flags = _out(q, out, out_dtype, flags)
-    code = _dtype_code(q.dtype)
-    need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
-                                     ENTRY_READONLY)
-    ws = _workspace(q.device, need)
-    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
-    _check(lib().gdn_frame_forward_readonly(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                            _ptr(state_in), _ptr(out), ctypes.byref(dims),
-                                            _stream(q.device, stream)))
+    st = _stream_of(q.device, stream)
+    with torch.cuda.device(q.device), torch.cuda.stream(st):
+        out, flags = _out(q, out, out_dtype, flags)
+        code = _dtype_code(q.dtype)
+        need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags,
+                                                                plan=plan)), ENTRY_READONLY)
+        ws = _workspace(q.device, need, st)
+        dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events,
+                         plan)
+        _check(lib().gdn_frame_forward_readonly(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                                _ptr(state_in), _ptr(out), ctypes.byref(dims), _handle(st)))
     return out
 
 
 def linear_attn_block_causal(q, k, v, n_frames, frame_len, state_in=None, z_in=None, state_out=None,
                              z_out=None, out=None, flags=RELU_QK, return_state=True, stream=None,
-                             out_dtype=None, events=None):
+                             out_dtype=None, events=None, plan=None):
     """linear_attn_block_causal.  Returns (out, state_out [B,H,d,d], z_out [B,H,d])."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     state_in = _f32(state_in, (B, H, d, d), "state_in")
     z_in = _f32(z_in, (B, H, d), "z_in")
-    out, flags = _out(q, out, out_dtype, flags)
-    if return_state:
-        if state_out is None:
-            state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-        if z_out is None:
-            z_out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
-    state_out = _f32(state_out, (B, H, d, d), "state_out")
-    z_out = _f32(z_out, (B, H, d), "z_out")
-    code = _dtype_code(q.dtype)
-    need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags)),
-                                     ENTRY_BLOCK_CAUSAL)
-    ws = _workspace(q.device, need)
-    dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events)
-    _check(lib().linear_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(z_in),
-                                          _ptr(state_out), _ptr(z_out), _ptr(out), ctypes.byref(dims),
-                                          _stream(q.device, stream)))
+    st = _stream_of(q.device, stream)
+    with torch.cuda.device(q.device), torch.cuda.stream(st):
+        out, flags = _out(q, out, out_dtype, flags)
+        if return_state:
+            if state_out is None:
+                state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+            if z_out is None:
+                z_out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+        state_out = _f32(state_out, (B, H, d, d), "state_out")
+        z_out = _f32(z_out, (B, H, d), "z_out")
+        code = _dtype_code(q.dtype)
+        need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags,
+                                                                plan=plan)), ENTRY_BLOCK_CAUSAL)
+        ws = _workspace(q.device, need, st)
+        dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events,
+                         plan)
+        _check(lib().linear_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(z_in),
+                                              _ptr(state_out), _ptr(z_out), _ptr(out), ctypes.byref(dims),
+                                              _handle(st)))
     return out, state_out, z_out
 
 
@@ -270,10 +296,12 @@ def softmax_attn_block_causal(q, k, v, n_frames, kv_frames, frame_len, out=None,
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
             raise ValueError("q, k, v must be contiguous device tensors of one dtype")
-    out, flags = _out(q, out, out_dtype, 0)
-    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(q.dtype), flags, events=events)
-    _check(lib().softmax_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(kv_frames),
-                                           ctypes.byref(dims), _stream(q.device, stream)))
+    st = _stream_of(q.device, stream)
+    with torch.cuda.device(q.device), torch.cuda.stream(st):
+        out, flags = _out(q, out, out_dtype, 0)
+        dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(q.dtype), flags, events=events)
+        _check(lib().softmax_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(kv_frames),
+                                               ctypes.byref(dims), _handle(st)))
     return out
 
 
@@ -289,18 +317,20 @@ def temporal_conv_block(x, weight, bias=None, carry_in=None, carry_out=None, out
         raise ValueError("carry_in must be a contiguous [B, P, C] tensor of x's dtype")
     weight = _f32(weight, (3, C), "weight")
     bias = _f32(bias, (C,), "bias")
-    if out is None:
-        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    if tuple(out.shape) != tuple(x.shape) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like x")
-    flags = OUT_F32 if out.dtype == torch.float32 and x.dtype != torch.float32 else 0
-    if out.dtype not in (x.dtype, torch.float32):
-        raise ValueError("out must have x's dtype or float32")
-    if carry_out is None and return_carry:
-        carry_out = torch.empty((B, P, C), dtype=x.dtype, device=x.device)
-    ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
-    _check(lib().temporal_conv_block(_ptr(x), _ptr(carry_in), _ptr(weight), _ptr(bias), _ptr(out), _ptr(carry_out),
-                                     B, F, P, C, _dtype_code(x.dtype), flags, ev, _stream(x.device, stream)))
+    st = _stream_of(x.device, stream)
+    with torch.cuda.device(x.device), torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+        if tuple(out.shape) != tuple(x.shape) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped like x")
+        flags = OUT_F32 if out.dtype == torch.float32 and x.dtype != torch.float32 else 0
+        if out.dtype not in (x.dtype, torch.float32):
+            raise ValueError("out must have x's dtype or float32")
+        if carry_out is None and return_carry:
+            carry_out = torch.empty((B, P, C), dtype=x.dtype, device=x.device)
+        ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
+        _check(lib().temporal_conv_block(_ptr(x), _ptr(carry_in), _ptr(weight), _ptr(bias), _ptr(out),
+                                         _ptr(carry_out), B, F, P, C, _dtype_code(x.dtype), flags, ev, _handle(st)))
     return out, carry_out
 
 
@@ -312,6 +342,8 @@ def rope3d_apply(x, n_frames, grid_h, grid_w, d_t, d_h, frame_offset=0, base=100
     if T != n_frames * grid_h * grid_w:
         raise ValueError("T=%d != n_frames * grid_h * grid_w" % T)
     ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
-    _check(lib().rope3d_apply(_ptr(x), B, H, n_frames, grid_h, grid_w, d, d_t, d_h, frame_offset, float(base),
-                              _dtype_code(x.dtype), ev, _stream(x.device, stream)))
+    st = _stream_of(x.device, stream)
+    with torch.cuda.device(x.device):
+        _check(lib().rope3d_apply(_ptr(x), B, H, n_frames, grid_h, grid_w, d, d_t, d_h, frame_offset, float(base),
+                                  _dtype_code(x.dtype), ev, _handle(st)))
     return x

@@ -16,6 +16,10 @@ Distributions (per token, per head):
   "near_one" gates: alpha = exp(-1e-3 * softplus(N(0, 1))), a slow decay that keeps
   the carried state alive across many frames.
   state_in (when requested) ~ N(0, std^2) in fp32.
+  keys="raw": k ~ N(0, 1) times a per-token scale 10^U(-2, 2), not normalised (the
+  kernels' own L2 normalisation then does real work); keys="short": k ~ N(0, 1) / sqrt(d)
+  times 10^U(-1, 0) per token, |k| below about 1 (unnormalised keys that keep the delta
+  rule contractive, for calls without normalisation).
 """
 from __future__ import annotations
 
@@ -38,14 +42,23 @@ def _normal(shape, seed, device):
 
 
 def gdn_inputs(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, workload_id=0, step=0,
-               device="cpu", gates="config", state_std=None, dv=None):
+               device="cpu", gates="config", state_std=None, dv=None, keys="unit"):
     """Inputs of the frame-wise gated delta rule: q, k, v [B,H,T,d], alpha, beta [B,H,T],
-    state_in [B,H,d_v,d_k] or None."""
+    state_in [B,H,d_v,d_k] or None.  keys: "unit" (L2-normalised), "raw" or "short"
+    (see the module docstring)."""
     dv = d if dv is None else dv
     T = n_frames * frame_len
     q = _normal((B, H, T, d), seed_for(workload_id, "q", step), device)
     k = _normal((B, H, T, d), seed_for(workload_id, "k", step), device)
-    k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    if keys == "unit":
+        k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    elif keys in ("raw", "short"):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed_for(workload_id, "z", step))
+        u = torch.rand((B, H, T, 1), generator=g, device=device, dtype=torch.float32)
+        k = k * (10.0 ** (4.0 * u - 2.0)) if keys == "raw" else k * (10.0 ** (u - 1.0)) / d ** 0.5
+    else:
+        raise ValueError(keys)
     v = _normal((B, H, T, dv), seed_for(workload_id, "v", step), device)
     xa = _normal((B, H, T), seed_for(workload_id, "alpha", step), device)
     xb = _normal((B, H, T), seed_for(workload_id, "beta", step), device)

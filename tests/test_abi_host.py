@@ -37,15 +37,15 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 6
+    assert gdn.lib().gdn_abi_version() == 7
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
     assert gdn.status_str(-99) == "unknown status"
 
 
-def dims(B=1, H=2, F=3, N=16, d=32, dtype=gdn.GDN_BF16, flags=gdn.NORMALIZE_K, ws=None, nbytes=0):
-    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None, 0)
+def dims(B=1, H=2, F=3, N=16, d=32, dtype=gdn.GDN_BF16, flags=gdn.NORMALIZE_K, ws=None, nbytes=0, wu=0, gf=0):
+    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None, 0, wu, gf)
 
 
 def wsb(dm, entry=gdn.ENTRY_FORWARD):
@@ -84,6 +84,17 @@ def test_window_plan():
                               gdn.ENTRY_BLOCK_CAUSAL) == 1
 
 
+def test_plan_overrides():
+    """dims.window_units and dims.group_frames cut the call differently (tests and tuning)."""
+    L = gdn.lib()
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=2, F=7, N=90, d=112, wu=4)), gdn.ENTRY_FORWARD) == 4
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=2, F=7, N=90, d=112, wu=4, gf=1)), gdn.ENTRY_FORWARD) == 4
+    # a group is never cut by a window: 3-frame groups in windows of >= 3 frames
+    assert L.gdn_window_count(ctypes.byref(dims(B=1, H=2, F=7, N=90, d=112, wu=4, gf=3)), gdn.ENTRY_FORWARD) == 3
+    # more frames per group -> fewer group maps in the workspace
+    assert wsb(dims(B=1, H=2, F=40, N=90, d=112, gf=40)) < wsb(dims(B=1, H=2, F=40, N=90, d=112, gf=1))
+
+
 def test_workspace_zero_for_invalid_or_empty():
     assert wsb(dims(d=48)) == 0            # unsupported d
     assert wsb(dims(dtype=7)) == 0
@@ -94,6 +105,7 @@ def test_workspace_zero_for_invalid_or_empty():
 @pytest.mark.parametrize("field,val,code", [
     ("dtype", 5, -3), ("B", -1, -2), ("frame_len", 0, -2), ("n_frames", -2, -2),
     ("d_k", 48, -7), ("flags", 32, -7), ("flags", gdn.RELU_QK, -7),
+    ("window_units", -1, -2), ("group_frames", -3, -2),
 ])
 def test_bad_dims_rejected(field, val, code):
     dm = dims()

@@ -141,15 +141,16 @@ def test_gdn_state_in_place():
     check("state", s, rs, 2e-2)
 
 
-def test_gdn_multi_window_equals_single(monkeypatch):
+def test_gdn_multi_window_equals_single():
     """Frames processed in several windows (state carried through the workspace)."""
     inp = gdn_inputs(1, 2, 7, 90, 112, workload_id=340, state_std=0.2, gates="near_one")
     dv = to_dev(inp)
     o1, s1 = gdn.frame_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 7, 90, state_in=dv["state_in"],
                                out_dtype=torch.float32)
-    monkeypatch.setenv("GDN_WINDOW_UNITS", "4")  # 2 frames per window for B*H = 2
+    plan = {"window_units": 4}  # 2 frames per window for B*H = 2
+    assert gdn.window_count(1, 2, 7, 90, 112, plan=plan) > 1
     o2, s2 = gdn.frame_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 7, 90, state_in=dv["state_in"],
-                               out_dtype=torch.float32)
+                               out_dtype=torch.float32, plan=plan)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     ro, rs = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], 7, 90,
@@ -215,12 +216,12 @@ def test_block_causal_480p_workload():
     run_bc_case(1, 20, 21, 390, 112, torch.bfloat16, seed=1)
 
 
-def test_block_causal_multi_window(monkeypatch):
+def test_block_causal_multi_window():
     inp = block_causal_inputs(1, 2, 5, 40, 112, workload_id=420, state_std=0.5)
     dv = to_dev(inp)
     o1, s1, z1 = gdn.linear_attn_block_causal(dv["q"], dv["k"], dv["v"], 5, 40, state_in=dv["state_in"], z_in=dv["z_in"])
-    monkeypatch.setenv("GDN_WINDOW_UNITS", "4")
-    o2, s2, z2 = gdn.linear_attn_block_causal(dv["q"], dv["k"], dv["v"], 5, 40, state_in=dv["state_in"], z_in=dv["z_in"])
+    o2, s2, z2 = gdn.linear_attn_block_causal(dv["q"], dv["k"], dv["v"], 5, 40, state_in=dv["state_in"], z_in=dv["z_in"],
+                                              plan={"window_units": 4})
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(z1, z2)
 
@@ -259,10 +260,10 @@ def test_gdn_gate_logits(entry, dtype):
 @pytest.mark.parametrize("d,dtype", [(112, torch.bfloat16), (16, torch.bfloat16), (32, torch.bfloat16),
                                      (64, torch.bfloat16), (128, torch.bfloat16), (16, torch.float32),
                                      (32, torch.float32), (64, torch.float32), (128, torch.float32)])
-def test_gdn_group_paths(entry, group, d, dtype, monkeypatch):
+def test_gdn_group_paths(entry, group, d, dtype):
     """Both organisations of a call: one frame per group (maps, chain over groups, readout)
     and a single group per (b, h) (maps from the known start state, no chain)."""
-    monkeypatch.setenv("GDN_GROUP_FRAMES", group)
+    plan = {"group_frames": int(group)}
     F, N = 5, 100
     inp = gdn_inputs(2, 2, F, N, d, dtype=dtype, workload_id=370, state_std=0.2, gates="near_one")
     dv = to_dev(inp)
@@ -270,12 +271,12 @@ def test_gdn_group_paths(entry, group, d, dtype, monkeypatch):
     s = dv["state_in"].clone()
     if entry == "readonly":
         out = gdn.frame_forward_readonly(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], F, N, state_in=s,
-                                         out_dtype=torch.float32)
+                                         out_dtype=torch.float32, plan=plan)
         st = None
     else:
         fn = gdn.token_forward if entry == "token" else gdn.frame_forward
         out, st = fn(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], F, N, state_in=s, state_out=s,
-                     out_dtype=torch.float32)  # state updated in place
+                     out_dtype=torch.float32, plan=plan)  # state updated in place
     torch.cuda.synchronize()
     nf, fl = (F * N, 1) if entry == "token" else (F, N)
     ro, rs = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], nf, fl,

@@ -28,6 +28,7 @@ def say(*a):
     (1, 20, 21, 22, 40, 112, 36, 38, 0),  # the 720p latent grid, d = 112
     (2, 3, 2, 3, 7, 64, 0, 32, 1000),     # no temporal part; late frames
     (1, 1, 5, 1, 1, 8, 8, 0, 3),          # temporal part only
+    (1, 2, 3, 2, 3, 16, 4, 6, (1 << 24) - 3),  # frames up to the largest exact float position
 ])
 def test_rope3d_parity(dtype, case):
     B, H, F, gh, gw, d, dt, dh, off = case

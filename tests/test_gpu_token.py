@@ -110,14 +110,14 @@ def test_token_frame_end_rows_match_frame_readout():
     assert (st.double() - sf.double()).abs().max() <= 2e-2 * sf.double().pow(2).mean().sqrt()
 
 
-def test_token_multi_window_equals_single(monkeypatch):
+def test_token_multi_window_equals_single():
     inp = gdn_inputs(1, 2, 7, 90, 112, workload_id=670, state_std=0.2, gates="near_one")
     dv = to_dev(inp)
     o1, s1 = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 7, 90, state_in=dv["state_in"],
                                out_dtype=torch.float32)
-    monkeypatch.setenv("GDN_WINDOW_UNITS", "4")  # 2 frames per window for B*H = 2
+    plan = {"window_units": 4}  # 2 frames per window for B*H = 2
     o2, s2 = gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 7, 90, state_in=dv["state_in"],
-                               out_dtype=torch.float32)
+                               out_dtype=torch.float32, plan=plan)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     ro, rs = oracle_tokens(inp, 7 * 90)
