@@ -9,7 +9,11 @@ inputs already resident in HBM.  Prints one JSON line:
   roofline      the dominant kernel's achieved algorithmic bandwidth against 8 TB/s; its
                 duration comes from HIP events the library records around each launch
   path          the same for the whole call (all three kernels)
-  cpu_baseline  the CPU oracle (float64, token by token, OpenMP) on a bounded sample
+  cpu_baseline  the CPU oracle (float64, token by token, OpenMP) on a bounded sample, with
+                the host CPU model and a one-thread figure
+  ms_per_step is the mean over the timed steps; ms_per_step_median and ms_per_step_min come
+  from events recorded between consecutive steps.  hbm_copy_GBps is the rate of a plain
+  2 GiB device copy on the same box (read + write bytes / time).
 """
 from __future__ import annotations
 
@@ -125,8 +129,9 @@ class HipEvents:
 
 
 def read_counters(workload, kind):
-    """HBM bytes per launch of the dominant kernel from a committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources (else None)."""
+    """HBM bytes per launch and matrix-core busy fraction of the dominant kernel from a
+    committed rocprofv3 counter summary, if it was taken on the current kernel sources
+    (else None)."""
     path = os.path.join(PROFILES, "counters_%s.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -138,9 +143,14 @@ def read_counters(workload, kind):
     if kv.get("kernel_source_sha") != kernel_source_hash(kind):
         return None
     try:
-        return {"kernel": kv["kernel"], "bytes": float(kv["hbm_bytes_per_launch"])}
+        r = {"kernel": kv["kernel"], "bytes": float(kv["hbm_bytes_per_launch"])}
     except (KeyError, ValueError):
         return None
+    try:
+        r["mfma_busy"] = float(kv["mfma_busy_frac"])
+    except (KeyError, ValueError):
+        r["mfma_busy"] = None
+    return r
 
 
 def setup(wl, device, gates="config"):
@@ -185,19 +195,23 @@ def scrubber(wl, device):
     return lambda i: buf.sum()
 
 
-def time_steps(step, steps, scrub=None, events=None):
-    """ms per step.  Without a scrub the steps run back to back between two events; with
-    one, each step is bracketed by its own events and the scrub runs outside them."""
+def time_steps(step, steps, scrub=None, events=None, per_step=None):
+    """ms per step (the mean).  Without a scrub the steps run back to back, with an event
+    recorded between consecutive steps (no synchronisation inside the timed region); with
+    one, each step is bracketed by its own events and the scrub runs outside them.  The
+    per-step times are appended to `per_step` when given."""
     import torch
     torch.cuda.synchronize()
     if scrub is None:
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        marks[0].record()
         for i in range(steps):
             step(events[i]) if events else step()
-        t1.record()
+            marks[i + 1].record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        if per_step is not None:
+            per_step.extend(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+        return marks[0].elapsed_time(marks[steps]) / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         scrub(i)
@@ -205,7 +219,10 @@ def time_steps(step, steps, scrub=None, events=None):
         step(events[i]) if events else step()
         ev[i][1].record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    times = [a.elapsed_time(b) for a, b in ev]
+    if per_step is not None:
+        per_step.extend(times)
+    return sum(times) / steps
 
 
 def near_one_timing(wl, device, ms_graded, scrub=None, steps=20, warmup=5):
@@ -285,12 +302,30 @@ def copy_bandwidth_gbps(device, nbytes=2 << 30):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(wl, inp, budget_heads=16, frames=None):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    """Cores this process may run on (the machine's CPU share), at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, inp, budget_heads=20, frames=None, threads=None):
     """The oracle (as it stands) on a bounded sample of the same inputs, on host cores."""
     import numpy as np
     import oracle
-    ncpu = os.cpu_count() or 1
-    cores = max(1, min(16, ncpu, wl.B * wl.H))
+    cores = max(1, min(threads or host_cores(), wl.B * wl.H))
     heads = min(wl.H, budget_heads)
     frames = wl.n_frames if frames is None else min(frames, wl.n_frames)
     T = frames * wl.frame_len
@@ -327,7 +362,7 @@ def cpu_baseline(wl, inp, budget_heads=16, frames=None):
     dt = time.perf_counter() - t0
     # tokens/s of the whole workload: the sample covers heads/H of each token's work
     value = T * heads / wl.H / dt
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": "B=1, %d of %d heads, %d of %d frames x %d tokens (%.1f s on %d threads, float64)"
                       % (heads, wl.H, frames, wl.n_frames, wl.frame_len, dt, cores)}
 
@@ -344,7 +379,8 @@ def main():
     ap.add_argument("--gates", default="config", choices=("config", "near_one"),
                     help="gate distribution of the timed run (near_one: the alpha ~ 1 stress variant)")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a 2 GiB device copy (a known-size kernel for counter scaling)")
+                    help="accepted for older command lines: the 2 GiB device copy (the box's reachable HBM "
+                         "rate, and a known-size kernel for counter scaling) now always runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (got --gpus %d); the multi-GPU sharding "
@@ -380,9 +416,13 @@ def main():
     ev = [hip.create(6 * nwin) for _ in range(args.steps)]
     scrub = scrubber(wl, dev)
     torch.cuda.synchronize()
+    per_step = []
     t_wall0 = time.perf_counter()
-    ms_step = time_steps(step, args.steps, scrub, ev)
+    ms_step = time_steps(step, args.steps, scrub, ev, per_step)
     t_wall = time.perf_counter() - t_wall0
+    per_step.sort()
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (
+        per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     names = {"block_causal": BC_KERNELS, "token": TOKEN_KERNELS, "softmax": SA_KERNELS,
              "tconv": TC_KERNELS, "rope": RP_KERNELS}.get(wl.kind, GDN_KERNELS)
     kms = [0.0] * nk  # per call, summed over the call's windows
@@ -403,20 +443,21 @@ def main():
     kms_launch = kms[j] / nwin
     counters = read_counters(args.workload, wl.kind)
     traffic = counters["bytes"] if counters and counters["kernel"] == kname else None
+    mfma_busy = counters["mfma_busy"] if counters and counters["kernel"] == kname else None
     if wl.kind == "softmax":
         # a dense contraction (QK^T and PV on the matrix cores): the MFMA roofline binds
         flops = softmax_flops(wl)
         achieved = flops / (kms_launch * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[wl.dtype]
         roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic, "mfma_busy_frac": mfma_busy, "mfma_busy_frac": mfma_busy,
                     "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_flops": flops}
     elif wl.kind in ("tconv", "rope"):
         # tconv: x read, y written, carry read and written; rope: x read and written
         kbytes = ((2 * wl.n_frames + 2) if wl.kind == "tconv" else 2 * wl.n_frames) * wl.B * wl.frame_len * wl.H * wl.d * es
         achieved = kbytes / (kms_launch * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "mfma_busy_frac": mfma_busy,
                     "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_bytes": kbytes}
     else:
         per = kernel_bytes_per_token_head(wl.kind, wl.d, es)
@@ -426,7 +467,7 @@ def main():
         achieved = kbytes / (kms_launch * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin,
+                    "traffic": traffic, "mfma_busy_frac": mfma_busy, "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin,
                     "algorithmic_bytes": round(kbytes),
                     "all_kernels_ms_per_call": {n: round(x, 4) for n, x in zip(names, kms)}}
     path_per = path_bytes_per_token_head(wl.kind, wl.d, es)
@@ -440,18 +481,25 @@ def main():
         # the alpha ~ 1 stress variant (slow decay: the maps and states keep full range);
         # the kernels do the same work whatever the gate values, so this should match
         extra["alpha_near_one"] = near_one_timing(wl, dev, ms_step, scrub)
-    if args.copy_calib:
-        extra["hbm_copy_GBps"] = round(copy_bandwidth_gbps(dev), 1)
+    # the HBM rate a plain 2 GiB device copy reaches on this machine, beside the spec peak
+    copy_gbps = copy_bandwidth_gbps(dev)
+    extra["hbm_copy_GBps"] = round(copy_gbps, 1)
+    path["frac_of_copy_rate"] = round(path_gbps / copy_gbps, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         # the softmax oracle costs ~N^2 F^2 d per head: a few heads of the same call
-        cpu = cpu_baseline(wl, inp, budget_heads=4 if wl.kind == "softmax" else 16)
+        cpu = cpu_baseline(wl, inp, budget_heads=4 if wl.kind == "softmax" else 20)
+        if wl.kind in ("gdn", "token", "block_causal"):
+            # one thread on one head and a quarter of the frames, for the per-core rate
+            one = cpu_baseline(wl, inp, budget_heads=1, frames=max(1, wl.n_frames // 4), threads=1)
+            cpu["single_thread"] = {"value": one["value"], "sample": one["sample"]}
 
     line = {
         "metric": {"softmax": METRIC_SA, "tconv": METRIC_TC, "rope": METRIC_RP}.get(wl.kind, METRIC),
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(ms_median, 4), "ms_per_step_min": round(per_step[0], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes of 720p/480p latent frames)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "d": wl.d, "n_frames": wl.n_frames,
