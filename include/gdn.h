@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum {
     GDN_OK = 0,
@@ -143,6 +143,27 @@ int gdn_frame_forward(const void* q, const void* k, const void* v,
                       const float* alpha, const float* beta,
                       const float* state_in, float* state_out, void* out,
                       const gdn_dims_t* dims, void* stream);
+
+/*
+ * gdn_frame_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * arguments and results, with the scratch taken from a static device array of
+ * gdn_noalloc_scratch_bytes() bytes (64 MiB) that each device holds until the process
+ * ends, instead of dims->workspace (ignored).  The entry and the kernels it launches
+ * allocate nothing.  A call whose workspace (gdn_workspace_bytes(dims, GDN_ENTRY_FORWARD))
+ * exceeds the array returns GDN_ERR_WORKSPACE before anything is enqueued; a smaller
+ * dims->window_units makes large calls fit.  All calls on one device share its array:
+ * calls that may run at the same time on one device (other streams, other host threads)
+ * race and must be serialised by the caller.  The array needs no initialisation and keeps
+ * the last call's garbage.
+ */
+int gdn_frame_forward_noalloc(const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta,
+                              const float* state_in, float* state_out, void* out,
+                              const gdn_dims_t* dims, void* stream);
+
+/* Size in bytes of the static scratch array of gdn_frame_forward_noalloc. */
+size_t gdn_noalloc_scratch_bytes(void);
 
 /*
  * Read-only-state variant for the denoising steps inside a frame ("SANA-Video" talk,

@@ -187,9 +187,60 @@ int gdn_common(const void* q, const void* k, const void* v, const float* alpha, 
 }
 
 }  // namespace
+
+// Scratch of the allocation-free entry (gdn_frame_forward_noalloc): one array per device,
+// held by the device until the process ends.  In host code the name `scratch` is a
+// host-side stand-in, never a device address: its device address is looked up once per
+// device (scratch_on_device) and only that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+hipError_t scratch_on_device(void** out) {
+    static PerDeviceOnce once;
+    static void* addr[PerDeviceOnce::kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= PerDeviceOnce::kMaxDevices) return hipErrorInvalidDevice;
+    e = once.run([&] {
+        void* ptr = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        addr[dev] = r == hipSuccess ? ptr : nullptr;
+        return r == hipSuccess && !ptr ? hipErrorInvalidSymbol : r;
+    });
+    if (e != hipSuccess) return e;
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
 }  // namespace gdn
 
 using namespace gdn;
+
+GDN_API int gdn_frame_forward_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                                      const float* beta, const float* state_in, float* state_out, void* out,
+                                      const gdn_dims_t* dims, void* stream) {
+    if (!dims) return GDN_ERR_NULL;
+    gdn_dims_t d = *dims;  // the caller's workspace fields are ignored
+    d.workspace = nullptr;
+    d.workspace_bytes = 0;
+    Plan p;
+    const int rc = plan_call(&d, GDN_ENTRY_FORWARD, &p);
+    if (rc != GDN_OK) return rc;
+    if (p.total > kScratchBytes) return GDN_ERR_WORKSPACE;  // beyond the static scratch
+    if (p.total > 0) {
+        void* ws = nullptr;
+        if (scratch_on_device(&ws) != hipSuccess) return GDN_ERR_HIP;
+        d.workspace = ws;
+        d.workspace_bytes = kScratchBytes;
+    }
+    return gdn_common(q, k, v, alpha, beta, state_in, state_out, out, &d, stream, GDN_ENTRY_FORWARD);
+}
+
+GDN_API size_t gdn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 GDN_API int gdn_frame_forward(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, const float* state_in, float* state_out, void* out,

@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(PKG, "libgdn_mi355x.so")
 GDN_BF16, GDN_F32 = 0, 1
 NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS = 1, 2, 4, 8, 16
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
-EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
-           "softmax_attn_block_causal", "temporal_conv_block", "rope3d_apply", "gdn_workspace_bytes", "gdn_window_count", "gdn_status_str", "gdn_abi_version")
+EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_noalloc", "gdn_noalloc_scratch_bytes",
+           "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
+           "softmax_attn_block_causal", "temporal_conv_block", "rope3d_apply", "gdn_workspace_bytes",
+           "gdn_window_count", "gdn_status_str", "gdn_abi_version")
 
 
 class GdnLibraryMissing(RuntimeError):
@@ -56,6 +58,10 @@ def lib():
         dp = ctypes.POINTER(Dims)
         L.gdn_frame_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
         L.gdn_frame_forward.restype = ctypes.c_int
+        L.gdn_frame_forward_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
+        L.gdn_frame_forward_noalloc.restype = ctypes.c_int
+        L.gdn_noalloc_scratch_bytes.argtypes = []
+        L.gdn_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.gdn_token_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, dp, vp]
         L.gdn_token_forward.restype = ctypes.c_int
         L.gdn_frame_forward_readonly.argtypes = [vp, vp, vp, fp, fp, fp, vp, dp, vp]
@@ -219,6 +225,27 @@ def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, stat
         fn = lib().gdn_token_forward if _entry == ENTRY_TOKEN else lib().gdn_frame_forward
         _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                   ctypes.byref(dims), _handle(st)))
+    return out, state_out
+
+
+def frame_forward_noalloc(q, k, v, alpha, beta, n_frames, frame_len, out, state_in=None, state_out=None,
+                          flags=NORMALIZE_K, stream=None, plan=None):
+    """gdn_frame_forward_noalloc: gdn_frame_forward with the library's static device
+    scratch instead of a workspace.  Allocates nothing: ``out`` (q's shape, q's dtype or
+    float32) must be given, state_out is optional.  Returns (out, state_out)."""
+    B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
+    alpha = _f32(alpha, (B, H, T), "alpha")
+    beta = _f32(beta, (B, H, T), "beta")
+    state_in = _f32(state_in, (B, H, d, d), "state_in")
+    state_out = _f32(state_out, (B, H, d, d), "state_out")
+    if out is None:
+        raise ValueError("frame_forward_noalloc allocates nothing: pass out")
+    out, flags = _out(q, out, None, flags)
+    st = _stream_of(q.device, stream)
+    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(q.dtype), flags, plan=plan)
+    with torch.cuda.device(q.device):
+        _check(lib().gdn_frame_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+                                               _ptr(state_out), _ptr(out), ctypes.byref(dims), _handle(st)))
     return out, state_out
 
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 7
+    assert gdn.lib().gdn_abi_version() == 8
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
@@ -240,3 +240,23 @@ def test_rope3d_argument_checks():
     assert rp(x=None) == -1
     assert rp(x=FAKE + 8) == -4
     assert rp(B=0, x=None) == 0 and rp(F=0, x=None) == 0
+
+
+def test_noalloc_entry_rejects_calls_beyond_its_scratch():
+    """gdn_frame_forward_noalloc: a call whose workspace exceeds the static scratch returns
+    GDN_ERR_WORKSPACE before anything is enqueued (the 60 s rollout in one window does);
+    argument errors are those of gdn_frame_forward."""
+    L = gdn.lib()
+    cap = L.gdn_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    big = dims(B=1, H=20, F=240, N=880, d=112)
+    assert wsb(big) > cap
+    f = L.gdn_frame_forward_noalloc
+    args = (FAKE, FAKE + 2 ** 28, FAKE + 2 ** 29, FAKE + 2 ** 30, FAKE + 2 ** 31, None, None, FAKE + 2 ** 32)
+    assert f(*args, ctypes.byref(big), None) == -6
+    assert f(*args, None, None) == -1
+    bad = dims(d=48)
+    assert f(*args, ctypes.byref(bad), None) == -7
+    # a smaller window makes the same call fit
+    small = dims(B=1, H=20, F=240, N=880, d=112, wu=400)
+    assert 0 < wsb(small) <= cap
