@@ -35,7 +35,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # is used only while its family's sources hash to the value recorded in it.
 _CSRC = "linear_attention_video_gated_amd/csrc/"
 KERNEL_SOURCES = {
-    "gdn": [_CSRC + f for f in ("gdn_frame.hip", "gdn_api.hip", "gdn_kernels.hpp", "common.hpp")],
+    "gdn": [_CSRC + f for f in ("gdn_frame.hpp", "gdn_frame.hip", "gdn_frame_rope.hip", "gdn_api.hip",
+                                "gdn_kernels.hpp", "gdn_plan.cpp", "common.hpp")],
     "block_causal": [_CSRC + f for f in ("block_causal.hip", "common.hpp")],
     "softmax": [_CSRC + f for f in ("softmax_attn.hip", "common.hpp")],
     "tconv": [_CSRC + f for f in ("temporal_conv.hip", "common.hpp")],
@@ -61,6 +62,7 @@ TC_KERNELS = ("tconv_block",)
 RP_KERNELS = ("rope3d_apply_kernel",)
 METRIC_RP = "3D rotary position embedding tokens/s (720p 5s q, H=20 d=112, in place) + % of HBM roofline"
 RP_GRID, RP_SPLIT = (22, 40), (36, 38)  # latent rows x columns of a 720p frame; d_t, d_h of d = 112
+ROPE_720P = {"d_t": RP_SPLIT[0], "d_h": RP_SPLIT[1], "grid_w": RP_GRID[1], "frame_offset": 0, "base": 10000.0}
 METRIC_TC = "causal temporal convolution with block carry tokens/s (720p 5s, C=2240) + % of HBM roofline"
 METRIC_SA = "frame-block-causal softmax attention fwd tokens/s (720p 5s, H=20 d=112) + % of bf16 MFMA peak"
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks of MI355X
@@ -278,8 +280,31 @@ def make_step(wl, inp, events=None):
     if wl.kind == "token":
         return lambda ev=None: gdn.token_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
                                                  state_in=inp["state_in"], state_out=st, out=out, events=ev)
+    if wl.kind == "gdn_rope":  # q and k rotated by the kernels as they load them
+        return lambda ev=None: gdn.frame_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
+                                                 state_in=inp["state_in"], state_out=st, out=out, events=ev,
+                                                 rope=ROPE_720P)
     return lambda ev=None: gdn.frame_forward(q, k, v, inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
                                              state_in=inp["state_in"], state_out=st, out=out, events=ev)
+
+
+def unfused_rope_timing(wl, inp, steps=10, warmup=3):
+    """ms per step of the same call with q and k rotated by two stand-alone in-place
+    passes (rope3d_apply) before an unrotated call: what the fused path replaces."""
+    import torch
+    from linear_attention_video_gated_amd import gdn
+    q, k = inp["q"].clone(), inp["k"].clone()
+    out = torch.empty_like(q)
+    st = torch.empty(wl.B, wl.H, wl.d, wl.d, device=q.device)
+
+    def step():
+        for x in (q, k):
+            gdn.rope3d_apply(x, wl.n_frames, RP_GRID[0], RP_GRID[1], RP_SPLIT[0], RP_SPLIT[1])
+        gdn.frame_forward(q, k, inp["v"], inp["alpha"], inp["beta"], wl.n_frames, wl.frame_len,
+                          state_in=inp["state_in"], state_out=st, out=out)
+    for _ in range(warmup):
+        step()
+    return round(time_steps(step, steps), 4)
 
 
 def copy_bandwidth_gbps(device, nbytes=2 << 30):
@@ -355,6 +380,9 @@ def cpu_baseline(wl, inp, budget_heads=20, frames=None, threads=None):
     else:
         a, b = take(inp["alpha"]), take(inp["beta"])
         s_in = inp["state_in"][:1, :heads].float().cpu().numpy() if inp["state_in"] is not None else None
+        if wl.kind == "gdn_rope":  # the rotation first, as the plain definition has it
+            q = oracle.rope3d(q, frames, RP_GRID[0], RP_GRID[1], RP_SPLIT[0], RP_SPLIT[1])
+            k = oracle.rope3d(k, frames, RP_GRID[0], RP_GRID[1], RP_SPLIT[0], RP_SPLIT[1])
         if wl.kind == "token":  # every token reads out: one-token frames
             oracle.gdn_forward(q, k, v, a, b, T, 1, state_in=s_in, n_threads=cores)
         else:
@@ -477,6 +505,8 @@ def main():
             "unit": "GB/s", "frac_of_8TBps": round(path_gbps / HBM_PEAK_GBPS, 4)}
 
     extra = {}
+    if wl.kind == "gdn_rope":
+        extra["unfused_rope_ms_per_step"] = unfused_rope_timing(wl, inp)
     if wl.kind in ("gdn", "stream", "token") and args.gates == "config":
         # the alpha ~ 1 stress variant (slow decay: the maps and states keep full range);
         # the kernels do the same work whatever the gate values, so this should match
@@ -490,7 +520,7 @@ def main():
     if not args.no_cpu_baseline:
         # the softmax oracle costs ~N^2 F^2 d per head: a few heads of the same call
         cpu = cpu_baseline(wl, inp, budget_heads=4 if wl.kind == "softmax" else 20)
-        if wl.kind in ("gdn", "token", "block_causal"):
+        if wl.kind in ("gdn", "gdn_rope", "token", "block_causal"):
             # one thread on one head and a quarter of the frames, for the per-core rate
             one = cpu_baseline(wl, inp, budget_heads=1, frames=max(1, wl.n_frames // 4), threads=1)
             cpu["single_thread"] = {"value": one["value"], "sample": one["sample"]}

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef enum {
     GDN_OK = 0,
@@ -98,10 +98,14 @@ enum {
     GDN_F_ADDITIVE = 1u << 1,    /* gated delta rule entries: S <- S + v k^T              */
     GDN_F_RELU_QK = 1u << 2,     /* block-causal entry: phi = ReLU on q and k (else id)  */
     GDN_F_OUT_F32 = 1u << 3,     /* out is float32 whatever dtype is (all entries)        */
-    GDN_F_GATE_LOGITS = 1u << 4  /* gated delta rule entries: alpha and beta hold logits a,
+    GDN_F_GATE_LOGITS = 1u << 4, /* gated delta rule entries: alpha and beta hold logits a,
                                     b; the gates are alpha = exp(-softplus(a)) (clamped
                                     below at FLT_MIN) and beta = 1 / (1 + e^-b), formed in
                                     float32 inside the kernels                            */
+    GDN_F_ROPE_QK = 1u << 5      /* gdn_frame_forward(_readonly, _noalloc): q and k are
+                                    rotated by the 3D rotary position embedding of
+                                    rope3d_apply (parameters in dims->rope_*) as the kernels
+                                    load them; the tensors in memory are not changed      */
 };
 
 enum { GDN_ENTRY_FORWARD = 0, GDN_ENTRY_READONLY = 1, GDN_ENTRY_BLOCK_CAUSAL = 2, GDN_ENTRY_TOKEN = 3 };
@@ -126,6 +130,16 @@ typedef struct gdn_dims {
     int32_t group_frames;         /* gated delta rule: frames per group of the frame-map
                                      kernel (default: chosen from B*H, n_frames, frame_len
                                      and the device's compute units)                     */
+    /* 3D rotary position embedding with GDN_F_ROPE_QK ("SANA-Video ... Block Linear
+     * Diffusion Transformer" talk, segment on temporal modelling; the axial reading of
+     * rope3d_apply): d is cut into parts of rope_d_t, rope_d_h and d - rope_d_t - rope_d_h
+     * dimensions (all even) rotated by the token's frame, latent row and latent column;
+     * in a part of n dimensions the pair (2i, 2i+1) turns by pos * rope_base^(-2i/n).
+     * frame_len = grid_h * rope_grid_w; token t of frame f sits at frame rope_frame_offset
+     * + f, row (t / rope_grid_w), column t mod rope_grid_w; rope_frame_offset + n_frames
+     * <= 2^24.  Ignored without the flag. */
+    int32_t rope_d_t, rope_d_h, rope_grid_w, rope_frame_offset;
+    float rope_base;
 } gdn_dims_t;
 
 /*

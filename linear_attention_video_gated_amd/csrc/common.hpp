@@ -287,6 +287,46 @@ __device__ __forceinline__ float wave_incl_scan2(float x, float& lo_out) {
     return hi;
 }
 
+// Rotary embedding angle in revolutions of position pos (an integer below 2^24, exact in
+// float) at frequency / 2 pi = gh + gl (double split into two floats): the fraction of the
+// rounded product (an exact subtraction) plus the product's exact remainder and the low
+// part.  Contraction is off: fusing the product into the subtraction would count its
+// remainder twice.
+__device__ __forceinline__ float rope_rev(float pos, float gh, float gl) {
+#pragma clang fp contract(off)
+    const float rh = pos * gh;
+    return (rh - __builtin_floorf(rh)) + (__builtin_fmaf(pos, gh, -rh) + pos * gl);
+}
+
+// t / w for 0 <= t < 2^24, w >= 1, from a float reciprocal rinv ~ 1 / w with an exact
+// correction of the quotient (the float estimate is within one of it)
+__device__ __forceinline__ int rope_div(int t, int w, float rinv) {
+    int h = (int)((float)t * rinv);
+    h -= (h * w > t) ? 1 : 0;
+    h += ((h + 1) * w <= t) ? 1 : 0;
+    return h;
+}
+
+// Rotates the pairs of a 16-byte vector of one token row (elements 2j0 .. 2j0 + 2n - 1):
+// pair j turns by pos[axis(j)] * freq_j, axis 0 below pair p1, 1 below p2, else 2; the
+// hardware sine and cosine take revolutions.  bf16 results are rounded to nearest even.
+template <typename E, typename V>
+__device__ __forceinline__ V rope_rotate(V v, int j0, float pos0, float pos1, float pos2, int p1, int p2,
+                                         const float* ghi, const float* glo) {
+    constexpr int NP = (int)(sizeof(V) / sizeof(E)) / 2;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+        const int j = j0 + e;
+        const float ps = j < p1 ? pos0 : (j < p2 ? pos1 : pos2);
+        const float fr = rope_rev(ps, ghi[j], glo[j]);
+        const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+        const float x0 = (float)v[2 * e], x1 = (float)v[2 * e + 1];
+        v[2 * e] = (E)(x0 * cs - x1 * sn);
+        v[2 * e + 1] = (E)(x0 * sn + x1 * cs);
+    }
+    return v;
+}
+
 // Split precision: bf16 operands that must carry ~16 significant bits are sent to the
 // matrix cores as hi + lo pairs (hi = RNE(x), lo = RNE(x - hi)); a product a*b is then
 // a_hi*b_hi + a_lo*b_hi + a_hi*b_lo (the lo*lo term is below fp32 accumulation noise).

@@ -10,6 +10,7 @@
 #include "gdn.h"
 #include "common.hpp"
 #include "gdn_kernels.hpp"
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -50,6 +51,28 @@ int set_state(const float* src, float* dst, long long n, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// Rotary-embedding arguments of a call (GDN_F_ROPE_QK): the pair frequencies of each part
+// computed in double on the host, over 2 pi, split into float hi + lo.
+RopeArgs rope_args(const gdn_dims_t* d) {
+    RopeArgs r;
+    memset(&r, 0, sizeof r);
+    if (!(d->flags & GDN_F_ROPE_QK)) return r;
+    r.on = 1;
+    r.p1 = d->rope_d_t / 2;
+    r.p2 = (d->rope_d_t + d->rope_d_h) / 2;
+    r.grid_w = d->rope_grid_w;
+    r.frame0 = d->rope_frame_offset;
+    const int size[3] = {d->rope_d_t, d->rope_d_h, d->d_k - d->rope_d_t - d->rope_d_h};
+    int j = 0;
+    for (int ax = 0; ax < 3; ++ax)
+        for (int i = 0; 2 * i < size[ax] && j < kRopePairs; ++i, ++j) {
+            const double f = pow((double)d->rope_base, -2.0 * i / size[ax]) / (2.0 * 3.141592653589793);
+            r.ghi[j] = (float)f;
+            r.glo[j] = (float)(f - (double)r.ghi[j]);
+        }
+    return r;
+}
+
 // entry GDN_ENTRY_FORWARD / _READONLY: frame maps, chain, frame-end readout;
 // GDN_ENTRY_TOKEN: group-end maps, chain, per-token readout pass.
 template <typename E, int ND>
@@ -66,6 +89,7 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
     void* agr = ws + p.off_ga;
     float* bgr = (float*)(ws + p.off_gb);
     float* sgrp = (float*)(ws + p.off_c);
+    const RopeArgs rope = rope_args(d);
     for (int wi = 0; wi < p.nwin; ++wi) {
         const int f0 = wi * p.nfw;
         const int nf = (d->n_frames - f0 < p.nfw) ? d->n_frames - f0 : p.nfw;
@@ -80,12 +104,12 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
         const int of32 = (d->flags & GDN_F_OUT_F32) ? 1 : 0;
         const P1Args a1{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, agr, bgr,
                         tok ? 0 : 1, nullptr, nullptr, single ? state_in : nullptr, 0, single ? 1 : 0,
-                        single ? state_out : nullptr, afr, bfr, xexp};
+                        single ? state_out : nullptr, afr, bfr, xexp, rope};
         const P1Args a3t{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, nullptr, nullptr,
                          0, q, out, s_before, of32, 0, single ? state_out : nullptr, nullptr, nullptr, nullptr};
         const P2Args a2{agr, bgr, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
         const P3Args a3{q, out, afr, bfr, xexp, single ? nullptr : sgrp, p.T, d->frame_len, f0, nf, p.G, of32,
-                        single ? 1 : 0};
+                        single ? 1 : 0, 0, rope};
         void* const* ev = (d->phase_events && wi < d->phase_windows) ? d->phase_events + 6 * wi : nullptr;
         if (tok && single) {  // the readout pass alone
             if (record(ev, 0, st) != hipSuccess || record(ev, 1, st) != hipSuccess) return GDN_ERR_HIP;

@@ -26,6 +26,19 @@
 
 namespace gdn {
 
+// 3D rotary position embedding on the load path (GDN_F_ROPE_QK): pair j of a token row
+// (elements 2j, 2j+1) turns by pos * freq_j, pos being the token's frame (pairs below p1),
+// latent row (pairs below p2) or latent column; freq_j / 2 pi is given as float hi + lo
+// (rounded from double) so that late frames keep the angle's full precision.
+constexpr int kRopePairs = 64;  // d <= 128
+struct RopeArgs {
+    int on;
+    int p1, p2;          // first pair of the row part and of the column part
+    int grid_w;          // latent columns: token t of a frame sits at (t / grid_w, t % grid_w)
+    int frame0;          // absolute frame index of the call's first frame
+    float ghi[kRopePairs], glo[kRopePairs];
+};
+
 struct P1Args {
     const void* k;
     const void* v;
@@ -54,6 +67,7 @@ struct P1Args {
     void* Afr;
     void* Bfr;
     int* Xexp;
+    RopeArgs rope;      // k rotated as it is loaded (frame maps pass)
 };
 
 struct P2Args {
@@ -82,6 +96,7 @@ struct P3Args {
     int b_is_state;     // the B maps are the true states (true-start frame maps): no compose
     int parts;          // workgroups per frame, each over a range of its 64-token chunks (set
                         // by the launcher)
+    RopeArgs rope;      // q rotated as it is loaded
 };
 
 struct BC1Args {
@@ -127,6 +142,10 @@ struct BC3Args {
 // 3: per-token readout (P1Args; recorded in the third launch's event slots).
 template <typename E, int ND>
 hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev);
+// the variants with the 3D rotary embedding on load (gdn_frame_rope.hip): phase 0 the frame
+// maps in `mode` (bit 0 normalise, bit 1 additive, bit 2 true start), phase 2 the readout
+template <typename E, int ND>
+hipError_t launch_gdn_rope(int phase, unsigned mode, const void* args, int BH, hipStream_t st);
 template <typename E, int ND>
 hipError_t launch_bc_window(const BC1Args&, const BC2Args&, const BC3Args&, int BH, hipStream_t,
                             void* const* ev);

@@ -78,8 +78,17 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p, int cus) {
     const uint32_t allowed = (entry == GDN_ENTRY_BLOCK_CAUSAL)
                                  ? (uint32_t)(GDN_F_RELU_QK | GDN_F_OUT_F32)
                                  : (uint32_t)(GDN_F_NORMALIZE_K | GDN_F_ADDITIVE | GDN_F_OUT_F32 |
-                                              GDN_F_GATE_LOGITS);
+                                              GDN_F_GATE_LOGITS | GDN_F_ROPE_QK);
     if (d->flags & ~allowed) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & GDN_F_ROPE_QK) {  // rotary embedding on the frame-wise entries' load path
+        if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY) return GDN_ERR_UNSUPPORTED;
+        const int dw = d->d_k - d->rope_d_t - d->rope_d_h;
+        if (d->rope_d_t < 0 || d->rope_d_h < 0 || dw < 0 || d->rope_grid_w < 1 || d->rope_frame_offset < 0 ||
+            !(d->rope_base > 0.f) || d->frame_len % d->rope_grid_w != 0 ||
+            (long long)d->rope_frame_offset + d->n_frames > (1LL << 24))
+            return GDN_ERR_DIMS;
+        if ((d->rope_d_t | d->rope_d_h | dw) & 1) return GDN_ERR_UNSUPPORTED;  // rotations act on pairs
+    }
     p->BH = (long long)d->B * d->H;
     p->T = (long long)d->n_frames * d->frame_len;
     if (p->BH > 65535) return GDN_ERR_DIMS;  // grid y extent

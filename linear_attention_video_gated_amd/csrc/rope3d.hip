@@ -39,10 +39,6 @@ struct RPArgs {
 
 template <typename E>
 __global__ __launch_bounds__(256) void rope3d_apply_kernel(RPArgs a) {
-    // no contraction in this kernel: the angle reduction below needs rh rounded, and
-    // fusing rh's product into the fraction's subtraction would count the product's
-    // remainder twice
-#pragma clang fp contract(off)
     constexpr int EPV = 16 / (int)sizeof(E);
     typedef E V __attribute__((ext_vector_type(EPV)));
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -58,12 +54,9 @@ __global__ __launch_bounds__(256) void rope3d_apply_kernel(RPArgs a) {
     for (int p = 0; p < EPV / 2; ++p) {
         const int j = j0 + 2 * p;
         const int ax = j < a.start[1] ? 0 : (j < a.start[2] ? 1 : 2);
-        // the angle in revolutions, pos * (ghi + glo): the rounded product's fraction (an
-        // exact subtraction) plus the product's exact remainder (fma) and the lo part;
-        // then the hardware sine and cosine of 2 pi times that fraction (v_sin_f32 and
-        // v_cos_f32 take revolutions)
-        const float gh = a.ghi[j >> 1], rh = pos[ax] * gh;
-        const float fr = (rh - __builtin_floorf(rh)) + (__builtin_fmaf(pos[ax], gh, -rh) + pos[ax] * a.glo[j >> 1]);
+        // the angle in revolutions, reduced exactly (rope_rev); then the hardware sine and
+        // cosine of 2 pi times that fraction (v_sin_f32 and v_cos_f32 take revolutions)
+        const float fr = rope_rev(pos[ax], a.ghi[j >> 1], a.glo[j >> 1]);
         const float s = __builtin_amdgcn_sinf(fr), c = __builtin_amdgcn_cosf(fr);
         const float x0 = (float)v[2 * p], x1 = (float)v[2 * p + 1];
         v[2 * p] = (E)(x0 * c - x1 * s);

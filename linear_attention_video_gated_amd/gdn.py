@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdn_mi355x.so")
 
 GDN_BF16, GDN_F32 = 0, 1
-NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS = 1, 2, 4, 8, 16
+NORMALIZE_K, ADDITIVE, RELU_QK, OUT_F32, GATE_LOGITS, ROPE_QK = 1, 2, 4, 8, 16, 32
 ENTRY_FORWARD, ENTRY_READONLY, ENTRY_BLOCK_CAUSAL, ENTRY_TOKEN = 0, 1, 2, 3
 EXPORTS = ("gdn_frame_forward", "gdn_frame_forward_noalloc", "gdn_noalloc_scratch_bytes",
            "gdn_frame_forward_readonly", "gdn_token_forward", "linear_attn_block_causal",
@@ -40,7 +40,9 @@ class Dims(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("phase_events", ctypes.c_void_p),
                 ("phase_windows", ctypes.c_int32), ("window_units", ctypes.c_int32),
-                ("group_frames", ctypes.c_int32)]
+                ("group_frames", ctypes.c_int32), ("rope_d_t", ctypes.c_int32), ("rope_d_h", ctypes.c_int32),
+                ("rope_grid_w", ctypes.c_int32), ("rope_frame_offset", ctypes.c_int32),
+                ("rope_base", ctypes.c_float)]
 
 
 _lib = None
@@ -108,17 +110,26 @@ def _dtype_code(dt):
     raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dt)
 
 
-def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0, events=None, plan=None):
+def make_dims(B, H, n_frames, frame_len, d, dtype_code, flags, workspace=None, nbytes=0, events=None, plan=None,
+              rope=None):
     """events: None or a ctypes array of 6 * n hipEvent_t handles, recorded around the
     three launches of each of the call's first n windows (per-kernel timing).
     plan: None or a dict with "window_units" and/or "group_frames" (the dims' plan
-    overrides, for tests and tuning)."""
+    overrides, for tests and tuning).
+    rope: None or a dict with "d_t", "d_h", "grid_w" and optionally "frame_offset" (0) and
+    "base" (10000): q and k are rotated by the 3D rotary embedding on the kernels' load
+    path (sets GDN_F_ROPE_QK)."""
     plan = plan or {}
+    r = rope or {}
+    if rope is not None:
+        flags |= ROPE_QK
     return Dims(B, H, n_frames, frame_len, d, d, dtype_code, flags,
                 None if workspace is None else workspace.data_ptr(), nbytes,
                 None if events is None else ctypes.cast(events, ctypes.c_void_p).value,
                 0 if events is None else len(events) // 6,
-                int(plan.get("window_units", 0)), int(plan.get("group_frames", 0)))
+                int(plan.get("window_units", 0)), int(plan.get("group_frames", 0)),
+                int(r.get("d_t", 0)), int(r.get("d_h", 0)), int(r.get("grid_w", 0)),
+                int(r.get("frame_offset", 0)), float(r.get("base", 10000.0)))
 
 
 def window_count(B, H, n_frames, frame_len, d, dtype=torch.bfloat16, flags=NORMALIZE_K, entry=ENTRY_FORWARD,
@@ -200,12 +211,12 @@ def _f32(t, shape, name):
 
 def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
                   out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
-                  events=None, plan=None, _entry=ENTRY_FORWARD):
+                  events=None, plan=None, rope=None, _entry=ENTRY_FORWARD):
     """gdn_frame_forward.  Returns (out [B,H,T,d], state_out [B,H,d,d] float32 or None).
     out_dtype=torch.float32 (or a float32 ``out``) returns the unrounded float32 result.
     stream: a torch stream of q's device (default: its current stream); the outputs this
     function allocates and its scratch buffer belong to that stream.  plan: the dims' plan
-    overrides (see make_dims)."""
+    overrides; rope: the 3D rotary embedding applied to q and k on load (see make_dims)."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     alpha = _f32(alpha, (B, H, T), "alpha")
     beta = _f32(beta, (B, H, T), "beta")
@@ -218,10 +229,10 @@ def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, stat
         state_out = _f32(state_out, (B, H, d, d), "state_out")
         code = _dtype_code(q.dtype)
         need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags,
-                                                                plan=plan)), _entry)
+                                                                plan=plan, rope=rope)), _entry)
         ws = _workspace(q.device, need, st)
         dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events,
-                         plan)
+                         plan, rope)
         fn = lib().gdn_token_forward if _entry == ENTRY_TOKEN else lib().gdn_frame_forward
         _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
                   ctypes.byref(dims), _handle(st)))
@@ -229,7 +240,7 @@ def frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, stat
 
 
 def frame_forward_noalloc(q, k, v, alpha, beta, n_frames, frame_len, out, state_in=None, state_out=None,
-                          flags=NORMALIZE_K, stream=None, plan=None):
+                          flags=NORMALIZE_K, stream=None, plan=None, rope=None):
     """gdn_frame_forward_noalloc: gdn_frame_forward with the library's static device
     scratch instead of a workspace.  Allocates nothing: ``out`` (q's shape, q's dtype or
     float32) must be given, state_out is optional.  Returns (out, state_out)."""
@@ -242,7 +253,7 @@ def frame_forward_noalloc(q, k, v, alpha, beta, n_frames, frame_len, out, state_
         raise ValueError("frame_forward_noalloc allocates nothing: pass out")
     out, flags = _out(q, out, None, flags)
     st = _stream_of(q.device, stream)
-    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(q.dtype), flags, plan=plan)
+    dims = make_dims(B, H, n_frames, frame_len, d, _dtype_code(q.dtype), flags, plan=plan, rope=rope)
     with torch.cuda.device(q.device):
         _check(lib().gdn_frame_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
                                                _ptr(state_out), _ptr(out), ctypes.byref(dims), _handle(st)))
@@ -251,16 +262,16 @@ def frame_forward_noalloc(q, k, v, alpha, beta, n_frames, frame_len, out, state_
 
 def token_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, state_out=None,
                   out=None, flags=NORMALIZE_K, return_state=True, stream=None, out_dtype=None,
-                  events=None, plan=None):
+                  events=None, plan=None, rope=None):
     """gdn_token_forward: every token reads the state after itself (o_t = S_t q_t).
     Same arguments and returns as frame_forward."""
     return frame_forward(q, k, v, alpha, beta, n_frames, frame_len, state_in=state_in, state_out=state_out,
                          out=out, flags=flags, return_state=return_state, stream=stream, out_dtype=out_dtype,
-                         events=events, plan=plan, _entry=ENTRY_TOKEN)
+                         events=events, plan=plan, rope=rope, _entry=ENTRY_TOKEN)
 
 
 def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=None, out=None,
-                           flags=NORMALIZE_K, stream=None, out_dtype=None, events=None, plan=None):
+                           flags=NORMALIZE_K, stream=None, out_dtype=None, events=None, plan=None, rope=None):
     """gdn_frame_forward_readonly.  Returns out; state_in is never written."""
     B, H, T, d = _shapes(q, k, v, n_frames, frame_len)
     alpha = _f32(alpha, (B, H, T), "alpha")
@@ -271,10 +282,10 @@ def frame_forward_readonly(q, k, v, alpha, beta, n_frames, frame_len, state_in=N
         out, flags = _out(q, out, out_dtype, flags)
         code = _dtype_code(q.dtype)
         need = lib().gdn_workspace_bytes(ctypes.byref(make_dims(B, H, n_frames, frame_len, d, code, flags,
-                                                                plan=plan)), ENTRY_READONLY)
+                                                                plan=plan, rope=rope)), ENTRY_READONLY)
         ws = _workspace(q.device, need, st)
         dims = make_dims(B, H, n_frames, frame_len, d, code, flags, ws, 0 if ws is None else ws.numel(), events,
-                         plan)
+                         plan, rope)
         _check(lib().gdn_frame_forward_readonly(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                                 _ptr(state_in), _ptr(out), ctypes.byref(dims), _handle(st)))
     return out

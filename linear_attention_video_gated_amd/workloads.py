@@ -43,5 +43,7 @@ WORKLOADS = {
         Workload("tconv_720p_5s", 8, "tconv", 1, 20, 21, 880, 112, "bf16"),
         # 3D RoPE of q on the 22 x 40 latent grid, d = 112 cut (36, 38, 38)
         Workload("rope_720p_5s", 9, "rope", 1, 20, 21, 880, 112, "bf16"),
+        # the 60 s rollout with the 3D RoPE of q and k fused into the kernels' load path
+        Workload("gdn_720p_60s_rope", 10, "gdn_rope", 1, 20, 240, 880, 112, "bf16"),
     ]
 }

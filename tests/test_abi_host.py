@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol_and_nothing_else():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 8
+    assert gdn.lib().gdn_abi_version() == 9
     for code in range(0, -9, -1):
         s = gdn.status_str(code)
         assert s and s != "unknown status"
@@ -45,7 +45,7 @@ def test_abi_version_and_status_strings():
 
 
 def dims(B=1, H=2, F=3, N=16, d=32, dtype=gdn.GDN_BF16, flags=gdn.NORMALIZE_K, ws=None, nbytes=0, wu=0, gf=0):
-    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None, 0, wu, gf)
+    return gdn.Dims(B, H, F, N, d, d, dtype, flags, ws, nbytes, None, 0, wu, gf, 0, 0, 0, 0, 10000.0)
 
 
 def wsb(dm, entry=gdn.ENTRY_FORWARD):
@@ -104,7 +104,7 @@ def test_workspace_zero_for_invalid_or_empty():
 
 @pytest.mark.parametrize("field,val,code", [
     ("dtype", 5, -3), ("B", -1, -2), ("frame_len", 0, -2), ("n_frames", -2, -2),
-    ("d_k", 48, -7), ("flags", 32, -7), ("flags", gdn.RELU_QK, -7),
+    ("d_k", 48, -7), ("flags", 64, -7), ("flags", gdn.RELU_QK, -7),
     ("window_units", -1, -2), ("group_frames", -3, -2),
 ])
 def test_bad_dims_rejected(field, val, code):
@@ -260,3 +260,24 @@ def test_noalloc_entry_rejects_calls_beyond_its_scratch():
     # a smaller window makes the same call fit
     small = dims(B=1, H=20, F=240, N=880, d=112, wu=400)
     assert 0 < wsb(small) <= cap
+
+
+def test_rope_flag_rules():
+    """GDN_F_ROPE_QK: the frame-wise entries only; parts even and within d; the frame
+    length a whole number of latent rows; frames below 2^24."""
+    def rd(dt=4, dh=6, gw=4, off=0, base=100.0, N=16, d=32, F=3):
+        dm = dims(N=N, d=d, F=F, flags=gdn.NORMALIZE_K | gdn.ROPE_QK)
+        dm.rope_d_t, dm.rope_d_h, dm.rope_grid_w, dm.rope_frame_offset, dm.rope_base = dt, dh, gw, off, base
+        return dm
+    L = gdn.lib()
+    assert wsb(rd()) > 0
+    assert wsb(rd(), entry=gdn.ENTRY_READONLY) > 0
+    assert wsb(rd(), entry=gdn.ENTRY_TOKEN) == 0                        # not on the per-token entry
+    assert L.gdn_window_count(ctypes.byref(rd()), gdn.ENTRY_TOKEN) == -7
+    assert L.gdn_window_count(ctypes.byref(rd(dt=3, dh=7)), gdn.ENTRY_FORWARD) == -7   # odd parts
+    assert L.gdn_window_count(ctypes.byref(rd(dt=30, dh=6)), gdn.ENTRY_FORWARD) == -2  # beyond d
+    assert L.gdn_window_count(ctypes.byref(rd(gw=5)), gdn.ENTRY_FORWARD) == -2         # 16 % 5 != 0
+    assert L.gdn_window_count(ctypes.byref(rd(gw=0)), gdn.ENTRY_FORWARD) == -2
+    assert L.gdn_window_count(ctypes.byref(rd(base=0.0)), gdn.ENTRY_FORWARD) == -2
+    assert L.gdn_window_count(ctypes.byref(rd(off=(1 << 24) - 2)), gdn.ENTRY_FORWARD) == -2
+    assert L.gdn_window_count(ctypes.byref(rd(off=(1 << 24) - 3)), gdn.ENTRY_FORWARD) == 1
