@@ -242,7 +242,42 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             }
         }
     };
-    auto dma_chunk = [&](int p, unsigned mask) { dma_tiles(p, 0, 2, true, mask); };
+    // With the rotary embedding the copying waves also rotate the keys they copied, so the
+    // key rows are dealt round-robin over the copying waves on their own (and the value rows
+    // likewise, starting half-way round): every copying wave gets about the same share of
+    // the rotation.  Key row block ii goes to wave number ii mod nw of the mask.
+    auto dma_chunk_rp = [&](int p, unsigned mask) {
+        if (!((mask >> w) & 1u)) return;
+        const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
+        const long long t0 = chunk_t0(p);
+        const int Cc = chunk_len(p);
+        for (int ts = 0; ts < 2; ++ts)
+            for (int ii = (wi + nw - ts * (nw / 2)) % nw; ii < L::KG; ii += nw) {
+                const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
+                const long long el = (t0 + min(row, Cc - 1)) * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
+                const int dst = ts == 0 ? L::OFF_K + (p % L::NBK) * L::KV_B : L::OFF_V + (p % L::NBV) * L::KV_B;
+                if constexpr (L::PIPE) {
+                    dma16((ts == 0 ? kp : vp) + el, smem + dst + ii * 1024);
+                } else {  // same, synchronous
+                    *(u32x4*)(smem + dst + ii * 1024 + 16 * lane) = *(const u32x4*)((ts == 0 ? kp : vp) + el);
+                }
+            }
+        if (!additive && wi == nw - 1) {
+            const long long tt = tok0 + t0 + min(lane, Cc - 1);
+            const int dst = L::OFF_RAW + (p % L::NBR) * L::RAW_B;
+            if constexpr (L::PIPE) {
+                dma4(a.alpha + tt, smem + dst);
+                dma4(a.beta + tt, smem + dst + 256);
+            } else {
+                ((float*)(smem + dst))[lane] = a.alpha[tt];
+                ((float*)(smem + dst + 256))[lane] = a.beta[tt];
+            }
+        }
+    };
+    auto dma_chunk = [&](int p, unsigned mask) {
+        if constexpr (ROPE) dma_chunk_rp(p, mask);
+        else dma_tiles(p, 0, 2, true, mask);
+    };
 
     // At the end of iteration q chunk q+2 must have landed (the prep wave reads it next)
     // while the copies of chunks q+3 .. q+PD may still be in flight: wait until at most
@@ -261,14 +296,19 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // chain wave on each SIMD finishes last and was measured stalling ~1,500 cycles per
     // chunk on its share of the copies)
     constexpr unsigned kCopyT = (TOK && L::PIPE) ? ((0xFu | (1u << ND)) & kAll) : kAll;
-    int ncopy = 0;  // copy instructions this wave issues per chunk
-    for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
-    if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
+    int ncopy = 0;  // copy instructions this wave issues per chunk (with all waves copying)
+    if constexpr (ROPE) {
+        for (int ii = w; ii < L::KG; ii += L::NW) ++ncopy;
+        for (int ii = (w + L::NW - L::NW / 2) % L::NW; ii < L::KG; ii += L::NW) ++ncopy;
+        if (!additive && w == L::NW - 1) ncopy += 2;
+    } else {
+        for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
+        if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
+    }
     // GDN_F_ROPE_QK: keys are rotated by the 3D rotary embedding in LDS, in place.  Each
-    // wave rotates the key granules it copied itself for chunk p (instruction i of the
-    // copy dealing copies 1 KB row block i / 2 of K when i is even), once its own copies of
-    // that chunk have completed and before the barrier that publishes the chunk, so every
-    // reader sees rotated keys and no wave waits for another.  Rows past the chunk's end
+    // wave rotates the key granules it copied itself for chunk p (dma_chunk_rp), once its
+    // own copies of that chunk have completed and before the barrier that publishes the
+    // chunk, so every reader sees rotated keys and no wave waits for another.  Rows past the chunk's end
     // hold copies of a valid row and are rotated harmlessly (their scale factors are 0).
     // (the frequencies are read from LDS, copied there at the kernel's start)
     const float* const sRP = (const float*)(smem + L::OFF_RP);
@@ -279,9 +319,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
         const int fl = p / nch, cq = p - fl * nch;
         const float pf = (float)(a.rope.frame0 + a.f0 + fw0 + fl);
-        for (int i = wi; i < 2 * L::KG; i += nw) {
-            if (i & 1) continue;
-            const int ii = i >> 1;
+        for (int ii = wi; ii < L::KG; ii += nw) {  // this wave's key row blocks (dma_chunk_rp)
             const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
             if (piece >= L::DG) continue;  // padding granule
             const int t = cq * 64 + row, hr = rope_div(t, a.rope.grid_w, rinv_w);
