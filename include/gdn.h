@@ -102,7 +102,8 @@ enum {
                                     b; the gates are alpha = exp(-softplus(a)) (clamped
                                     below at FLT_MIN) and beta = 1 / (1 + e^-b), formed in
                                     float32 inside the kernels                            */
-    GDN_F_ROPE_QK = 1u << 5      /* gdn_frame_forward(_readonly, _noalloc): q and k are
+    GDN_F_ROPE_QK = 1u << 5      /* gdn_frame_forward(_readonly, _noalloc) and
+                                    gdn_token_forward: q and k are
                                     rotated by the 3D rotary position embedding of
                                     rope3d_apply (parameters in dims->rope_*) as the kernels
                                     load them; the tensors in memory are not changed      */
@@ -199,7 +200,7 @@ int gdn_frame_forward_readonly(const void* q, const void* k, const void* v,
  * with one-token frames.  Arguments, layouts, state semantics, flags and errors are those
  * of gdn_frame_forward; n_frames and frame_len only set how T = n_frames * frame_len
  * tokens are cut into chunks and windows (the result does not depend on them beyond
- * rounding).
+ * rounding), and, with GDN_F_ROPE_QK, the tokens' rotary positions.
  */
 int gdn_token_forward(const void* q, const void* k, const void* v,
                       const float* alpha, const float* beta,

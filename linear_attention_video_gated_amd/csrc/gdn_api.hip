@@ -106,7 +106,7 @@ int run_gdn(const void* q, const void* k, const void* v, const float* alpha, con
                         tok ? 0 : 1, nullptr, nullptr, single ? state_in : nullptr, 0, single ? 1 : 0,
                         single ? state_out : nullptr, afr, bfr, xexp, rope};
         const P1Args a3t{k, v, alpha, beta, p.T, d->frame_len, f0, nf, p.G, BH, d->flags, nullptr, nullptr,
-                         0, q, out, s_before, of32, 0, single ? state_out : nullptr, nullptr, nullptr, nullptr};
+                         0, q, out, s_before, of32, 0, single ? state_out : nullptr, nullptr, nullptr, nullptr, rope};
         const P2Args a2{agr, bgr, wi == 0 ? state_in : carry, last ? state_out : carry, sgrp, nf, p.G};
         const P3Args a3{q, out, afr, bfr, xexp, single ? nullptr : sgrp, p.T, d->frame_len, f0, nf, p.G, of32,
                         single ? 1 : 0, 0, rope};

@@ -42,11 +42,14 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
     if (phase == 3) {
         const P1Args& p1 = *(const P1Args*)args;
         const dim3 grid((p1.nf + p1.G - 1) / p1.G, BH);
-        switch (p1.flags & 3u) {
-        case 0: hipLaunchKernelGGL((gdn_token_readout<E, ND, 0>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
-        case 1: hipLaunchKernelGGL((gdn_token_readout<E, ND, 1>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
-        case 2: hipLaunchKernelGGL((gdn_token_readout<E, ND, 2>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
-        default: hipLaunchKernelGGL((gdn_token_readout<E, ND, 3>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+        if (p1.rope.on) {
+            if ((e = launch_gdn_rope<E, ND>(3, p1.flags & 3u, args, BH, st)) != hipSuccess) return e;
+        } else {
+            switch (p1.flags & 3u) {
+#define GDN_TOK(M) case M: hipLaunchKernelGGL((gdn_token_readout<E, ND, M>), grid, dim3(LT::NT), LT::LDS_B, st, p1); break;
+                GDN_TOK(0) GDN_TOK(1) GDN_TOK(2) GDN_TOK(3)
+#undef GDN_TOK
+            }
         }
     } else if (phase == 0) {
         const P1Args& p1 = *(const P1Args*)args;

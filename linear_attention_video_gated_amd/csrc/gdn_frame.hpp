@@ -155,7 +155,7 @@ __host__ __device__ constexpr int frTm(int I) { return 6 + I; }
 // per-tile choices they make are not branches and calls without rotation carry none of it.
 template <typename E, int ND, int MODE, bool TOK>
 __device__ __forceinline__ void affine_body(P1Args a) {
-    constexpr bool ROPE = !TOK && (MODE & 8) != 0;
+    constexpr bool ROPE = (MODE & 8) != 0;
     using L = P1<E, ND, TOK, ROPE>;
     using O = Ops<E>;
     using F8 = typename O::F8;
@@ -275,7 +275,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         }
     };
     auto dma_chunk = [&](int p, unsigned mask) {
-        if constexpr (ROPE) dma_chunk_rp(p, mask);
+        if constexpr (ROPE && !TOK) dma_chunk_rp(p, mask);
         else dma_tiles(p, 0, 2, true, mask);
     };
 
@@ -297,7 +297,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // chunk on its share of the copies)
     constexpr unsigned kCopyT = (TOK && L::PIPE) ? ((0xFu | (1u << ND)) & kAll) : kAll;
     int ncopy = 0;  // copy instructions this wave issues per chunk (with all waves copying)
-    if constexpr (ROPE) {
+    if constexpr (ROPE && !TOK) {
         for (int ii = w; ii < L::KG; ii += L::NW) ++ncopy;
         for (int ii = (w + L::NW - L::NW / 2) % L::NW; ii < L::KG; ii += L::NW) ++ncopy;
         if (!additive && w == L::NW - 1) ncopy += 2;
@@ -305,27 +305,40 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         for (int i = w; i < 2 * L::KG; i += L::NW) ++ncopy;
         if (!additive && w == (2 * L::KG) % L::NW) ncopy += 2;
     }
-    // GDN_F_ROPE_QK: keys are rotated by the 3D rotary embedding in LDS, in place.  Each
-    // wave rotates the key granules it copied itself for chunk p (dma_chunk_rp), once its
-    // own copies of that chunk have completed and before the barrier that publishes the
-    // chunk, so every reader sees rotated keys and no wave waits for another.  Rows past the chunk's end
+    // GDN_F_ROPE_QK: keys (and, in the per-token pass, queries) are rotated by the 3D rotary
+    // embedding in LDS, in place.  Each wave rotates the granules it copied itself for
+    // chunk p (dma_chunk_rp; dma_tiles in the per-token pass), once its own copies of that
+    // chunk have completed and before the barrier that publishes the chunk, so every
+    // reader sees rotated values and no wave waits for another.  Rows past the chunk's end
     // hold copies of a valid row and are rotated harmlessly (their scale factors are 0).
     // (the frequencies are read from LDS, copied there at the kernel's start)
     const float* const sRP = (const float*)(smem + L::OFF_RP);
     const float rinv_w = ROPE ? 1.f / (float)a.rope.grid_w : 0.f;
-    auto rotate_own = [&](int p, unsigned mask) {
-        if constexpr (!ROPE) return;
-        if (!((mask >> w) & 1u)) return;
-        const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
+    // rotates the granule that copy lane `lane` of row block ii of chunk p's tile `buf` holds
+    auto rotate_granule = [&](E* buf, int p, int ii) {
         const int fl = p / nch, cq = p - fl * nch;
         const float pf = (float)(a.rope.frame0 + a.f0 + fw0 + fl);
-        for (int ii = wi; ii < L::KG; ii += nw) {  // this wave's key row blocks (dma_chunk_rp)
-            const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
-            if (piece >= L::DG) continue;  // padding granule
-            const int t = cq * 64 + row, hr = rope_div(t, a.rope.grid_w, rinv_w);
-            V16* g16 = (V16*)((unsigned char*)KB_(p) + row * L::KPB + piece * 16);
-            *g16 = rope_rotate<E>(*g16, piece * (L::G::EPV / 2), pf, (float)hr, (float)(t - hr * a.rope.grid_w),
-                                  a.rope.p1, a.rope.p2, sRP, sRP + kRopePairs);
+        const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
+        if (piece >= L::DG) return;  // padding granule
+        const int t = cq * 64 + row, hr = rope_div(t, a.rope.grid_w, rinv_w);
+        V16* g16 = (V16*)((unsigned char*)buf + row * L::KPB + piece * 16);
+        *g16 = rope_rotate<E>(*g16, piece * (L::G::EPV / 2), pf, (float)hr, (float)(t - hr * a.rope.grid_w),
+                              a.rope.p1, a.rope.p2, sRP, sRP + kRopePairs);
+    };
+    auto rotate_own = [&](int p, unsigned mask) {
+        if constexpr (!ROPE || TOK) return;
+        if (!((mask >> w) & 1u)) return;
+        const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
+        for (int ii = wi; ii < L::KG; ii += nw) rotate_granule(KB_(p), p, ii);  // this wave's key row blocks (dma_chunk_rp)
+    };
+    // the per-token pass: the K and Q row blocks this wave copied with dma_tiles(p, tf, nt, ., mask)
+    auto rotate_tiles = [&](int p, int tf, int nt, unsigned mask) {
+        if constexpr (!ROPE || !TOK) return;
+        if (!((mask >> w) & 1u)) return;
+        const int wi = __builtin_popcount(mask & ((1u << w) - 1u)), nw = __builtin_popcount(mask);
+        for (int i = wi; i < nt * L::KG; i += nw) {
+            const int ts = tf + i % nt;
+            if (ts != 1) rotate_granule(ts == 0 ? KB_(p) : QB_(p), p, i / nt);  // V is not rotated
         }
     };
     auto wait_dma_behind = [&](int q) {
@@ -928,7 +941,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         }
     };
 
-    // rotary frequencies to LDS, read there by rotate_own
+    // rotary frequencies to LDS, read there by rotate_granule
     if constexpr (ROPE) {
         if (tid < 2 * kRopePairs)
             ((float*)(smem + L::OFF_RP))[tid] = tid < kRopePairs ? a.rope.ghi[tid] : a.rope.glo[tid - kRopePairs];
@@ -959,6 +972,9 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             dma_tiles(0, 1, 2, false, kAll);
             if (nq > 1) dma_tiles(1, 0, 1, true, kAll);
             wait_vmem();
+            rotate_tiles(0, 0, 1, kAll);
+            rotate_tiles(0, 1, 2, kAll);
+            if (nq > 1) rotate_tiles(1, 0, 1, kAll);
             lds_barrier();  // chunk 0 and chunk 1's K in LDS
             prep1(0, gr, R);
             prep2(0, gr, R);
@@ -977,6 +993,8 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     prep3(q + 1);
                 }
                 wait_vmem();
+                if (q + 2 < nq) rotate_tiles(q + 2, 0, 1, kCopyT);
+                if (q + 1 < nq) rotate_tiles(q + 1, 1, 2, kCopyT);
                 lds_barrier();  // B3: chunk q+1 prepared and in LDS, chunk q+2's K in LDS
             }
         } else if constexpr (TOK) {
@@ -984,6 +1002,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             for (int q = 0; q < nq; ++q) {
                 dma_tiles(q, 0, 3, true, kAll);
                 wait_vmem();
+                rotate_tiles(q, 0, 3, kAll);
                 lds_barrier();
                 prep1(q, gr, R);
                 lds_barrier();
@@ -1091,6 +1110,9 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 dma_tiles(0, 1, 2, false, kAll);
                 if (nq > 1) dma_tiles(1, 0, 1, true, kAll);
                 wait_vmem();
+                rotate_tiles(0, 0, 1, kAll);
+                rotate_tiles(0, 1, 2, kAll);
+                if (nq > 1) rotate_tiles(1, 0, 1, kAll);
                 lds_barrier();
                 lds_barrier();
                 for (int q = 0; q < nq; ++q) {
@@ -1101,12 +1123,15 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     lds_barrier();  // B2
                     chain_tok(q, XB, Ur);
                     wait_vmem();
+                    if (q + 2 < nq) rotate_tiles(q + 2, 0, 1, kCopyT);
+                    if (q + 1 < nq) rotate_tiles(q + 1, 1, 2, kCopyT);
                     lds_barrier();  // B3
                 }
             } else {
                 for (int q = 0; q < nq; ++q) {
                     dma_tiles(q, 0, 3, true, kAll);
                     wait_vmem();
+                    rotate_tiles(q, 0, 3, kAll);
                     lds_barrier();
                     lds_barrier();
                     lds_barrier();
@@ -1197,7 +1222,7 @@ __global__ __launch_bounds__((P1<E, ND, false, (MODE & 8) != 0>::NT), 1) void gd
 // (the state before the group, from the chain), B part only, writing o_t = S_t q_t for
 // every token (TOK branches of the body above).
 template <typename E, int ND, int MODE>
-__global__ __launch_bounds__((P1<E, ND, true>::NT), 1) void gdn_token_readout(P1Args a) {
+__global__ __launch_bounds__((P1<E, ND, true, (MODE & 8) != 0>::NT), 1) void gdn_token_readout(P1Args a) {
     affine_body<E, ND, MODE, true>(a);
 }
 

@@ -80,8 +80,9 @@ int check_dims(const gdn_dims_t* d, int entry, Plan* p, int cus) {
                                  : (uint32_t)(GDN_F_NORMALIZE_K | GDN_F_ADDITIVE | GDN_F_OUT_F32 |
                                               GDN_F_GATE_LOGITS | GDN_F_ROPE_QK);
     if (d->flags & ~allowed) return GDN_ERR_UNSUPPORTED;
-    if (d->flags & GDN_F_ROPE_QK) {  // rotary embedding on the frame-wise entries' load path
-        if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & GDN_F_ROPE_QK) {  // rotary embedding on the gated-delta-rule entries' load path
+        if (entry != GDN_ENTRY_FORWARD && entry != GDN_ENTRY_READONLY && entry != GDN_ENTRY_TOKEN)
+            return GDN_ERR_UNSUPPORTED;
         const int dw = d->d_k - d->rope_d_t - d->rope_d_h;
         if (d->rope_d_t < 0 || d->rope_d_h < 0 || dw < 0 || d->rope_grid_w < 1 || d->rope_frame_offset < 0 ||
             !(d->rope_base > 0.f) || d->frame_len % d->rope_grid_w != 0 ||

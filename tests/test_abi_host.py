@@ -263,7 +263,7 @@ def test_noalloc_entry_rejects_calls_beyond_its_scratch():
 
 
 def test_rope_flag_rules():
-    """GDN_F_ROPE_QK: the frame-wise entries only; parts even and within d; the frame
+    """GDN_F_ROPE_QK: the gated-delta-rule entries only; parts even and within d; the frame
     length a whole number of latent rows; frames below 2^24."""
     def rd(dt=4, dh=6, gw=4, off=0, base=100.0, N=16, d=32, F=3):
         dm = dims(N=N, d=d, F=F, flags=gdn.NORMALIZE_K | gdn.ROPE_QK)
@@ -272,8 +272,12 @@ def test_rope_flag_rules():
     L = gdn.lib()
     assert wsb(rd()) > 0
     assert wsb(rd(), entry=gdn.ENTRY_READONLY) > 0
-    assert wsb(rd(), entry=gdn.ENTRY_TOKEN) == 0                        # not on the per-token entry
-    assert L.gdn_window_count(ctypes.byref(rd()), gdn.ENTRY_TOKEN) == -7
+    assert wsb(rd(), entry=gdn.ENTRY_TOKEN) > 0                         # the per-token entry too
+    bc = rd()
+    bc.flags = 0
+    assert L.gdn_window_count(ctypes.byref(bc), gdn.ENTRY_BLOCK_CAUSAL) == 1
+    bc.flags = gdn.ROPE_QK                                              # not the block-causal entry
+    assert L.gdn_window_count(ctypes.byref(bc), gdn.ENTRY_BLOCK_CAUSAL) == -7
     assert L.gdn_window_count(ctypes.byref(rd(dt=3, dh=7)), gdn.ENTRY_FORWARD) == -7   # odd parts
     assert L.gdn_window_count(ctypes.byref(rd(dt=30, dh=6)), gdn.ENTRY_FORWARD) == -2  # beyond d
     assert L.gdn_window_count(ctypes.byref(rd(gw=5)), gdn.ENTRY_FORWARD) == -2         # 16 % 5 != 0

@@ -1,7 +1,8 @@
-"""GPU parity of the 3D rotary embedding fused into the frame-wise gated-delta-rule path
+"""GPU parity of the 3D rotary embedding fused into the gated-delta-rule path
 (GDN_F_ROPE_QK, through the C ABI): the kernels rotate k as the frame-map pass loads it
-and q as the readout loads it; the oracle rotates q and k first (oracle.rope3d, float64)
-and then runs the plain recurrence (oracle.gdn_forward).  With bf16 inputs the rotated q
+and q as the readout loads it (the per-token entry's readout pass rotates both as it
+loads them); the oracle rotates q and k first (oracle.rope3d, float64) and then runs the
+plain recurrence (oracle.gdn_forward; one-token frames for the per-token readout).  With bf16 inputs the rotated q
 and k are bf16 operands, as the stand-alone bf16 rotation pass writes them: the oracle's
 rotated tensors are rounded to bf16 (nearest even) before the recurrence -- the rounding
 of q alone moves the heavy-tailed outputs (max ~15 RMS) by up to ~3e-2 RMS, so comparing
@@ -48,7 +49,10 @@ def run(B, H, F, gh, gw, d, dt, dh, dtype, seed, entry="frame", off=0, base=1000
     rope = {"d_t": dt, "d_h": dh, "grid_w": gw, "frame_offset": off, "base": base}
     additive = bool(flags & gdn.ADDITIVE)
     a_, b_ = (None, None) if additive else (dv["alpha"], dv["beta"])
-    if entry == "readonly":
+    if entry == "token":
+        out, st = gdn.token_forward(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"], flags=flags,
+                                    out_dtype=torch.float32, rope=rope, plan=plan)
+    elif entry == "readonly":
         out = gdn.frame_forward_readonly(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"],
                                          flags=flags, out_dtype=torch.float32, rope=rope, plan=plan)
         st = None
@@ -63,14 +67,15 @@ def run(B, H, F, gh, gw, d, dt, dh, dtype, seed, entry="frame", off=0, base=1000
         qr = torch.from_numpy(qr).to(torch.bfloat16)
         kr = torch.from_numpy(kr).to(torch.bfloat16)
     oflags = (oracle.NORMALIZE_K if flags & gdn.NORMALIZE_K else 0) | (oracle.ADDITIVE if additive else 0)
-    ro, rs = oracle.gdn_forward(qr, kr, inp["v"], inp["alpha"], inp["beta"], F, N, state_in=inp["state_in"],
+    fo, no = (F * N, 1) if entry == "token" else (F, N)
+    ro, rs = oracle.gdn_forward(qr, kr, inp["v"], inp["alpha"], inp["beta"], fo, no, state_in=inp["state_in"],
                                 flags=oflags)
     r1 = check("out", out, ro, TOL[dtype])
     r2 = check("state", st, rs, TOL[dtype]) if st is not None else 0.0
     say("  out err/rms=%.2e state err/rms=%.2e" % (r1, r2))
 
 
-@pytest.mark.parametrize("entry", ["frame", "readonly"])
+@pytest.mark.parametrize("entry", ["frame", "readonly", "token"])
 @pytest.mark.parametrize("dtype,d,dt,dh", [(torch.bfloat16, 112, 36, 38), (torch.float32, 64, 20, 22),
                                            (torch.float32, 112, 36, 38), (torch.bfloat16, 128, 40, 44),
                                            (torch.bfloat16, 32, 8, 12)])
@@ -81,15 +86,17 @@ def test_rope_fused_ragged(entry, dtype, d, dt, dh, plan):
     run(1, 2, 3, 10, 15, d, dt, dh, dtype, seed=1000 + d, entry=entry, plan=plan)
 
 
-def test_rope_fused_720p_grid():
+@pytest.mark.parametrize("entry", ["frame", "token"])
+def test_rope_fused_720p_grid(entry):
     """The 22 x 40 latent grid of a 720p frame, d = 112 cut (36, 38, 38), several heads."""
-    run(1, 4, 3, 22, 40, 112, 36, 38, torch.bfloat16, seed=1010, gates="config", state=None)
+    run(1, 4, 3, 22, 40, 112, 36, 38, torch.bfloat16, seed=1010, gates="config", state=None, entry=entry)
 
 
+@pytest.mark.parametrize("entry", ["frame", "token"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_rope_fused_late_frames(dtype):
+def test_rope_fused_late_frames(dtype, entry):
     """Absolute frame positions just below 2^24 (exact float positions), base 100."""
-    run(2, 2, 3, 4, 8, 64, 16, 24, dtype, seed=1020, off=(1 << 24) - 3, base=100.0)
+    run(2, 2, 3, 4, 8, 64, 16, 24, dtype, seed=1020, off=(1 << 24) - 3, base=100.0, entry=entry)
 
 
 def test_rope_fused_parts_and_additive():
@@ -98,9 +105,7 @@ def test_rope_fused_parts_and_additive():
     run(1, 2, 4, 5, 20, 112, 40, 0, torch.bfloat16, seed=1031, flags=gdn.ADDITIVE | gdn.NORMALIZE_K)
 
 
-def test_rope_fused_token_entry_rejected():
-    inp = gdn_inputs(1, 1, 1, 16, 32, workload_id=1040)
-    dv = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
-    with pytest.raises(gdn.GdnError):
-        gdn.token_forward(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], 1, 16,
-                          rope={"d_t": 8, "d_h": 12, "grid_w": 4})
+def test_rope_fused_token_parts_and_additive():
+    """The per-token entry with no spatial-row part and with the additive update."""
+    run(1, 2, 4, 5, 20, 112, 40, 0, torch.bfloat16, seed=1032, entry="token")
+    run(1, 2, 4, 5, 20, 64, 0, 32, torch.float32, seed=1033, entry="token", flags=gdn.ADDITIVE | gdn.NORMALIZE_K)
