@@ -43,6 +43,7 @@
 #include "common.hpp"
 #include "gdn_kernels.hpp"
 #include <float.h>
+#include <type_traits>
 
 namespace gdn {
 
@@ -117,7 +118,11 @@ template <typename E, int ND, bool TOK = false, bool RP = false> struct P1 {
     static constexpr bool OV = !TOK && BF && ov_bytes() <= 160 * 1024;
     static constexpr bool PIPE = BF && (!TOK || tok_bytes() <= 160 * 1024);
     static constexpr int NPW = OV ? 2 : 1;        // prep waves
-    static constexpr int NW = ND + NPW;           // chain waves + prep waves
+    // helper waves (OV at d = 112): they form the chunk's W column tiles, which the chain
+    // waves would otherwise substitute beside their U tiles.  Twelve waves are three per
+    // SIMD, the same register budget as nine.
+    static constexpr int NH = (OV && ND == 7) ? 3 : 0;
+    static constexpr int NW = ND + NPW + NH;      // chain waves + prep waves + helper waves
     static constexpr int NT = 64 * NW;
     static constexpr int NB = PIPE ? 2 : 1;       // fragment sets
     static constexpr int NBK = OV ? 4 : (!PIPE ? 1 : 3);                 // K chunk buffers
@@ -181,7 +186,8 @@ __device__ __forceinline__ void affine_body(P1Args a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const bool prep = (w >= ND);
+    const bool prep = (w >= ND) && (w < ND + L::NPW);
+    const bool helper = w >= ND + L::NPW;  // (L::NH > 0 only)
     const int gi = blockIdx.x, bh = blockIdx.y;
     const int N = a.frame_len;
     const int fw0 = gi * a.G;                              // first frame (in window) of the group
@@ -585,7 +591,11 @@ __device__ __forceinline__ void affine_body(P1Args a) {
     // correction's operand Z_I is rounded to bf16.  R = diag(b e^G n) K  or  diag(b) V.
     // W goes to LDS pre-scaled by -kts and U stays in registers scaled by kts, so that the
     // state update's innovation is U~ + W~ X^T straight off the matrix cores.
-    auto subst = [&](int q, f32x4 (&Ur)[4]) {
+    // column tile cw of W (to LDS, transposed) and/or of U (to Ur, this wave's own)
+    // PART: 0 both, 1 U only, 2 W only
+    auto subst_part = [&](int q, f32x4 (&Ur)[4], int cw, auto PART) {
+        constexpr int P = decltype(PART)::value;
+        constexpr bool DW = P != 1, DU = P != 2;
         const float* sc = SC(q);
         const E* fr = FR(q);
         const E* kb = KB_(q);
@@ -594,31 +604,39 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         F4 pw[4], pu[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            // lane (c, g): tokens 16I + 4g + i, column 16w + c
-            const f32x4 kcol = __builtin_convertvector(O::ldtr(kb, L::KPB, 16 * I, 16 * w, lane), f32x4);
-            const f32x4 vcol = __builtin_convertvector(O::ldtr(vb, L::KPB, 16 * I, 16 * w, lane), f32x4);
-            const f32x4 ws = *(const f32x4*)(sc + 16 * I + 4 * g);
-            const f32x4 bs = *(const f32x4*)(sc + 64 + 16 * I + 4 * g);
-            f32x4 zw = ws * kcol, zu = bs * vcol;
+            // lane (c, g): tokens 16I + 4g + i, column 16cw + c
+            f32x4 zw, zu;
+            if constexpr (DW) {
+                const f32x4 kcol = __builtin_convertvector(O::ldtr(kb, L::KPB, 16 * I, 16 * cw, lane), f32x4);
+                zw = *(const f32x4*)(sc + 16 * I + 4 * g) * kcol;
+            }
+            if constexpr (DU) {
+                const f32x4 vcol = __builtin_convertvector(O::ldtr(vb, L::KPB, 16 * I, 16 * cw, lane), f32x4);
+                zu = *(const f32x4*)(sc + 64 + 16 * I + 4 * g) * vcol;
+            }
             if (I > 0) {
                 f32x4 aw = zero4(), au = zero4();
 #pragma unroll
                 for (int J = 0; J < I; ++J) {
                     const F4 lf = *(const F4*)(fr + (frL(I, J) * 64 + lane) * 4);
-                    aw = O::mma16(lf, pw[J], aw);
-                    au = O::mma16(lf, pu[J], au);
+                    if constexpr (DW) aw = O::mma16(lf, pw[J], aw);
+                    if constexpr (DU) au = O::mma16(lf, pu[J], au);
                 }
-                zw -= aw;
-                zu -= au;
+                if constexpr (DW) zw -= aw;
+                if constexpr (DU) zu -= au;
             }
             const F4 tmf = *(const F4*)(fr + (frTm(I) * 64 + lane) * 4);
-            XW[I] = O::mma16(tmf, O::pack4(zw), zw);
-            Ur[I] = O::mma16(tmf, O::pack4(zu), zu);
-            pw[I] = O::pack4(XW[I]);
-            pu[I] = O::pack4(Ur[I]);
+            if constexpr (DW) {
+                XW[I] = O::mma16(tmf, O::pack4(zw), zw);
+                pw[I] = O::pack4(XW[I]);
+            }
+            if constexpr (DU) {
+                Ur[I] = O::mma16(tmf, O::pack4(zu), zu);
+                pu[I] = O::pack4(Ur[I]);
+            }
         }
-        // W^T row 16w + c, tokens 16I + 4g .. +3: one 8-byte piece per lane and block
-        E* const wt = (E*)((char*)WB_(q) + (16 * w + c) * L::WPB) + 4 * g;
+        // W^T row 16cw + c, tokens 16I + 4g .. +3: one 8-byte piece per lane and block
+        E* const wt = (E*)((char*)WB_(q) + (16 * cw + c) * L::WPB) + 4 * g;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 wv;
@@ -628,12 +646,24 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 const f32x4 s = *(const f32x4*)(sc + 128 + 16 * I + 4 * g);
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    wv[ii] = -s[ii] * XW[I][ii];
-                    Ur[I][ii] *= s[ii];
+                    if constexpr (DW) wv[ii] = -s[ii] * XW[I][ii];
+                    if constexpr (DU) Ur[I][ii] *= s[ii];
                 }
             }
-            O::st4(wt + 16 * I, wv);
+            if constexpr (DW) O::st4(wt + 16 * I, wv);
         }
+    };
+    // the chain waves' substitution: both tiles of column w, or only U's where helper
+    // waves form W
+    auto subst = [&](int q, f32x4 (&Ur)[4]) {
+        if constexpr (L::NH > 0) subst_part(q, Ur, w, std::integral_constant<int, 1>{});
+        else subst_part(q, Ur, w, std::integral_constant<int, 0>{});
+    };
+    // helper wave h: W column tiles h, h + NH, ...
+    auto subst_helper = [&](int q) {
+        f32x4 unused[4];
+        for (int cw = w - ND - L::NPW; cw < ND; cw += (L::NH > 0 ? L::NH : ND))
+            subst_part(q, unused, cw, std::integral_constant<int, 2>{});
     };
 
     // Operand fragment of the row-major chunk tile `buf` (K or Q, pitch KPB): lane (c, g)
@@ -1084,6 +1114,27 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                 prep3(q);
                 lds_barrier();
                 lds_barrier();
+                lds_barrier();
+            }
+        }
+    } else if (helper) {
+        // helper waves (OV): the W column tiles of chunk q+1 beside the chain waves' state
+        // update of chunk q, with the chain waves' barriers
+        if constexpr (L::NH > 0) {
+            dma_chunk(0, kAll);
+            if (nq > 1) dma_chunk(1, kAll);
+            wait_vmem();
+            rotate_own(0, kAll);
+            if (nq > 1) rotate_own(1, kAll);
+            if (nq > 2) dma_chunk(2, kAll);
+            lds_barrier();
+            lds_barrier();
+            subst_helper(0);
+            wait_vmem();
+            if (nq > 2) rotate_own(2, kAll);
+            lds_barrier();
+            for (int q = 0; q < nq; ++q) {
+                if (q + 1 < nq) subst_helper(q + 1);
                 lds_barrier();
             }
         }
