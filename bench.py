@@ -478,7 +478,7 @@ def main():
         achieved = flops / (kms_launch * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[wl.dtype]
         roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic, "mfma_busy_frac": mfma_busy, "mfma_busy_frac": mfma_busy,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic, "mfma_busy_frac": mfma_busy,
                     "kernel_ms": round(kms_launch, 4), "launches_per_call": nwin, "algorithmic_flops": flops}
     elif wl.kind in ("tconv", "rope"):
         # tconv: x read, y written, carry read and written; rope: x read and written
