@@ -27,7 +27,7 @@ int device_cus() {
     static int cus[PerDeviceOnce::kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PerDeviceOnce::kMaxDevices) return 256;
-    once.run([&] {
+    (void)once.run([&] {
         int n = 0;
         const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
         cus[dev] = (e == hipSuccess && n > 0) ? n : 256;

@@ -82,6 +82,27 @@ def test_gdn_ragged_multi_chunk(d, dtype):
     run_gdn_case(1, 2, 3, 150, d, dtype, seed=100 + d)
 
 
+@pytest.mark.parametrize("d", [112, 32, 16, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gdn_one_frame(d, dtype):
+    """One-frame calls (the frame maps pass starts from the known state and writes the
+    frame-end state as its map; no chain): a ragged frame (three chunks and a tail), every
+    head dimension, bf16 output checked as the RNE of the fp32 one."""
+    run_gdn_case(2, 3, 1, 200, d, dtype, seed=150 + d, state_std=0.2, gates="near_one")
+
+
+@pytest.mark.parametrize("N", [1, 16, 63, 64, 65, 880])
+def test_gdn_one_frame_lengths(N):
+    """One-frame calls of every length class: shorter than one token tile, one chunk, a
+    chunk plus one token, and the 720p frame (14 chunks)."""
+    run_gdn_case(2, 2, 1, N, 112, torch.bfloat16, seed=170 + N, state_std=0.1)
+
+
+def test_gdn_one_frame_additive():
+    run_gdn_case(1, 2, 1, 130, 64, torch.float32, seed=190, state_std=0.2,
+                 flags=gdn.ADDITIVE | gdn.NORMALIZE_K)
+
+
 @pytest.mark.parametrize("N", [1, 16, 48, 64, 65, 127, 390, 880])
 def test_gdn_frame_lengths_d112(N):
     F = 3 if N >= 390 else 5

@@ -86,6 +86,14 @@ def test_rope_fused_ragged(entry, dtype, d, dt, dh, plan):
     run(1, 2, 3, 10, 15, d, dt, dh, dtype, seed=1000 + d, entry=entry, plan=plan)
 
 
+@pytest.mark.parametrize("entry", ["frame", "readonly"])
+@pytest.mark.parametrize("dtype,d,dt,dh", [(torch.bfloat16, 112, 36, 38), (torch.float32, 64, 20, 22),
+                                           (torch.bfloat16, 128, 40, 44)])
+def test_rope_fused_one_frame(entry, dtype, d, dt, dh):
+    """One-frame calls (true-start frame maps, readout from the frame-end state)."""
+    run(2, 2, 1, 10, 15, d, dt, dh, dtype, seed=1005 + d, entry=entry)
+
+
 @pytest.mark.parametrize("entry", ["frame", "token"])
 def test_rope_fused_720p_grid(entry):
     """The 22 x 40 latent grid of a 720p frame, d = 112 cut (36, 38, 38), several heads."""
