@@ -84,7 +84,10 @@ template <typename E, int ND, bool TOK = false, bool RP = false> struct P1 {
     // W staged transposed (row = a d_k column of W, 64 tokens per row)
     static constexpr int WRB = 64 * (int)sizeof(E);
     static constexpr int WPB = pitch(WRB);
-    static constexpr int LD_P = 20;               // diagonal L blocks pitch (floats)
+    static constexpr int LD_P = 20;               // diagonal L blocks: row pitch (floats)
+    // block stride: 16 rows plus 4 floats, so that the inverse's broadcast reads of the
+    // four blocks (one address per block, 16 lanes each) fall in different banks
+    static constexpr int LD_BS = 16 * LD_P + 4;
     static constexpr int NFR = 10;                // fragments: 6 L_IJ, 4 (T_II - I)
     static constexpr int FR_E = NFR * 64 * 4;     // elements per fragment set
     static constexpr int KV_B = al(64 * KPB);
@@ -98,7 +101,7 @@ template <typename E, int ND, bool TOK = false, bool RP = false> struct P1 {
     static constexpr int W_B = al(G::D * WPB);
     // TOK: the 10 lower-triangle 16x16 tiles of the decay-masked (K Q^T), hi (+ lo) fragments
     static constexpr int AQ_B = TOK ? al(10 * SplitCount<E>::N * 64 * 4 * (int)sizeof(E)) : 0;
-    static constexpr int LD_B = al(4 * 16 * LD_P * 4);
+    static constexpr int LD_B = al(4 * LD_BS * 4);
     // prep wave's per-token scalars: [0,64) G, [64,128) n, [128,192) b n, [192,256) the
     // within-block decay, [256,448) the cross-block decays; fp32 inputs add [448,512) the
     // low part of G
@@ -537,7 +540,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             if (I != J) {
                 if (has_off(R)) *(F4*)(fr + (frL(I, J) * 64 + lane) * 4) = O::pack4(gr[q]);
             } else {
-                if (has_diag(R)) *(f32x4*)(sLD + (16 * I + c) * L::LD_P + 4 * g) = gr[q];
+                if (has_diag(R)) *(f32x4*)(sLD + I * L::LD_BS + c * L::LD_P + 4 * g) = gr[q];
             }
         }
     };
@@ -550,7 +553,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
         // T[r][j] = [r == j] - sum_{k > j} T[r][k] L[k][j].  Each solved entry updates all
         // earlier columns (independent FMAs) with row k of the block.
         const int bb = lane >> 4, r = lane & 15;
-        const float* lb = sLD + (16 * bb) * L::LD_P;
+        const float* lb = sLD + bb * L::LD_BS;
         // rows 15..PRE are read up front, the others when the solve gets there (registers)
         constexpr int PRE = L::OV ? 8 : 16;
         f32x4 lr[16][4];
