@@ -121,10 +121,11 @@ template <typename E, int ND, bool TOK = false, bool RP = false> struct P1 {
     static constexpr bool OV = !TOK && BF && ov_bytes() <= 160 * 1024;
     static constexpr bool PIPE = BF && (!TOK || tok_bytes() <= 160 * 1024);
     static constexpr int NPW = OV ? 2 : 1;        // prep waves
-    // helper waves (OV at d = 112): they form the chunk's W column tiles, which the chain
-    // waves would otherwise substitute beside their U tiles.  Twelve waves are three per
-    // SIMD, the same register budget as nine.
-    static constexpr int NH = (OV && ND == 7) ? 3 : 0;
+    // helper waves at d = 112 (OV, and the per-token pass's two-barrier schedule): they form
+    // the chunk's W column tiles, which the chain waves would otherwise substitute beside
+    // their U tiles (and, in the per-token pass, the intra-chunk weight tiles past the
+    // chain waves' one each).  Twelve waves are three per SIMD: at most 168 registers.
+    static constexpr int NH = ((OV || (TOK && PIPE)) && ND == 7) ? 3 : 0;
     static constexpr int NW = ND + NPW + NH;      // chain waves + prep waves + helper waves
     static constexpr int NT = 64 * NW;
     static constexpr int NB = PIPE ? 2 : 1;       // fragment sets
@@ -1019,7 +1020,7 @@ __device__ __forceinline__ void affine_body(P1Args a) {
                     dma_tiles(q + 1, 1, 2, false, kCopyT);
                     prep1(q + 1, gr, R);
                 }
-                aqk(q, ND, 1);  // the tiles past the chain waves' one each
+                if constexpr (L::NH == 0) aqk(q, ND, 1);  // the tiles past the chain waves' one each
                 lds_barrier();  // B2: W and the intra-chunk weights of chunk q staged
                 if (q + 1 < nq) {
                     prep2(q + 1, gr, R);
@@ -1121,9 +1122,26 @@ __device__ __forceinline__ void affine_body(P1Args a) {
             }
         }
     } else if (helper) {
-        // helper waves (OV): the W column tiles of chunk q+1 beside the chain waves' state
-        // update of chunk q, with the chain waves' barriers
-        if constexpr (L::NH > 0) {
+        // helper waves, with the chain waves' barriers.  Per-token pass: the W column tiles
+        // of chunk q and intra-chunk weight tile ND + h beside the chain waves'
+        // substitution; OV: the W column tiles of chunk q+1 beside the state update of q.
+        if constexpr (TOK && L::NH > 0) {
+            dma_tiles(0, 0, 1, true, kAll);
+            dma_tiles(0, 1, 2, false, kAll);
+            if (nq > 1) dma_tiles(1, 0, 1, true, kAll);
+            wait_vmem();
+            rotate_tiles(0, 0, 1, kAll);
+            rotate_tiles(0, 1, 2, kAll);
+            if (nq > 1) rotate_tiles(1, 0, 1, kAll);
+            lds_barrier();
+            lds_barrier();
+            for (int q = 0; q < nq; ++q) {
+                subst_helper(q);
+                aqk(q, w - L::NPW, 10);  // tile ND + h
+                lds_barrier();  // B2
+                lds_barrier();  // B3
+            }
+        } else if constexpr (L::NH > 0) {
             dma_chunk(0, kAll);
             if (nq > 1) dma_chunk(1, kAll);
             wait_vmem();
