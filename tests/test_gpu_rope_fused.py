@@ -107,6 +107,16 @@ def test_rope_fused_late_frames(dtype, entry):
     run(2, 2, 3, 4, 8, 64, 16, 24, dtype, seed=1020, off=(1 << 24) - 3, base=100.0, entry=entry)
 
 
+@pytest.mark.parametrize("entry", ["frame", "readonly", "token"])
+def test_rope_fused_several_windows(entry):
+    """Seven frames in windows of two frames (window_units = 4 over B*H = 2; groups of one
+    and of two frames), each window's frames rotated at their absolute positions (offset 5)."""
+    run(1, 2, 7, 6, 10, 64, 12, 20, torch.float32, seed=1040, entry=entry, off=5,
+        plan={"window_units": 4, "group_frames": 1})
+    run(1, 2, 7, 6, 10, 112, 36, 38, torch.bfloat16, seed=1041, entry=entry, off=5,
+        plan={"window_units": 4, "group_frames": 2})
+
+
 def test_rope_fused_parts_and_additive():
     """No temporal part, and the additive (block-causal-like) update."""
     run(1, 2, 4, 5, 20, 112, 0, 56, torch.bfloat16, seed=1030)
