@@ -34,6 +34,9 @@ class GdnError(RuntimeError):
         self.code = code
 
 
+ABI_VERSION = 9  # GDN_ABI_VERSION of include/gdn.h that Dims mirrors
+
+
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("n_frames", ctypes.c_int32),
                 ("frame_len", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
@@ -85,6 +88,9 @@ def lib():
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         L.gdn_abi_version.restype = ctypes.c_int
+        if L.gdn_abi_version() != ABI_VERSION:  # the Dims layout above is that version's
+            raise RuntimeError("%s has ABI version %d, this binding needs %d: rebuild it (build.py)"
+                               % (LIB_PATH, L.gdn_abi_version(), ABI_VERSION))
         _lib = L
     return _lib
 

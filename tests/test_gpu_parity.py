@@ -46,17 +46,18 @@ def to_dev(inp):
     return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
 
 
-def run_gdn_case(B, H, F, N, d, dtype, seed, gates="config", state_std=None, flags=gdn.NORMALIZE_K):
-    say("case gdn B=%d H=%d F=%d N=%d d=%d %s seed=%d gates=%s state=%s flags=%d" %
-        (B, H, F, N, d, dtype, seed, gates, state_std, flags))
+def run_gdn_case(B, H, F, N, d, dtype, seed, gates="config", state_std=None, flags=gdn.NORMALIZE_K, plan=None):
+    say("case gdn B=%d H=%d F=%d N=%d d=%d %s seed=%d gates=%s state=%s flags=%d plan=%s" %
+        (B, H, F, N, d, dtype, seed, gates, state_std, flags, plan))
     inp = gdn_inputs(B, H, F, N, d, dtype=dtype, workload_id=seed, gates=gates, state_std=state_std)
     dv = to_dev(inp)
     additive = bool(flags & gdn.ADDITIVE)
     a_, b_ = (None, None) if additive else (dv["alpha"], dv["beta"])
     out, st = gdn.frame_forward(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"], flags=flags,
-                                out_dtype=torch.float32)
+                                out_dtype=torch.float32, plan=plan)
     if dtype == torch.bfloat16:
-        ob, sb = gdn.frame_forward(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"], flags=flags)
+        ob, sb = gdn.frame_forward(dv["q"], dv["k"], dv["v"], a_, b_, F, N, state_in=dv["state_in"], flags=flags,
+                                   plan=plan)
         torch.cuda.synchronize()
         assert torch.equal(ob, out.to(torch.bfloat16)), "bf16 out is not RNE of the float32 result"
         assert torch.equal(sb, st)
