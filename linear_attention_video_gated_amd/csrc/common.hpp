@@ -51,11 +51,25 @@ template <typename V> __device__ __forceinline__ void buf_st(V x, __amdgpu_buffe
     else __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 0);
 }
 
-// maximum over the 64 lanes of a wave (every lane receives it)
+// Maximum over the 64 lanes of a wave, returned to every lane: DPP row rotations by 8, 4, 2
+// and 1 give each lane its 16-lane row's maximum; row_bcast:15 and row_bcast:31 carry it
+// across the four rows into the last one (lanes of the rows a step does not write keep
+// their value), and lane 63's value is read out.  (Shuffles through LDS, one per step, made
+// the frame-map kernel about 1% slower.)
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
+#define GDN_DPPMAX(CTRL, ROWMASK)                                                                      \
+    {                                                                                                  \
+        const int b = __builtin_bit_cast(int, x);                                                      \
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, ROWMASK, 0xf, false))); \
+    }
+    GDN_DPPMAX(0x128, 0xf)
+    GDN_DPPMAX(0x124, 0xf)
+    GDN_DPPMAX(0x122, 0xf)
+    GDN_DPPMAX(0x121, 0xf)
+    GDN_DPPMAX(0x142, 0xa)
+    GDN_DPPMAX(0x143, 0xc)
+#undef GDN_DPPMAX
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 template <typename E> struct Ops;
