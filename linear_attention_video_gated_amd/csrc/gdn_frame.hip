@@ -66,9 +66,9 @@ hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st,
             }
         }
     } else if (phase == 1) {
-        constexpr int lds2 = P2<E, ND>::LDS_B;
-        hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3((ND + P2<E, ND>::SPW - 1) / P2<E, ND>::SPW, BH), dim3(256),
-                           lds2, st, *(const P2Args*)args);
+        using L2 = P2<E, ND>;
+        hipLaunchKernelGGL((gdn_frame_chain<E, ND>), dim3(L2::grid(BH)), dim3(L2::NT), L2::LDS_B, st,
+                           *(const P2Args*)args, BH);
     } else {
         P3Args p3 = *(const P3Args*)args;
 

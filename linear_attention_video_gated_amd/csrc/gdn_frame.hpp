@@ -16,9 +16,9 @@
 //     partial map (A_{g,<=f}, B_{g,<=f}) of the group so far is written out.  With a
 //     single group per (b, h) the start state is known and the pass runs from it (true
 //     start: B only, the B maps are the states).
-//  2. gdn_frame_chain   -- one 4-wave workgroup per (b, h, 4 row slices of S): the serial
-//     part, one d x d product per GROUP:  S_g = S_{g-1} A_g + B_g.  Writes the state
-//     before every group and the final state.
+//  2. gdn_frame_chain   -- one workgroup per (b, h, 16-row slice of S): the serial part,
+//     one product per GROUP:  S_g = S_{g-1} A_g + B_g.  Writes the state before every
+//     group and the final state.
 //  3. gdn_frame_readout -- one workgroup per (b, h, frame), or per part of a frame's
 //     chunks when a call has few frames: composes S_f = S_{g-1} A_{g,<=f} + B_{g,<=f},
 //     then streams Q in and O = Q S_f^T out.
@@ -1301,113 +1301,102 @@ __global__ __launch_bounds__((P1<E, ND, true, (MODE & 8) != 0>::NT), 1) void gdn
 // -------------------------------------------------------------------------------------
 // Phase 2: the serial chain over groups, S_g = S_{g-1} A_g + B_g
 // -------------------------------------------------------------------------------------
-// One workgroup of 4 waves per (b, h, 4 row slices of S).  The group maps are read from
-// HBM once per workgroup: each step's A fragments are staged in LDS (double-buffered)
-// and the next step's are already in flight in registers while this step computes.
+// Rows of S never mix, so each 16-row slice runs its own chain: one workgroup of ND
+// waves per (b, h, slice), wave t computing output column tile t of the slice.  A step
+// is short (KB x 3 dependent products per wave), so it is the latency of fetching the
+// group maps that bounds the chain: each wave streams only its own column tile of A
+// (KB fragments per part) and its tile of B, straight into registers, PD groups ahead
+// of the step that uses them.  The slice's state tiles meet in LDS once per step
+// (double-buffered, one barrier) so that every wave holds the full rows as B operands.
+// Workgroups are numbered so that the ND slices of one (b, h) share an XCD (workgroup i
+// goes to XCD i mod 8) and so its L2: the ND-fold reads of a map come from there.
 template <typename E, int ND> struct P2 {
     static constexpr int KB = (ND + 1) / 2;
     static constexpr int NS = SplitCount<E>::N;
-    static constexpr int APK_E = ND * KB * 64 * 8;             // one part of A (elements)
-    static constexpr int TOTV = NS * APK_E * (int)sizeof(E) / 16;  // 16-byte pieces of A
-    static constexpr int NV = (TOTV + 255) / 256;              // per thread
-    static constexpr int SPW = 4;                              // slices per workgroup
-    static constexpr int LDS_B = 2 * NS * APK_E * (int)sizeof(E);
+    static constexpr int APK_E = ND * KB * 64 * 8;  // one part of A (elements)
+    static constexpr int PD = 3;                     // groups in flight ahead of the step
+    static constexpr int NT = 64 * ND;
+    static constexpr int LDS_B = 2 * ND * 64 * 16;   // two sets of the slice's state tiles
+    // workgroups for BH (b, h) pairs: 8 XCDs x ceil(BH / 8) pairs x ND slices
+    static int grid(int BH) { return 8 * ((BH + 7) / 8) * ND; }
 };
 
 template <typename E, int ND>
-__global__ __launch_bounds__(256, 1) void gdn_frame_chain(P2Args a) {
+__global__ __launch_bounds__((P2<E, ND>::NT), 1) void gdn_frame_chain(P2Args a, int BH) {
     using O = Ops<E>;
     using F8 = typename O::F8;
     using P = P2<E, ND>;
-    constexpr int D = 16 * ND, KB = P::KB, APK_E = P::APK_E, NS = P::NS;
+    constexpr int D = 16 * ND, KB = P::KB, APK_E = P::APK_E, PD = P::PD;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
-    E* const sA = (E*)smem;  // [2][NS * APK_E]
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    f32x4* const sX = (f32x4*)smem;  // [2][ND tiles][64 lanes]
+    const int lane = threadIdx.x & 63, t = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int s = blockIdx.x * P::SPW + w;  // row slice of this wave
-    const bool active = s < ND;
-    const int bh = blockIdx.y;
+    // workgroup i: XCD x = i % 8, its k-th workgroup there is slice k % ND of pair
+    // x + 8 (k / ND)
+    const int wg = blockIdx.x, k = wg >> 3;
+    const int bh = (wg & 7) + 8 * (k / ND), s = k % ND;
+    if (bh >= BH) return;  // whole workgroup: no barrier is reached
     const int ngw = (a.nf + a.G - 1) / a.G;
 
-    u32x4 pa[P::NV];
-    auto loadA = [&](int gi) {
-        const u32x4* src = (const u32x4*)((const E*)a.Agr + ((long long)bh * ngw + gi) * NS * APK_E);
-#pragma unroll
-        for (int k = 0; k < P::NV; ++k)
-            if (tid + 256 * k < P::TOTV) pa[k] = src[tid + 256 * k];
-    };
-    auto storeA = [&](int buf) {
-        u32x4* dst = (u32x4*)(sA + buf * NS * APK_E);
-#pragma unroll
-        for (int k = 0; k < P::NV; ++k)
-            if (tid + 256 * k < P::TOTV) dst[tid + 256 * k] = pa[k];
-    };
-    f32x4 bt[ND], btn[ND];
-    auto loadB = [&](int gi, f32x4 (&b)[ND]) {
-        if (!active) return;
-        const float* p = a.Bgr + ((long long)bh * ngw + gi) * (ND * ND * 256) + (long long)s * ND * 256;
-#pragma unroll
-        for (int t = 0; t < ND; ++t) b[t] = *(const f32x4*)(p + t * 256 + lane * 4);
-    };
-
-    // state tiles: X[t] lane (c,g) = S[16s + c][16t + 4g + i]
-    f32x4 X[ND];
-    const long long srow = (long long)(16 * s + c) * D;
-#pragma unroll
-    for (int t = 0; t < ND; ++t)
-        X[t] = (active && a.state_src) ? *(const f32x4*)(a.state_src + (long long)bh * D * D + srow + 16 * t + 4 * g)
-                                       : zero4();
-    loadA(0);
-    loadB(0, bt);
-    storeA(0);
-    if (ngw > 1) {
-        loadA(1);
-        loadB(1, btn);
+    // prefetch ring: slot j holds group gi = j (mod PD)
+    F8 ah[PD][KB], al[PD][KB];
+    f32x4 bt[PD];
+    const E* const abase = (const E*)a.Agr + (long long)bh * ngw * P::NS * APK_E + (t * KB * 64 + lane) * 8;
+    const float* const bbase = a.Bgr + (long long)bh * ngw * (ND * ND * 256) + (s * ND + t) * 256 + lane * 4;
+#define GDN_CHAIN_LOAD(J, GI)                                                                  \
+    {                                                                                          \
+        const E* src = abase + (long long)(GI) * P::NS * APK_E;                                \
+        _Pragma("unroll") for (int kb = 0; kb < KB; ++kb) {                                    \
+            ah[J][kb] = O::ld8(src + kb * 512);                                                \
+            if (O::kSplit) al[J][kb] = O::ld8(src + APK_E + kb * 512);                         \
+        }                                                                                      \
+        bt[J] = *(const f32x4*)(bbase + (long long)(GI) * (ND * ND * 256));                    \
     }
-    lds_barrier();
-    for (int gi = 0; gi < ngw; ++gi) {
-        if (active) {
-            // state before the group, for the readout
-            float* sg = a.Sgrp + ((long long)bh * ngw + gi) * D * D + srow;
+    // this wave's tile of the state: lane (c, g) = S[16 s + c][16 t + 4 g + i]
+    const long long srow = (long long)(16 * s + c) * D + 16 * t + 4 * g;
+    f32x4 X = a.state_src ? *(const f32x4*)(a.state_src + (long long)bh * D * D + srow) : zero4();
+    // The steps of a full run of PD groups issue the same memory operations whatever the
+    // data (prefetch indices clamped to the last group), so the wait before each step's
+    // products counts only the loads it needs; a run of groups that varies would make it
+    // wait for every load in flight.
 #pragma unroll
-            for (int t = 0; t < ND; ++t) *(f32x4*)(sg + 16 * t + 4 * g) = X[t];
-            // X <- B + A^T X (the group's maps), A streamed from LDS tile by tile
-            const E* ah = sA + (gi & 1) * NS * APK_E;
-            F8 xh[KB], xl[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                O::split8(X[2 * kb], (2 * kb + 1 < ND) ? X[(2 * kb + 1) % ND] : zero4(), xh[kb], xl[kb]);
-#pragma unroll
-            for (int t = 0; t < ND; ++t) {
-                f32x4 acc = bt[t];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const int off = ((t * KB + kb) * 64 + lane) * 8;
-                    const F8 fh = O::ld8(ah + off);
-                    acc = O::mma32(fh, xh[kb], acc);
-                    if (O::kSplit) {
-                        acc = O::mma32(O::ld8(ah + APK_E + off), xh[kb], acc);
-                        acc = O::mma32(fh, xl[kb], acc);
-                    }
-                }
-                X[t] = acc;
-            }
-        }
-        if (gi + 1 < ngw) {
-            storeA((gi + 1) & 1);
-#pragma unroll
-            for (int t = 0; t < ND; ++t) bt[t] = btn[t];
-            if (gi + 2 < ngw) {
-                loadA(gi + 2);
-                loadB(gi + 2, btn);
-            }
-        }
-        lds_barrier();
+    for (int j = 0; j < PD; ++j) GDN_CHAIN_LOAD(j, j < ngw ? j : ngw - 1)
+#define GDN_CHAIN_STEP(J, GI, PREFETCH)                                                        \
+    {                                                                                          \
+        const int gi_ = (GI);                                                                  \
+        /* state before the group, for the readout */                                         \
+        *(f32x4*)(a.Sgrp + ((long long)bh * ngw + gi_) * D * D + srow) = X;                    \
+        f32x4* const xs = sX + (gi_ & 1) * ND * 64;                                            \
+        xs[t * 64 + lane] = X;                                                                 \
+        lds_barrier();                                                                         \
+        /* X <- B + A^T X over the whole rows of the slice */                                 \
+        f32x4 acc = bt[J];                                                                     \
+        _Pragma("unroll") for (int kb = 0; kb < KB; ++kb) {                                    \
+            F8 xh, xl;                                                                         \
+            O::split8(xs[2 * kb * 64 + lane], (2 * kb + 1 < ND) ? xs[(2 * kb + 1) * 64 + lane] \
+                                                                : zero4(), xh, xl);            \
+            acc = O::mma32(ah[J][kb], xh, acc);                                                \
+            if (O::kSplit) {                                                                   \
+                acc = O::mma32(al[J][kb], xh, acc);                                            \
+                acc = O::mma32(ah[J][kb], xl, acc);                                            \
+            }                                                                                  \
+        }                                                                                      \
+        /* the slot's next loads stay behind its last products: they reuse its registers */ \
+        asm volatile("" : "+v"(acc)::"memory");                                               \
+        X = acc;                                                                               \
+        if (PREFETCH) GDN_CHAIN_LOAD(J, gi_ + PD < ngw ? gi_ + PD : ngw - 1)                   \
     }
-    if (active && a.state_dst) {
+    int g0 = 0;
+    for (; g0 + PD <= ngw; g0 += PD) {
 #pragma unroll
-        for (int t = 0; t < ND; ++t) *(f32x4*)(a.state_dst + (long long)bh * D * D + srow + 16 * t + 4 * g) = X[t];
+        for (int j = 0; j < PD; ++j) GDN_CHAIN_STEP(j, g0 + j, true)
     }
+#pragma unroll
+    for (int j = 0; j < PD - 1; ++j)
+        if (g0 + j < ngw) GDN_CHAIN_STEP(j, g0 + j, false)
+#undef GDN_CHAIN_STEP
+#undef GDN_CHAIN_LOAD
+    if (a.state_dst) *(f32x4*)(a.state_dst + (long long)bh * D * D + srow) = X;
 }
 
 // -------------------------------------------------------------------------------------

@@ -143,7 +143,8 @@ struct BC3Args {
 template <typename E, int ND>
 hipError_t launch_gdn_phase(int phase, const void* args, int BH, hipStream_t st, void* const* ev);
 // the variants with the 3D rotary embedding on load (gdn_frame_rope.hip): phase 0 the frame
-// maps in `mode` (bit 0 normalise, bit 1 additive, bit 2 true start), phase 2 the readout
+// maps in `mode` (bit 0 normalise, bit 1 additive, bit 2 true start), phase 2 the readout,
+// phase 3 the per-token readout (mode bits 0 and 1)
 template <typename E, int ND>
 hipError_t launch_gdn_rope(int phase, unsigned mode, const void* args, int BH, hipStream_t st);
 template <typename E, int ND>

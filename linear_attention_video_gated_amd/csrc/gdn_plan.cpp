@@ -50,11 +50,11 @@ size_t bc_unit_bytes(int nd, int esize, size_t* part, size_t* pack) {
 // workgroup per (b, h, group) and one workgroup per CU (its LDS footprint), so its time
 // goes as (rounds of workgroups over the device's CUs) x (frames per group); the serial
 // chain takes one step per group.  G minimises the sum of the two, with about 0.051 us
-// per token of a frame in the frame-map kernel and 3 us per chain step (measured at
+// per token of a frame in the frame-map kernel and 1 us per chain step (measured at
 // d = 112 on MI355X).  Windows hold whole groups.
 int group_frames(long long BH, int n_frames, int frame_len, int cus) {
     const long long ncu = cus > 0 ? cus : 256;
-    const double per_frame = 0.051 * frame_len, per_step = 3.0;
+    const double per_frame = 0.051 * frame_len, per_step = 1.0;
     int best = 1;
     double best_cost = 1e300;
     for (int G = 1; G <= n_frames && G <= 64; ++G) {
