@@ -117,6 +117,18 @@ def test_gdn_slow_gates_carry_state(dtype):
                  state_std=0.3)
 
 
+@pytest.mark.parametrize("d,dtype", [(112, torch.bfloat16), (128, torch.bfloat16), (64, torch.bfloat16),
+                                     (32, torch.float32), (16, torch.float32)])
+def test_gdn_chain_group_counts(d, dtype):
+    """The chain over groups at every group count up to 8 (whole runs of its three-group
+    prefetch and the tails after them), with (b, h) counts that leave part of its
+    eight-way workgroup numbering idle, a carried state in and out, and alpha ~ 1 so that
+    every group's map reaches the outputs."""
+    for ngw, H in [(1, 3), (2, 3), (3, 9), (4, 1), (5, 9), (6, 3), (7, 11), (8, 2)]:
+        run_gdn_case(1, H, ngw, 40, d, dtype, seed=330 + ngw, gates="near_one", state_std=0.2,
+                     plan={"group_frames": 1})
+
+
 @pytest.mark.parametrize("normalize", [True, False])
 def test_gdn_additive_reduction(normalize):
     flags = gdn.ADDITIVE | (gdn.NORMALIZE_K if normalize else 0)
