@@ -12,8 +12,9 @@ inputs already resident in HBM.  Prints one JSON line:
   cpu_baseline  the CPU oracle (float64, token by token, OpenMP) on a bounded sample, with
                 the host CPU model and a one-thread figure
   ms_per_step is the mean over the timed steps; ms_per_step_median and ms_per_step_min come
-  from events recorded between consecutive steps.  hbm_copy_GBps is the rate of a plain
-  2 GiB device copy on the same box (read + write bytes / time).
+  from events recorded between consecutive steps.  Every event inside the timed region is a
+  timing-only HIP event (no cache write-back at its record).  hbm_copy_GBps is the rate of
+  a plain 2 GiB device copy on the same box (read + write bytes / time).
 """
 from __future__ import annotations
 
@@ -100,11 +101,17 @@ def kernel_source_hash(kind):
 
 
 class HipEvents:
-    """hipEvent_t handles from the HIP runtime torch already loaded (same runtime)."""
+    """hipEvent_t handles from the HIP runtime torch already loaded (same runtime).  They are
+    timing-only events (hipEventDisableSystemFence): recording one does not write back and
+    invalidate the caches, which a default event does and which the library's own calls
+    never do; the elapsed times are read only after a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
         self.rt = ctypes.CDLL("libamdhip64.so.7")
-        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -113,10 +120,16 @@ class HipEvents:
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
-            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.rt.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             arr[i] = h
         return arr
+
+    def record(self, h):
+        """Record on torch's current stream (where the library's calls go by default)."""
+        import torch
+        if self.rt.hipEventRecord(h, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         self.rt.hipEventSynchronize(b)
@@ -197,31 +210,41 @@ def scrubber(wl, device):
     return lambda i: buf.sum()
 
 
+_HIP = None
+
+
 def time_steps(step, steps, scrub=None, events=None, per_step=None):
     """ms per step (the mean).  Without a scrub the steps run back to back, with an event
     recorded between consecutive steps (no synchronisation inside the timed region); with
     one, each step is bracketed by its own events and the scrub runs outside them.  The
-    per-step times are appended to `per_step` when given."""
+    per-step times are appended to `per_step` when given.  Timing-only HIP events."""
     import torch
+    global _HIP
+    if _HIP is None:
+        _HIP = HipEvents()
+    hip = _HIP
     torch.cuda.synchronize()
     if scrub is None:
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        marks[0].record()
+        marks = hip.create(steps + 1)
+        hip.record(marks[0])
         for i in range(steps):
             step(events[i]) if events else step()
-            marks[i + 1].record()
+            hip.record(marks[i + 1])
         torch.cuda.synchronize()
         if per_step is not None:
-            per_step.extend(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
-        return marks[0].elapsed_time(marks[steps]) / steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            per_step.extend(hip.elapsed_ms(marks[i], marks[i + 1]) for i in range(steps))
+        ms = hip.elapsed_ms(marks[0], marks[steps]) / steps
+        hip.destroy(marks)
+        return ms
+    ev = hip.create(2 * steps)
     for i in range(steps):
         scrub(i)
-        ev[i][0].record()
+        hip.record(ev[2 * i])
         step(events[i]) if events else step()
-        ev[i][1].record()
+        hip.record(ev[2 * i + 1])
     torch.cuda.synchronize()
-    times = [a.elapsed_time(b) for a, b in ev]
+    times = [hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)]
+    hip.destroy(ev)
     if per_step is not None:
         per_step.extend(times)
     return sum(times) / steps
