@@ -10,8 +10,9 @@
 //
 // One launch.  A workgroup (8 waves for bf16, 4 for float32) takes 32 consecutive queries
 // of one (b, h) per wave and streams the keys it needs -- those up to the end of its last
-// query's frame -- in blocks of 64 through LDS (global -> LDS copies; the next block's
-// copies in flight while this one is used).  Per block and wave, on the matrix cores:
+// query's frame -- in blocks of 64 through LDS (global -> LDS copies one block ahead).
+// Software-pipelined: a block's scores are formed while the previous block's exponentials
+// are taken, in one scheduling region.  Per block and wave, on the matrix cores:
 //   S^T = K Q^T   (4 key tiles x 2 query tiles, k = d; K rows read as 16-byte pieces):
 //                 the accumulator gives each lane one query column, 16 of its keys, so
 //                 the row maximum needs two lane exchanges;
@@ -63,14 +64,16 @@ template <typename E, int ND> struct SAL {
     static constexpr int BLK_B = 64 * KPB;             // one K or V block
     static constexpr int NI = BLK_B / 1024;            // 1 KB copy instructions per K or V block
     // bf16: 8 waves (256 queries share each key block's copy); float32: 4 waves (register
-    // budget).  Two block buffers: the next block's copies overlap this block's products
-    // (a third buffer, two blocks in flight, measured slower at 8 waves)
+    // budget).  Two K slots and two V slots: a block's scores are formed one step before
+    // its PV product, and the copies of the next K and V land one step ahead
     static constexpr int NWV = BF ? 8 : 4;
     static constexpr int NT = 64 * NWV;
     static constexpr int QT = 32 * NWV;                // queries per workgroup
-    static constexpr int NBUF = 2;
-    static constexpr int NU = (2 * NI + NWV - 1) / NWV;  // copy instructions per wave and block (at most)
-    static constexpr int LDS_B = NBUF * 2 * BLK_B;     // [NBUF] x (K, V)
+    // K slots carry 64 zero bytes after their last row: the score operand reads 32 bytes
+    // per lane from column 32 kb + 8 g, which runs past d on the last row
+    static constexpr int PADB = 64;
+    static constexpr int KSLOT = BLK_B + PADB;
+    static constexpr int LDS_B = 2 * KSLOT + 2 * BLK_B;  // K slots 0, 1, then V slots 0, 1
     static_assert(BLK_B % 1024 == 0, "blocks are whole 1 KB copies");
     static_assert(LDS_B <= 160 * 1024, "LDS budget");
 };
@@ -113,34 +116,34 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
     const E* vp = (const E*)a.v + (long long)bh * a.Tk * D;
     const E* qp = (const E*)a.q + (long long)bh * a.Tq * D;
 
-    // block b's copies: instruction i = w + NWV u moves 1 KB of K (i < NI) or V; lane l's
-    // 16 bytes are granule ii * 64 + l of the block (row, piece), the same for every
-    // block, so each lane keeps its element offsets; rows past the keys copy the last key
-    // (finite values; their weights are masked to zero)
-    constexpr int NU = L::NU;
-    const int ncp = (2 * L::NI - w + L::NWV - 1) / L::NWV;  // this wave's copies per block
-    int roff[NU], prow[NU];
+    // Copies of a K or V block: instruction ii = w + NWV u moves 1 KB; lane l's 16 bytes are
+    // granule ii * 64 + l of the block (row, piece), the same for every block, so each lane
+    // keeps its element offsets; rows past the keys copy the last key (finite values;
+    // their weights are masked to zero).  K of block b lands in K slot b % 2, V in V slot
+    // b % 2 (LDS: K slots 0, 1 then V slots 0, 1).
+    constexpr int NUK = (L::NI + L::NWV - 1) / L::NWV;
+    int roff[NUK], prow[NUK];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int i = w + L::NWV * u, ii = i >= L::NI ? i - L::NI : i;
+    for (int u = 0; u < NUK; ++u) {
+        const int ii = w + L::NWV * u;
         const int gidx = ii * 64 + lane, row = gidx / L::KG, piece = gidx - row * L::KG;
         prow[u] = row;
         roff[u] = row * D + min(piece, L::DG - 1) * (16 / (int)sizeof(E));
     }
-    auto copy = [&](int b) {
-        unsigned char* dst = smem + (b % L::NBUF) * 2 * L::BLK_B;
+    auto copy = [&](const E* src, int b, int boff) {
+        unsigned char* dst = smem + boff;
         const bool tail = 64LL * (b + 1) > a.Tk;  // the last block of the keys may be ragged
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int i = w + L::NWV * u;
-            if (i >= 2 * L::NI) break;
-            const int which = i >= L::NI, ii = which ? i - L::NI : i;
-            const E* base = (which ? vp : kp) + 64LL * b * D;
+        for (int u = 0; u < NUK; ++u) {
+            const int ii = w + L::NWV * u;
+            if (ii >= L::NI) break;
             int off = roff[u];
             if (tail) off += (int)(min(64LL * b + prow[u], a.Tk - 1) - 64LL * b - prow[u]) * D;
-            dma16(base + off, dst + which * L::BLK_B + ii * 1024);
+            dma16(src + 64LL * b * D + off, dst + ii * 1024);
         }
     };
+    auto copyK = [&](int b) { copy(kp, b, (b & 1) * L::KSLOT); };
+    auto copyV = [&](int b) { copy(vp, b, 2 * L::KSLOT + (b & 1) * L::BLK_B); };
 
     // this wave's queries: q0 + 32w + 16qt + c (qt = 0, 1); those past Tq compute on the
     // last query's values and are not stored
@@ -162,9 +165,14 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
             qf[qt][kb] = col < D ? O::ld8(r + col) : O::zero8();
         }
     }
-    // the first blocks' copies go out after the Q loads: the wait before block 0 then
-    // covers both
-    for (int b = 0; b < L::NBUF - 1 && b < nblk; ++b) copy(b);
+    // Software pipeline over key blocks: iteration b forms the scores of block b + 1 on
+    // the matrix cores beside block b's exponentials on the vector units, then block b's
+    // PV product.  Iteration b reads K of b + 1 and V of b, while K of b + 2 and V of b + 1
+    // are copied into the slots that K of b and V of b - 1 have left.  The first copies go
+    // out after the Q loads: the wait before block 0 then covers both.
+    copyK(0);
+    copyV(0);
+    if (nblk > 1) copyK(1);
     f32x4 acc[2][ND];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
@@ -177,34 +185,38 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
     F8 ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (E)1.f;
-
-    for (int b = 0; b < nblk; ++b) {
-        // this wave's copies of block b done (and the Q loads); those of the next block
-        // may still be in flight
-        wait_vmem_le(ncp * min(L::NBUF - 2, nblk - 1 - b));
-        lds_barrier();  // every wave's copies visible; block b-1's buffers free
-        if (b + L::NBUF - 1 < nblk) copy(b + L::NBUF - 1);
-        if (!active || 64LL * b >= kmax_w) continue;  // no query of this wave sees block b
-        const unsigned char* kbuf = smem + (b % L::NBUF) * 2 * L::BLK_B;
-        const E* vbuf = (const E*)(kbuf + L::BLK_B);
-        // S^T tiles: s[qt][kt] lane (c, g) = q(16qt + c) . k(64b + 16kt + 4g + i)
-        f32x4 s[2][4];
+    // S^T tiles of block bb: sc[qt][kt] lane (c, g) = q(16qt + c) . k(64bb + 16kt + 4g + i)
+    auto scores = [&](int bb, f32x4 (&sc)[2][4]) {
+        const unsigned char* kbuf = smem + (bb & 1) * L::KSLOT;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) s[qt][kt] = zero4();
+            for (int kt = 0; kt < 4; ++kt) sc[qt][kt] = zero4();
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 // IDENT slot map: key row 16kt + c, d 32kb + 8g .. +7.  Past d the piece
-                // holds the next row's (or, after row 63, the V block's) finite values, which
-                // meet zero slots of Q
+                // holds the next row's (or, after row 63, the next slot's) finite values,
+                // which meet zero slots of Q
                 const F8 kf = O::ld8((const E*)(kbuf + (16 * kt + c) * L::KPB) + 32 * kb + 8 * g);
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) s[qt][kt] = O::mma32(kf, qf[qt][kb], s[qt][kt]);
+                for (int qt = 0; qt < 2; ++qt) sc[qt][kt] = O::mma32(kf, qf[qt][kb], sc[qt][kt]);
             }
         }
+    };
+    if (tid < 2 * L::PADB / 4) ((float*)(smem + (tid >> 4) * L::KSLOT + L::BLK_B))[tid & 15] = 0.f;
+    f32x4 s[2][4], sn[2][4];
+    wait_vmem_le(0);
+    lds_barrier();
+    if (active) scores(0, s);  // key 0 is seen by every query
+    for (int b = 0; b < nblk; ++b) {
+        wait_vmem_le(0);  // this wave's copies of K of b + 1 and V of b done
+        lds_barrier();    // every wave's copies visible; iteration b - 1's slots free
+        if (b + 2 < nblk) copyK(b + 2);
+        if (b + 1 < nblk) copyV(b + 1);
+        if (!active || 64LL * b >= kmax_w) continue;  // no query of this wave sees block b
+        const E* vbuf = (const E*)(smem + 2 * L::KSLOT + (b & 1) * L::BLK_B);
         if (64LL * (b + 1) > kmin_w) {  // some query of the wave misses some key of the block
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
@@ -216,30 +228,42 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
                         if (16 * kt + 4 * g + i >= rel) s[qt][kt][i] = -INFINITY;
             }
         }
-        F8 pf[2][2];
+        // the maxima of the raw scores; the scale (s log2 e > 0) commutes with them
+        float mc[2];
+        bool move[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            // the maximum of the raw scores; the scale (s log2 e > 0) commutes with it
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qt][kt][i]);
-            mx = across_g_max(mx);
-            // The reference point m of the exponentials moves only when some query of the
-            // wave sees a score more than 2^8 above it (always in block 0, whose key 0 every
-            // query sees, so m is finite from then on): the weights stay <= 256 and the
-            // rescaling of the accumulators is skipped for most blocks; the quotient is the
-            // same softmax whatever the reference point.
-            const float mc = mx * a.sl2e;
-            if (__builtin_amdgcn_ballot_w64(mc > m[qt] + 8.f) != 0) {
-                const float mn = fmaxf(m[qt], mc);
+            mc[qt] = across_g_max(mx) * a.sl2e;
+            move[qt] = __builtin_amdgcn_ballot_w64(mc[qt] > m[qt] + 8.f) != 0;
+        }
+        // The reference point m of the exponentials moves only when some query of the
+        // wave sees a score more than 2^8 above it (always in block 0, whose key 0 every
+        // query sees, so m is finite from then on): the weights stay <= 256 and the
+        // rescaling of the accumulators is skipped for most blocks; the quotient is the
+        // same softmax whatever the reference point.
+        if (move[0] || move[1]) {
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                if (!move[qt]) continue;
+                const float mn = fmaxf(m[qt], mc[qt]);
                 const float corr = hw_exp2(m[qt] - mn);
                 m[qt] = mn;
                 lsum[qt] *= corr;
 #pragma unroll
                 for (int t = 0; t < ND; ++t) acc[qt][t] *= corr;
             }
+        }
+        // one scheduling region: block b + 1's scores (formed whether or not the wave
+        // uses them: its K slot holds finite keys) beside block b's exponentials
+        scores(b + 1 < nblk ? b + 1 : b, sn);
+        F8 pf[2][2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
             const float mn = m[qt];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
@@ -264,6 +288,10 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) lsum[qt] = O::mma32(ones, pf[qt][st], lsum[qt]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s[qt][kt] = sn[qt][kt];
     }
     if (!active) return;
 #pragma unroll
