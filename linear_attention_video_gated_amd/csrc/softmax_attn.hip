@@ -205,7 +205,8 @@ __global__ __launch_bounds__((SAL<E, ND>::NT), 1) void sa_fwd(SAArgs a) {
             }
         }
     };
-    if (tid < 2 * L::PADB / 4) ((float*)(smem + (tid >> 4) * L::KSLOT + L::BLK_B))[tid & 15] = 0.f;
+    constexpr int PADF = L::PADB / 4;  // floats of one K slot's zero tail
+    if (tid < 2 * PADF) ((float*)(smem + (tid / PADF) * L::KSLOT + L::BLK_B))[tid % PADF] = 0.f;
     f32x4 s[2][4], sn[2][4];
     wait_vmem_le(0);
     lds_barrier();

@@ -43,3 +43,26 @@ def test_rope3d_parity(dtype, case):
     rms = float(np.sqrt((ref ** 2).mean()))
     err = float(np.abs(got - ref).max())
     assert err <= TOL[dtype] * rms, (err, rms)
+
+
+def test_rope3d_wide_index():
+    """A tensor of more than 2^31 16-byte groups (34 GB of bf16), which the pass walks
+    with 64-bit indices: frames at its start, middle and end against the oracle."""
+    B, H, gh, gw, d, dt, dh = 1, 1, 64, 64, 128, 40, 44
+    F = 32800  # 32800 * 4096 tokens * 16 groups > 2^31
+    say("case rope3d wide index F=%d grid=%dx%d d=%d" % (F, gh, gw, d))
+    g = torch.Generator(device=DEV).manual_seed(950)
+    x = torch.randn((B, H, F * gh * gw, d), generator=g, device=DEV, dtype=torch.bfloat16)
+    N = gh * gw
+    frames = [0, 16001, 32767, F - 1]
+    before = {f: x[:, :, f * N:(f + 1) * N].cpu() for f in frames}
+    gdn.rope3d_apply(x, F, gh, gw, dt, dh)
+    torch.cuda.synchronize()
+    for f in frames:
+        got = x[:, :, f * N:(f + 1) * N].double().cpu().numpy()
+        ref = oracle.rope3d(before[f], 1, gh, gw, dt, dh, frame_offset=f)
+        rms = float(np.sqrt((ref ** 2).mean()))
+        err = float(np.abs(got - ref).max())
+        assert err <= TOL[torch.bfloat16] * rms, (f, err, rms)
+    del x
+    torch.cuda.empty_cache()
