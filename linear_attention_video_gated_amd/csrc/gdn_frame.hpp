@@ -37,7 +37,8 @@
 // U are formed block by block as X_I = Z_I + (T_II - I) Z_I with Z_I = R_I - sum_{J<I}
 // L_IJ X_J kept in fp32, so only the operand of the correction (T_II - I) Z_I is rounded.
 // The per-frame maps that only the readout composes with are kept in fp16 with a power
-// of two per 16-row slice (11 significant bits, below the rounding of the bf16 output);
+// of two per 16-row slice (11 significant bits, below the rounding of the bf16 output;
+// the readout takes A to the fp16 matrix cores as stored, against S as an fp16 hi + lo pair);
 // the group maps that the chain carries keep the hi + lo pair (A) and fp32 (B).
 #pragma once
 #include "common.hpp"
@@ -1470,51 +1471,81 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
         for (int t = 0; t < ND; ++t) X[u][t] = a.Sgrp ? *(const f32x4*)(sg + 16 * t + 4 * g) : zero4();
     }
     if constexpr (O::kSplit) {
-        // row slice t of the stored A is A's rows 16t.. scaled by 2^-e_t, so the columns
-        // 16t.. of S (the same k_in) are scaled by 2^e_t
+        // bf16 inputs: the stored A is fp16, row slice t (A's rows 16t..) scaled by 2^-e_t,
+        // and goes to the fp16 matrix cores as it is.  The columns 16t.. of S (the same
+        // k_in) take 2^e_t, and the whole of this wave's rows one more power of two 2^sc
+        // that puts their largest magnitude below 2^14 (exponents added, so nothing
+        // underflows on the way); S is then an fp16 hi + lo pair (22 significant bits).
+        // The product is formed from zero in that scale, scaled back by 2^-sc and added
+        // to B (a decayed A can make 2^sc large: B itself is never scaled).
+        int emax = -100000;
 #pragma unroll
         for (int t = 0; t < ND; ++t) {
-            const int e = ex[t];
+            float mt = 0.f;
 #pragma unroll
             for (int u = 0; u < NSL; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[u][t][i] = __builtin_amdgcn_ldexpf(X[u][t][i], e);
+                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, fabsf(X[u][t][i]));
+            if (mt > 0.f) emax = max(emax, __builtin_amdgcn_frexp_expf(mt) + ex[t]);
         }
-    }
-    F8 xh[NSL][KB], xl[NSL][KB];
+        emax = (int)wave_max((float)emax);
+        const int sc = emax > -100000 ? 14 - emax : 0;
+        f16x8 sh16[NSL][KB], sl16[NSL][KB];
 #pragma unroll
-    for (int u = 0; u < NSL; ++u)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            O::split8(X[u][2 * kb], (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4(), xh[u][kb], xl[u][kb]);
-#pragma unroll
-    for (int t = 0; t < ND; ++t) {
-        F8 fh[KB], fl[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int off = ((t * KB + kb) * 64 + lane) * 8;
-            if constexpr (O::kSplit) {
-                // fp16 (11 significant bits) -> a bf16 hi + lo pair, exactly
-                const f16x8 h = *(const f16x8*)((const _Float16*)a.Afr + unit * APK_E + off);
-                O::split8(__builtin_convertvector(__builtin_shufflevector(h, h, 0, 1, 2, 3), f32x4),
-                          __builtin_convertvector(__builtin_shufflevector(h, h, 4, 5, 6, 7), f32x4), fh[kb], fl[kb]);
-            } else {
-                fh[kb] = O::ld8((const E*)a.Afr + unit * APK_E + off);
-                fl[kb] = O::zero8();
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < NSL; ++u) {
-            f32x4 acc = ldB(own[u] ? w + 4 * u : 0, t);
+        for (int u = 0; u < NSL; ++u)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                acc = O::mma32(fh[kb], xh[u][kb], acc);
-                if (O::kSplit) {
-                    acc = O::mma32(fl[kb], xh[u][kb], acc);
-                    acc = O::mma32(fh[kb], xl[u][kb], acc);
+                f32x4 lo4 = X[u][2 * kb], hi4 = (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4();
+                const int e0 = ex[2 * kb] + sc, e1 = (2 * kb + 1 < ND) ? ex[(2 * kb + 1) % ND] + sc : 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo4[i] = __builtin_amdgcn_ldexpf(lo4[i], e0);
+                    hi4[i] = __builtin_amdgcn_ldexpf(hi4[i], e1);
                 }
+                const f16x4 h0 = to_f16x4(lo4), h1 = to_f16x4(hi4);
+                const f16x4 l0 = to_f16x4(lo4 - __builtin_convertvector(h0, f32x4));
+                const f16x4 l1 = to_f16x4(hi4 - __builtin_convertvector(h1, f32x4));
+                sh16[u][kb] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                sl16[u][kb] = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            X[u][t] = acc;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+            f16x8 fa[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                fa[kb] = *(const f16x8*)((const _Float16*)a.Afr + unit * APK_E + ((t * KB + kb) * 64 + lane) * 8);
+#pragma unroll
+            for (int u = 0; u < NSL; ++u) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[kb], sh16[u][kb], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[kb], sl16[u][kb], acc, 0, 0, 0);
+                }
+                const f32x4 bt = ldB(own[u] ? w + 4 * u : 0, t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[u][t][i] = __builtin_amdgcn_ldexpf(acc[i], -sc) + bt[i];
+            }
+        }
+    } else {
+        // fp32 inputs: maps and states in fp32 on the fp32 matrix cores
+        F8 xf[NSL][KB];
+#pragma unroll
+        for (int u = 0; u < NSL; ++u)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) xf[u][kb] = O::pack8(X[u][2 * kb], (2 * kb + 1 < ND) ? X[u][(2 * kb + 1) % ND] : zero4());
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+            F8 fa[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) fa[kb] = O::ld8((const E*)a.Afr + unit * APK_E + ((t * KB + kb) * 64 + lane) * 8);
+#pragma unroll
+            for (int u = 0; u < NSL; ++u) {
+                f32x4 acc = ldB(own[u] ? w + 4 * u : 0, t);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) acc = O::mma32(fa[kb], xf[u][kb], acc);
+                X[u][t] = acc;
+            }
         }
     }
     }
