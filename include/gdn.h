@@ -42,7 +42,9 @@
  *  - dtype (GDN_BF16 or GDN_F32) is the type of q, k, v and, unless GDN_F_OUT_F32 is
  *    set, of out.  bf16 inputs are contracted on bf16 matrix cores with float32
  *    accumulation and a float32 state; operands that carry the state are split into
- *    bf16 hi + lo pairs so they keep ~16 significant bits.  float32 inputs run on
+ *    bf16 hi + lo pairs so they keep ~16 significant bits (the readout's composition
+ *    with the fp16 per-frame maps runs on fp16 matrix cores, the state as an fp16
+ *    hi + lo pair under a power-of-two scale).  float32 inputs run on
  *    float32 matrix cores.  A bf16 out is the round-to-nearest-even of the float32
  *    result that GDN_F_OUT_F32 returns.
  *  - Supported: d_k == d_v in {16, 32, 64, 112, 128}; frame_len >= 1; every pointer
