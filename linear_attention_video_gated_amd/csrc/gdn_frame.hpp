@@ -1431,6 +1431,7 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
     const int nch_all = (N + 63) / 64, cpp = (nch_all + a.parts - 1) / a.parts;
     const int c0 = part * cpp, c1 = min(nch_all, c0 + cpp);
     if (c0 >= c1) return;
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
     const int ngw = (a.nf + a.G - 1) / a.G;
     const int gi = fw / a.G;
     const long long unit = (long long)bh * a.nf + fw;
@@ -1488,6 +1489,15 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
                 for (int i = 0; i < 4; ++i) mt = fmaxf(mt, fabsf(X[u][t][i]));
             if (mt > 0.f) emax = max(emax, __builtin_amdgcn_frexp_expf(mt) + ex[t]);
         }
+        // the frame's A map (the same for every wave) staged once in the Q buffers, which
+        // the compose runs before: one coalesced copy instead of four waves each reading
+        // it from L2
+        static_assert(APK_E * 2 <= P3<E, ND, ROPE>::OFF_RP, "the A map fits in the Q buffers");
+        _Float16* const sA = (_Float16*)smem;
+        {
+            const u32x4* src = (const u32x4*)((const _Float16*)a.Afr + unit * APK_E);
+            for (int i = tid; i < APK_E / 8; i += 256) ((u32x4*)sA)[i] = src[i];
+        }
         emax = (int)wave_max((float)emax);
         const int sc = emax > -100000 ? 14 - emax : 0;
         f16x8 sh16[NSL][KB], sl16[NSL][KB];
@@ -1508,12 +1518,12 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
                 sh16[u][kb] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
                 sl16[u][kb] = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
+        lds_barrier();  // the A map in LDS
 #pragma unroll
         for (int t = 0; t < ND; ++t) {
             f16x8 fa[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                fa[kb] = *(const f16x8*)((const _Float16*)a.Afr + unit * APK_E + ((t * KB + kb) * 64 + lane) * 8);
+            for (int kb = 0; kb < KB; ++kb) fa[kb] = *(const f16x8*)(sA + ((t * KB + kb) * 64 + lane) * 8);
 #pragma unroll
             for (int u = 0; u < NSL; ++u) {
                 f32x4 acc = zero4();
@@ -1527,6 +1537,7 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
                 for (int i = 0; i < 4; ++i) X[u][t][i] = __builtin_amdgcn_ldexpf(acc[i], -sc) + bt[i];
             }
         }
+        lds_barrier();  // every wave has read the A map: the Q buffers are free
     } else {
         // fp32 inputs: maps and states in fp32 on the fp32 matrix cores
         F8 xf[NSL][KB];
@@ -1565,7 +1576,6 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
     constexpr int EPV = Ops<E>::EPV;
     constexpr int CBQ = D / EPV;                           // 16-byte pieces per token row
     constexpr int QV = (64 * CBQ + 255) / 256;             // pieces per thread per chunk
-    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
     E* const sQ = (E*)smem;                                // [2][64][QP]
     using V16 = typename Ops<E>::V16;
     const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw) * N;
