@@ -1411,7 +1411,9 @@ __global__ __launch_bounds__((P2<E, ND>::NT), 1) void gdn_frame_chain(P2Args a, 
 // LDS of the readout: two 64-token Q chunks (row pitch d + 8), then (ROPE: q rotated by the
 // 3D rotary embedding as it is loaded) the rotary frequencies
 template <typename E, int ND, bool ROPE = false> struct P3 {
-    static constexpr int OFF_RP = 2 * 64 * (16 * ND + 8) * (int)sizeof(E);  // after the Q buffers
+    // bf16 inputs: one 64-token chunk of O staged after the Q buffers, written out as whole rows
+    static constexpr int OFF_O = 2 * 64 * (16 * ND + 8) * (int)sizeof(E);
+    static constexpr int OFF_RP = OFF_O + (sizeof(E) == 2 ? 64 * (16 * ND + 8) * 2 : 0);
     static constexpr int LDS_B = OFF_RP + (ROPE ? 2 * kRopePairs * 4 : 0);
 };
 
@@ -1577,6 +1579,7 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
     constexpr int CBQ = D / EPV;                           // 16-byte pieces per token row
     constexpr int QV = (64 * CBQ + 255) / 256;             // pieces per thread per chunk
     E* const sQ = (E*)smem;                                // [2][64][QP]
+    E* const sO = (E*)(smem + P3<E, ND, ROPE>::OFF_O);     // [64][QP] (bf16 output)
     using V16 = typename Ops<E>::V16;
     const long long tok0 = (long long)bh * a.T + (long long)(a.f0 + fw) * N;
     const E* qp = (const E*)a.q + tok0 * D;
@@ -1646,11 +1649,21 @@ __global__ __launch_bounds__(256, 2) void gdn_frame_readout(P3Args a) {
                     acc = O::mma32(sh[u][kb], qb[kb], acc);
                     if (O::kSplit) acc = O::mma32(sl_[u][kb], qb[kb], acc);
                 }
-                if (t < N) {
+                if (O::kSplit && !a.out_f32) {  // staged: lane (c, g) holds 4 outputs of token 16 tl + c
+                    O::st4(sO + (16 * tl + c) * QP + 16 * (w + 4 * u) + 4 * g, acc);
+                } else if (t < N) {
                     const long long o = (tok0 + t) * D + 16 * (w + 4 * u) + 4 * g;
                     if (a.out_f32) *(f32x4*)((float*)a.out + o) = acc;
                     else O::st4((E*)a.out + o, acc);
                 }
+            }
+        }
+        if (O::kSplit && !a.out_f32) {
+            lds_barrier();  // the chunk's O rows complete in LDS
+            for (int v = tid; v < 64 * CBQ; v += 256) {
+                const int row = v / CBQ, cb = v - row * CBQ;
+                if (64 * ch + row < N)
+                    *(V16*)((E*)a.out + (tok0 + 64 * ch + row) * D + cb * EPV) = *(const V16*)(sO + row * QP + cb * EPV);
             }
         }
         if (ch + 1 < c1) {
